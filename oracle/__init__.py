@@ -1,0 +1,124 @@
+"""CPU oracle for paged grouped-query attention: loader and build step.
+
+TEST INFRASTRUCTURE ONLY. The test suite, the package smoke check and the benchmark's
+CPU-baseline leg are the only callers. The HIP library never imports this package and
+this package imports nothing from the HIP library; the two share only the seeded input
+arrays from ``workloads``.
+
+The arithmetic lives in ``paged_attn_oracle.c`` (plain C, double precision): a gather of
+each request's pages into dense K/V followed by plain softmax attention, plus an optional
+split-and-merge mode. ``attention(batch)`` returns unrounded fp64 results.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "paged_attn_oracle.c")
+LIB = os.path.join(_HERE, "liboracle_paged_attn.so")
+# A test may point the loader at another build of the oracle (a planted-mistake copy).
+_LIB_OVERRIDE = os.environ.get("FL_ORACLE_LIB")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP, -O2, no fast-math: IEEE double arithmetic)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def load(path: Optional[str] = None):
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    if path is None and _LIB_OVERRIDE:
+        path = _LIB_OVERRIDE
+    p = path or LIB
+    if p == LIB and (not os.path.exists(p) or os.path.getmtime(p) < os.path.getmtime(SRC)):
+        build(force=True)
+    lib = ctypes.CDLL(p)
+    lib.oracle_paged_attention.restype = ctypes.c_int
+    lib.oracle_paged_attention.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_double,
+        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_decode.restype = ctypes.c_int
+    lib.oracle_decode.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    if path is None or path == _LIB_OVERRIDE:
+        _lib = lib
+    return lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def paged_attention(dtype_code: int, qo_indptr, kv_indptr, kv_indices, last_page_len,
+                    num_pages: int, num_qo_heads: int, num_kv_heads: int, head_dim: int,
+                    page_size: int, q, k_pool, v_pool, causal: bool = True,
+                    sm_scale: float = 0.0, num_splits: int = 1, num_threads: int = 0,
+                    lib=None):
+    """Raw entry: returns (out[rows, Hq, D] float64, lse[rows, Hq] float64)."""
+    lib = lib or load()
+    kv_indptr = np.ascontiguousarray(kv_indptr, dtype=np.int32)
+    kv_indices = np.ascontiguousarray(kv_indices, dtype=np.int32)
+    last_page_len = np.ascontiguousarray(last_page_len, dtype=np.int32)
+    B = int(kv_indptr.shape[0]) - 1
+    if qo_indptr is not None:
+        qo_indptr = np.ascontiguousarray(qo_indptr, dtype=np.int32)
+        rows = int(qo_indptr[-1])
+    else:
+        rows = B
+    q = np.ascontiguousarray(q)
+    k_pool = np.ascontiguousarray(k_pool)
+    v_pool = np.ascontiguousarray(v_pool)
+    out = np.zeros((rows, num_qo_heads, head_dim), dtype=np.float64)
+    lse = np.zeros((rows, num_qo_heads), dtype=np.float64)
+    rc = lib.oracle_paged_attention(
+        int(dtype_code), B, _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices),
+        _ptr(last_page_len), int(num_pages), int(num_qo_heads), int(num_kv_heads), int(head_dim),
+        int(page_size), _ptr(q), _ptr(k_pool), _ptr(v_pool), int(bool(causal)), float(sm_scale),
+        int(num_splits), _ptr(out), _ptr(lse), int(num_threads))
+    if rc != 0:
+        raise OracleError(f"oracle_paged_attention returned {rc}")
+    return out, lse
+
+
+def attention(batch, num_splits: int = 1, num_threads: int = 0, lib=None):
+    """Oracle result for a ``workloads.Batch``: (out fp64 [rows, Hq, D], lse fp64 [rows, Hq])."""
+    return paged_attention(batch.dtype_code, batch.qo_indptr, batch.kv_indptr, batch.kv_indices,
+                           batch.last_page_len, batch.num_pages, batch.num_qo_heads,
+                           batch.num_kv_heads, batch.head_dim, batch.page_size, batch.q,
+                           batch.k_pool, batch.v_pool, batch.causal, batch.sm_scale, num_splits,
+                           num_threads, lib=lib)
+
+
+def decode(dtype_code: int, values: np.ndarray, lib=None) -> np.ndarray:
+    """The oracle's own decoding of stored 16/32-bit values to float64."""
+    lib = lib or load()
+    a = np.ascontiguousarray(values)
+    dst = np.zeros(a.size, dtype=np.float64)
+    rc = lib.oracle_decode(int(dtype_code), _ptr(a), int(a.size), _ptr(dst))
+    if rc != 0:
+        raise OracleError(f"oracle_decode returned {rc}")
+    return dst.reshape(a.shape)
+
+
+def max_threads(lib=None) -> int:
+    return int((lib or load()).oracle_max_threads())

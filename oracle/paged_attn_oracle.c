@@ -1,0 +1,270 @@
+/*
+ * CPU oracle for paged grouped-query attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and the
+ * CPU-baseline leg of the benchmark may load this file's library. The product path
+ * never calls it, and it shares no code, header or table with the HIP library.
+ *
+ * What it computes (written from the definitions, in double precision):
+ *
+ *   Paged cache (flashlet README, design bullets: the NHD pool
+ *   [pages, page_size, kv_heads, head_dim]; the page table kv_indptr / kv_indices /
+ *   last_page_len of a paged KV cache). Request r owns pages
+ *   kv_indices[kv_indptr[r] .. kv_indptr[r+1]) and
+ *       kv_len[r] = (kv_indptr[r+1] - kv_indptr[r] - 1) * page_size + last_page_len[r].
+ *   Logical token t of request r sits in page kv_indices[kv_indptr[r] + t / page_size],
+ *   slot t % page_size. The oracle first gathers each request's K and V rows into dense
+ *   arrays, then works on the dense arrays only.
+ *
+ *   Ragged rows (flashlet README, design bullets: one plan()/run() call takes prefill
+ *   chunks and decode rows together, and the causal mask covers both). Request r owns
+ *   query rows qo_indptr[r] .. qo_indptr[r+1]. Reading of the causal mask: query row i
+ *   of a request with qo_len rows sits at position kv_len - qo_len + i, so it attends
+ *   keys t <= kv_len - qo_len + i (bottom-right alignment); for a single decode row this
+ *   is every cached key.
+ *
+ *   Grouped-query heads (Torchlet README: GQA): query head h reads kv head
+ *   h / (num_qo_heads / num_kv_heads).
+ *
+ *   Plain softmax attention per (row, head):
+ *       s_t = scale * sum_d q[d] * k_t[d]
+ *       m   = max_t s_t,  p_t = exp(s_t - m),  l = sum_t p_t
+ *       out = sum_t p_t * v_t / l,  lse = m + log(l)          (natural log)
+ *
+ *   Split mode (num_splits > 1) follows "A library kernel for decode", What changed:
+ *   a request's keys are cut into slices, each slice gives a partial result, and the
+ *   partials are merged. Here the allowed keys [0, n) of a row are cut into num_splits
+ *   consecutive slices of ceil(n / num_splits) keys (empty slices dropped); slice j gives
+ *   (o_j, lse_j) by the plain formula above, and the merge is
+ *       M = max_j lse_j,  w_j = exp(lse_j - M),  out = sum_j w_j o_j / sum_j w_j,
+ *       lse = M + log(sum_j w_j).
+ *   In exact arithmetic both modes give the same numbers.
+ *
+ * Storage types: 1 = IEEE binary16, 2 = bfloat16, 3 = binary32. 16-bit values are read
+ * as raw bit patterns and decoded here by their published bit layouts.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG (-1)
+#define ORACLE_NO_MEM (-2)
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double decode_f16(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);               /* subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f | 0x400), e - 25);  /* (1024 + f) * 2^(e - 15 - 10) */
+    return sign ? -v : v;
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+static double decode_bf16(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float x;
+    memcpy(&x, &u, sizeof x);
+    return (double)x;
+}
+
+static double load_elem(const void *base, int dtype, size_t i)
+{
+    switch (dtype) {
+    case 1: return decode_f16(((const uint16_t *)base)[i]);
+    case 2: return decode_bf16(((const uint16_t *)base)[i]);
+    default: return (double)((const float *)base)[i];
+    }
+}
+
+/* Decode n stored values to double (exported so the decoders can be checked alone). */
+int oracle_decode(int dtype, const void *src, int64_t n, double *dst)
+{
+    if (dtype < 1 || dtype > 3 || n < 0 || (n > 0 && (!src || !dst)))
+        return ORACLE_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = load_elem(src, dtype, (size_t)i);
+    return ORACLE_OK;
+}
+
+/* Plain softmax attention of one query vector over keys [t0, t1) of dense K, V.
+ * Writes o[D] (weighted mean) and returns lse; an empty range returns -inf, o = 0. */
+static double attend_range(const double *qv, const double *K, const double *V, int D,
+                           int t0, int t1, double scale, double *s, double *o)
+{
+    for (int d = 0; d < D; ++d)
+        o[d] = 0.0;
+    if (t1 <= t0)
+        return -INFINITY;
+    double m = -INFINITY;
+    for (int t = t0; t < t1; ++t) {
+        double acc = 0.0;
+        const double *kt = K + (size_t)t * D;
+        for (int d = 0; d < D; ++d)
+            acc += qv[d] * kt[d];
+        s[t] = scale * acc;
+        if (s[t] > m)
+            m = s[t];
+    }
+    double l = 0.0;
+    for (int t = t0; t < t1; ++t) {
+        double p = exp(s[t] - m);
+        l += p;
+        const double *vt = V + (size_t)t * D;
+        for (int d = 0; d < D; ++d)
+            o[d] += p * vt[d];
+    }
+    for (int d = 0; d < D; ++d)
+        o[d] /= l;
+    return m + log(l);
+}
+
+/*
+ * out[rows * Hq * D] and lse[rows * Hq] (lse may be NULL) receive the unrounded
+ * double results; rows = qo_indptr[batch] (qo_indptr == NULL means one row per request).
+ * num_threads <= 0 uses the OpenMP default. Returns 0, or a negative code when the
+ * metadata is inconsistent (no memory outside the given arrays is touched then).
+ */
+int oracle_paged_attention(int dtype, int batch, const int32_t *qo_indptr,
+                           const int32_t *kv_indptr, const int32_t *kv_indices,
+                           const int32_t *last_page_len, int64_t num_pages,
+                           int num_qo_heads, int num_kv_heads, int head_dim, int page_size,
+                           const void *q, const void *k_pool, const void *v_pool,
+                           int causal, double sm_scale, int num_splits,
+                           double *out, double *lse, int num_threads)
+{
+    if (dtype < 1 || dtype > 3 || batch < 0 || num_qo_heads <= 0 || num_kv_heads <= 0 ||
+        num_qo_heads % num_kv_heads || head_dim <= 0 || page_size <= 0 || num_splits < 0)
+        return ORACLE_BAD_ARG;
+    if (batch == 0)
+        return ORACLE_OK;
+    if (!kv_indptr || !kv_indices || !last_page_len || !q || !k_pool || !v_pool || !out)
+        return ORACLE_BAD_ARG;
+    const int Hq = num_qo_heads, Hkv = num_kv_heads, D = head_dim, P = page_size;
+    const int G = Hq / Hkv;
+    if (kv_indptr[0] != 0 || (qo_indptr && qo_indptr[0] != 0))
+        return ORACLE_BAD_ARG;
+    for (int r = 0; r < batch; ++r) {
+        int np_ = kv_indptr[r + 1] - kv_indptr[r];
+        int qlen = qo_indptr ? qo_indptr[r + 1] - qo_indptr[r] : 1;
+        if (np_ < 1 || qlen < 0 || last_page_len[r] < 1 || last_page_len[r] > P)
+            return ORACLE_BAD_ARG;
+        int64_t kv_len = (int64_t)(np_ - 1) * P + last_page_len[r];
+        if (causal && qlen > kv_len)
+            return ORACLE_BAD_ARG;
+        for (int j = kv_indptr[r]; j < kv_indptr[r + 1]; ++j)
+            if (kv_indices[j] < 0 || kv_indices[j] >= num_pages)
+                return ORACLE_BAD_ARG;
+    }
+    const double scale = sm_scale > 0.0 ? sm_scale : 1.0 / sqrt((double)D);
+    const int S = num_splits > 1 ? num_splits : 1;
+    const int pairs = batch * Hkv;
+    int status = ORACLE_OK;
+
+#ifdef _OPENMP
+    if (num_threads > 0)
+        omp_set_num_threads(num_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int pr = 0; pr < pairs; ++pr) {
+        const int r = pr / Hkv, g = pr % Hkv;
+        const int np_ = kv_indptr[r + 1] - kv_indptr[r];
+        const int kv_len = (np_ - 1) * P + last_page_len[r];
+        const int row0 = qo_indptr ? qo_indptr[r] : r;
+        const int qlen = qo_indptr ? qo_indptr[r + 1] - qo_indptr[r] : 1;
+        double *K = malloc((size_t)kv_len * D * sizeof(double));
+        double *V = malloc((size_t)kv_len * D * sizeof(double));
+        double *s = malloc((size_t)kv_len * sizeof(double));
+        double *qv = malloc((size_t)D * sizeof(double));
+        double *o = malloc((size_t)D * sizeof(double));
+        double *acc = malloc((size_t)D * sizeof(double));
+        if (!K || !V || !s || !qv || !o || !acc) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            status = ORACLE_NO_MEM;
+        } else {
+            /* gather: token t -> page kv_indices[kv_indptr[r] + t / P], slot t % P */
+            for (int t = 0; t < kv_len; ++t) {
+                int64_t page = kv_indices[kv_indptr[r] + t / P];
+                size_t src = (((size_t)page * P + (size_t)(t % P)) * Hkv + g) * D;
+                for (int d = 0; d < D; ++d) {
+                    K[(size_t)t * D + d] = load_elem(k_pool, dtype, src + d);
+                    V[(size_t)t * D + d] = load_elem(v_pool, dtype, src + d);
+                }
+            }
+            for (int i = 0; i < qlen; ++i) {
+                const int n = causal ? kv_len - qlen + i + 1 : kv_len; /* keys [0, n) */
+                for (int hh = 0; hh < G; ++hh) {
+                    const int h = g * G + hh;
+                    const size_t qi = ((size_t)(row0 + i) * Hq + h) * D;
+                    for (int d = 0; d < D; ++d)
+                        qv[d] = load_elem(q, dtype, qi + d);
+                    double *dst = out + qi;
+                    double L;
+                    if (S == 1) {
+                        L = attend_range(qv, K, V, D, 0, n, scale, s, dst);
+                    } else {
+                        const int len = (n + S - 1) / S;
+                        double M = -INFINITY;
+                        for (int j = 0; j < S; ++j) {
+                            int a = j * len, b = a + len < n ? a + len : n;
+                            if (a >= b)
+                                continue;
+                            double lj = attend_range(qv, K, V, D, a, b, scale, s, o);
+                            if (lj > M)
+                                M = lj;
+                        }
+                        double wsum = 0.0;
+                        for (int d = 0; d < D; ++d)
+                            acc[d] = 0.0;
+                        for (int j = 0; j < S; ++j) {
+                            int a = j * len, b = a + len < n ? a + len : n;
+                            if (a >= b)
+                                continue;
+                            double lj = attend_range(qv, K, V, D, a, b, scale, s, o);
+                            double w = exp(lj - M);
+                            wsum += w;
+                            for (int d = 0; d < D; ++d)
+                                acc[d] += w * o[d];
+                        }
+                        for (int d = 0; d < D; ++d)
+                            dst[d] = acc[d] / wsum;
+                        L = M + log(wsum);
+                    }
+                    if (lse)
+                        lse[(size_t)(row0 + i) * Hq + h] = L;
+                }
+            }
+        }
+        free(K);
+        free(V);
+        free(s);
+        free(qv);
+        free(o);
+        free(acc);
+    }
+    return status;
+}
+
+/* Threads an OpenMP parallel region of the oracle uses (1 without OpenMP). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

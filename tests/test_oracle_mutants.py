@@ -1,0 +1,67 @@
+"""The oracle pins must catch plausible mistakes.
+
+Each case copies the oracle's C source, plants one mistake (a dropped term, a wrong sign
+or index, a swapped operand), builds the copy in a temporary directory and runs the pin
+suite against it in a subprocess. Every mutant must make the pins fail. CPU only.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "paged_attn_oracle.c")
+
+MUTANTS = {
+    "head_map_interleaved": ("const int h = g * G + hh;", "const int h = hh * Hkv + g;"),
+    "slot_off_by_one": ("size_t src = (((size_t)page * P + (size_t)(t % P)) * Hkv + g) * D;",
+                        "size_t src = (((size_t)page * P + (size_t)((t + 1) % P)) * Hkv + g) * D;"),
+    "page_table_ignores_request": ("int64_t page = kv_indices[kv_indptr[r] + t / P];",
+                                   "int64_t page = kv_indices[t / P];"),
+    "causal_top_left": ("const int n = causal ? kv_len - qlen + i + 1 : kv_len;",
+                        "const int n = causal ? i + 1 : kv_len;"),
+    "no_max_subtraction": ("double p = exp(s[t] - m);", "double p = exp(s[t]);"),
+    "no_normaliser": ("        o[d] /= l;\n", "        o[d] /= 1.0;\n"),
+    "lse_without_log": ("return m + log(l);", "return m + l;"),
+    "merge_weight_sign": ("double w = exp(lj - M);", "double w = exp(M - lj);"),
+    "k_v_swapped": ("V[(size_t)t * D + d] = load_elem(v_pool, dtype, src + d);",
+                    "V[(size_t)t * D + d] = load_elem(k_pool, dtype, src + d);"),
+    "scale_dropped": ("s[t] = scale * acc;", "s[t] = acc;"),
+    "last_key_dropped": ("for (int t = t0; t < t1; ++t) {\n        double p",
+                         "for (int t = t0; t < t1 - 1; ++t) {\n        double p"),
+    "f16_exponent_bias": ("v = ldexp((double)(f | 0x400), e - 25);", "v = ldexp((double)(f | 0x400), e - 24);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o",
+                           str(lib), str(mpath), "-lm"])
+    env = dict(os.environ, FL_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
+    assert "failed" in r.stdout
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """Control: the same build-and-run route with no planted mistake passes the pins."""
+    mpath = tmp_path / "copy.c"
+    shutil.copy(SRC, mpath)
+    lib = tmp_path / "libcopy.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o",
+                           str(lib), str(mpath), "-lm"])
+    env = dict(os.environ, FL_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:]
