@@ -1,0 +1,178 @@
+/*
+ * fl_paged_attn.h — batched grouped-query attention over a paged KV cache (gfx950).
+ *
+ * One plan per scheduling step, one run per layer, following the plan()/run() split of
+ * an attention backend (flashlet README, repository layout: backends/base.py) and the
+ * practice of keeping per-step metadata in persistent device buffers that are updated
+ * in place (flashlet README, design bullets), so that run() always launches with the
+ * same arguments.
+ *
+ * Operation (run). For request r with query rows qo_indptr[r] .. qo_indptr[r+1] and
+ * pages kv_indices[kv_indptr[r] .. kv_indptr[r+1]) holding
+ *     kv_len[r] = (kv_indptr[r+1] - kv_indptr[r] - 1) * page_size + last_page_len[r]
+ * cached tokens (token t lives in page kv_indices[kv_indptr[r] + t / page_size], slot
+ * t % page_size), every query row i and query head h computes softmax attention
+ *     out[row, h, :] = sum_t softmax_t(sm_scale * q[row, h, :] . K[t, h / G, :]) V[t, h / G, :]
+ * with G = num_qo_heads / num_kv_heads (grouped-query attention, Torchlet README) over the
+ * keys t <= kv_len - qo_len + i when causal (bottom-right alignment: a decode row sees its
+ * whole history, a prefill chunk's rows see the history plus the chunk up to themselves;
+ * flashlet README, design bullets: one ragged call covers prefill chunks and decode rows
+ * and the causal mask covers both), or all kv_len keys otherwise.
+ * Long histories are cut into slices that run on different compute units and the
+ * per-slice results are merged by log-sum-exp ("A library kernel for decode",
+ * What changed); the result is the same attention up to floating-point rounding.
+ *
+ * Memory layout (all row-major, contiguous):
+ *   q, out       [rows, num_qo_heads, head_dim]           rows = qo_indptr[batch]
+ *   k_pool,
+ *   v_pool       [num_pages, page_size, num_kv_heads, head_dim]   one layer
+ *                (the NHD pool of the flashlet README, design bullets)
+ *   lse          [rows, num_qo_heads] float, natural log of the softmax denominator
+ *                plus the row maximum (optional)
+ * q, the pools and out share one element type (fl_dtype). Accumulation is fp32.
+ *
+ * Ownership. The caller owns every pointer it passes. fl_paged_attn_plan copies the host
+ * arrays before it returns. The handle owns its persistent device metadata buffers, its
+ * fp32 partial-result workspace (sized at create time from fl_config) and two pinned host
+ * staging buffers.
+ *
+ * Streams. plan() validates and partitions on the host, then enqueues one host-to-device
+ * copy of the work list on `stream`. run() only enqueues kernels on `stream`; it neither
+ * allocates nor synchronises. plan() and run() of one handle must be ordered on one
+ * stream (or the caller orders them). A handle is not thread-safe.
+ *
+ * Errors. Every call returns an fl_status; on failure fl_last_error() gives a message
+ * (thread-local, valid until the next call on that thread). No exception crosses this
+ * interface. A failed plan leaves the handle un-planned; run() then returns
+ * FL_ERR_NOT_PLANNED. Page ids are checked on the host at plan time; kernels do no
+ * bounds checks of their own.
+ */
+#ifndef FL_PAGED_ATTN_H
+#define FL_PAGED_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FL_OK = 0,
+    FL_ERR_INVALID_ARG = -1,   /* inconsistent metadata, NULL pointer, bad sizes       */
+    FL_ERR_UNSUPPORTED = -2,   /* head_dim, page_size, dtype or group outside the set   */
+    FL_ERR_CAPACITY = -3,      /* batch, rows, pages or splits beyond the handle's caps */
+    FL_ERR_NOT_PLANNED = -4,   /* run() before a successful plan()                      */
+    FL_ERR_HIP = -5            /* a HIP runtime call failed (message has the HIP error) */
+} fl_status;
+
+typedef enum { FL_F16 = 1, FL_BF16 = 2, FL_F32 = 3 } fl_dtype;
+
+typedef struct fl_paged_attn *fl_handle;
+
+typedef struct {
+    int32_t num_qo_heads;      /* Hq, a multiple of num_kv_heads                         */
+    int32_t num_kv_heads;      /* Hkv >= 1                                               */
+    int32_t head_dim;          /* 64 or 128                                              */
+    int32_t page_size;         /* power of two in [16, 256]                              */
+    int32_t dtype;             /* fl_dtype of q, pools and out                           */
+    int32_t max_batch;         /* most requests one plan may hold                        */
+    int32_t max_qo_rows;       /* most query rows one plan may hold (qo_indptr[batch])   */
+    int64_t max_kv_pages;      /* most page-table entries one plan may hold              */
+    int32_t num_cus;           /* compute units to plan for; 0 = ask the device
+                                  (a host-only handle then plans for 256)                */
+    int32_t split_items_per_cu;/* target slices per compute unit when splitting long
+                                  histories; 0 = library default                         */
+    int32_t min_split_tokens;  /* shortest slice the planner makes; 0 = library default  */
+    int32_t reserved;          /* must be 0                                              */
+} fl_config;
+
+/*
+ * Create a handle for one configuration on HIP device `device` (>= 0). device == -1 makes
+ * a host-only handle: plan() validates and builds the work list without any HIP call
+ * (for inspecting plans on machines without a GPU); run() on it returns
+ * FL_ERR_UNSUPPORTED. On success *out receives the handle.
+ */
+fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out);
+
+/* Free the handle and everything it owns. Waits for the handle's pending work. NULL is a no-op. */
+fl_status fl_paged_attn_destroy(fl_handle h);
+
+/*
+ * Build the work list for one step (once per step, shared by every layer's run()).
+ *   batch            number of requests, 0 <= batch <= max_batch
+ *   qo_indptr        host int32[batch+1], prefix sums of query rows per request, [0] = 0;
+ *                    NULL means one row per request (pure decode). A request may have
+ *                    0 rows. With causal != 0 each request needs qo_len <= kv_len.
+ *   kv_indptr        host int32[batch+1], prefix sums of pages per request, [0] = 0;
+ *                    every request holds at least one page (kv_len >= 1)
+ *   kv_indices       host int32[kv_indptr[batch]], physical page ids in [0, num_pages);
+ *                    requests may share pages (read-only prefix sharing)
+ *   last_page_len    host int32[batch], each in [1, page_size]
+ *   num_pages        pool size, the bound for page ids
+ *   causal           nonzero: bottom-right causal mask (a no-op for single decode rows)
+ *   sm_scale         softmax scale; <= 0 means 1/sqrt(head_dim)
+ *   num_splits       0: the planner picks the slices from the lengths and the compute
+ *                    unit count; > 0: cut every row block's keys into that many slices
+ *                    (fewer when the history has fewer 16-token tiles)
+ *   stream           hipStream_t for the host-to-device copy (NULL: the null stream)
+ * The work list depends only on the lengths, never on page ids, so two plans over the
+ * same lengths give bit-identical results for any page assignment.
+ */
+fl_status fl_paged_attn_plan(fl_handle h, int32_t batch, const int32_t *qo_indptr,
+                             const int32_t *kv_indptr, const int32_t *kv_indices,
+                             const int32_t *last_page_len, int64_t num_pages, int32_t causal,
+                             float sm_scale, int32_t num_splits, void *stream);
+
+/*
+ * Compute attention for one layer with the current plan. Device pointers:
+ *   q       [rows, num_qo_heads, head_dim]
+ *   k_pool  [num_pages, page_size, num_kv_heads, head_dim]
+ *   v_pool  same layout as k_pool
+ *   out     [rows, num_qo_heads, head_dim], written in full
+ *   lse     float[rows, num_qo_heads] or NULL
+ * All pointers 16-byte aligned. Enqueues on `stream` and returns; never synchronises or
+ * allocates, so it may be captured into a HIP graph.
+ */
+fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, const void *v_pool,
+                            void *out, float *lse, void *stream);
+
+/*
+ * Facts about the current plan: work items (workgroups of the attention launch), the
+ * largest number of slices any row block was cut into, and the partial-result bytes the
+ * plan uses. Any output pointer may be NULL.
+ */
+fl_status fl_paged_attn_plan_info(fl_handle h, int32_t *num_work_items, int32_t *max_splits,
+                                  int64_t *workspace_bytes);
+
+/*
+ * Copy the current plan's work list to host memory: FL_WORK_ITEM_INTS int32 per item in
+ * launch order, fields as named by FL_WI_* below. *num_items receives the item count;
+ * at most `capacity` items are written.
+ */
+#define FL_WORK_ITEM_INTS 16
+enum {
+    FL_WI_Q_START = 0,   /* first query row of the request                              */
+    FL_WI_QO_LEN = 1,    /* query rows of the request                                   */
+    FL_WI_KV_LEN = 2,    /* cached tokens of the request                                */
+    FL_WI_PAGE_BASE = 3, /* kv_indptr[request]                                          */
+    FL_WI_KV_HEAD = 4,
+    FL_WI_ROW_BEGIN = 5, /* first row of the block in (query row * G + head in group)   */
+    FL_WI_NUM_ROWS = 6,  /* rows in the block (<= 16)                                   */
+    FL_WI_TOK_BEGIN = 7, /* key slice [tok_begin, tok_end)                               */
+    FL_WI_TOK_END = 8,
+    FL_WI_PART_ROW = 9,  /* -1: writes the final output; else its rows in the workspace */
+    FL_WI_REQUEST = 10,
+    FL_WI_SPLIT = 11,    /* slice index within its row block                            */
+    FL_WI_NUM_SPLITS = 12
+};
+fl_status fl_paged_attn_get_work_items(fl_handle h, int32_t *items, int32_t capacity,
+                                       int32_t *num_items);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char *fl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FL_PAGED_ATTN_H */

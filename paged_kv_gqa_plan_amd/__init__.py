@@ -1,0 +1,202 @@
+"""Python binding for ``libfl_paged_attn.so``: paged grouped-query attention on gfx950.
+
+Argument marshalling only. Every step of the computation runs in the library's HIP
+kernels; the functions below carry the C interface's names and pass plain pointers,
+sizes and host arrays through ctypes. torch is used by the optional ``PagedAttention``
+helper for device memory and streams only (``tensor.data_ptr()``,
+``torch.cuda.current_stream().cuda_stream``).
+
+The library is built in-tree (``paged_kv_gqa_plan_amd/_build.py``); importing the
+binding without it raises at once — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+from ._build import LIB as LIB_PATH
+
+FL_OK, FL_ERR_INVALID_ARG, FL_ERR_UNSUPPORTED, FL_ERR_CAPACITY = 0, -1, -2, -3
+FL_ERR_NOT_PLANNED, FL_ERR_HIP = -4, -5
+FL_F16, FL_BF16, FL_F32 = 1, 2, 3
+FL_WORK_ITEM_INTS = 16
+WORK_ITEM_FIELDS = ("q_start", "qo_len", "kv_len", "page_base", "kv_head", "row_begin",
+                    "num_rows", "tok_begin", "tok_end", "part_row", "request", "split",
+                    "num_splits")
+STATUS_NAMES = {0: "FL_OK", -1: "FL_ERR_INVALID_ARG", -2: "FL_ERR_UNSUPPORTED",
+                -3: "FL_ERR_CAPACITY", -4: "FL_ERR_NOT_PLANNED", -5: "FL_ERR_HIP"}
+DTYPE_CODES = {"f16": FL_F16, "bf16": FL_BF16, "f32": FL_F32}
+
+
+class fl_config(ctypes.Structure):
+    _fields_ = [("num_qo_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("max_qo_rows", ctypes.c_int32), ("max_kv_pages", ctypes.c_int64),
+                ("num_cus", ctypes.c_int32), ("split_items_per_cu", ctypes.c_int32),
+                ("min_split_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class FlError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+EXPORTED = ("fl_paged_attn_create", "fl_paged_attn_destroy", "fl_paged_attn_plan",
+            "fl_paged_attn_run", "fl_paged_attn_plan_info", "fl_paged_attn_get_work_items",
+            "fl_last_error")
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load the built library (raises if it is missing)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is not built; run `python -c 'import __graft_entry__ as g; "
+                          f"g.build()'` (hipcc, gfx950)")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.fl_paged_attn_create.argtypes = [ctypes.POINTER(fl_config), ctypes.c_int, ctypes.POINTER(vp)]
+    lib.fl_paged_attn_destroy.argtypes = [vp]
+    lib.fl_paged_attn_plan.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, ctypes.c_float, i32, vp]
+    lib.fl_paged_attn_run.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.fl_paged_attn_plan_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                            ctypes.POINTER(i64)]
+    lib.fl_paged_attn_get_work_items.argtypes = [vp, vp, i32, ctypes.POINTER(i32)]
+    for name in EXPORTED[:-1]:
+        getattr(lib, name).restype = ctypes.c_int
+    lib.fl_last_error.argtypes = []
+    lib.fl_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(st: int, where: str):
+    if st != FL_OK:
+        raise FlError(st, where, fl_last_error())
+
+
+def _i32(a) -> Optional[np.ndarray]:
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def fl_last_error() -> str:
+    return load_library().fl_last_error().decode()
+
+
+def fl_paged_attn_create(cfg: fl_config, device: int) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(load_library().fl_paged_attn_create(ctypes.byref(cfg), int(device), ctypes.byref(h)),
+           "fl_paged_attn_create")
+    return h
+
+
+def fl_paged_attn_destroy(h) -> None:
+    _check(load_library().fl_paged_attn_destroy(h), "fl_paged_attn_destroy")
+
+
+def fl_paged_attn_plan(h, batch: int, qo_indptr, kv_indptr, kv_indices, last_page_len,
+                       num_pages: int, causal: bool = True, sm_scale: float = 0.0,
+                       num_splits: int = 0, stream: int = 0) -> None:
+    """Host arrays (anything numpy turns into int32) for the metadata; ``stream`` is a
+    hipStream_t as an integer (0 = null stream)."""
+    qo, kp, ki, lp = _i32(qo_indptr), _i32(kv_indptr), _i32(kv_indices), _i32(last_page_len)
+    _check(load_library().fl_paged_attn_plan(h, int(batch), _p(qo), _p(kp), _p(ki), _p(lp),
+                                             int(num_pages), int(bool(causal)), float(sm_scale),
+                                             int(num_splits), ctypes.c_void_p(int(stream))),
+           "fl_paged_attn_plan")
+
+
+def fl_paged_attn_run(h, q: int, k_pool: int, v_pool: int, out: int, lse: Optional[int] = None,
+                      stream: int = 0) -> None:
+    """Device pointers as integers (e.g. ``tensor.data_ptr()``); lse may be None."""
+    _check(load_library().fl_paged_attn_run(h, ctypes.c_void_p(q), ctypes.c_void_p(k_pool),
+                                            ctypes.c_void_p(v_pool), ctypes.c_void_p(out),
+                                            ctypes.c_void_p(lse or 0), ctypes.c_void_p(int(stream))),
+           "fl_paged_attn_run")
+
+
+def fl_paged_attn_plan_info(h) -> Tuple[int, int, int]:
+    n, s, b = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(load_library().fl_paged_attn_plan_info(h, ctypes.byref(n), ctypes.byref(s),
+                                                  ctypes.byref(b)), "fl_paged_attn_plan_info")
+    return n.value, s.value, b.value
+
+
+def fl_paged_attn_get_work_items(h) -> np.ndarray:
+    """The current plan's work list as an int32 array [items, FL_WORK_ITEM_INTS]."""
+    lib = load_library()
+    n = ctypes.c_int32()
+    _check(lib.fl_paged_attn_get_work_items(h, None, 0, ctypes.byref(n)),
+           "fl_paged_attn_get_work_items")
+    buf = np.zeros((max(n.value, 1), FL_WORK_ITEM_INTS), dtype=np.int32)
+    _check(lib.fl_paged_attn_get_work_items(h, _p(buf), n.value, ctypes.byref(n)),
+           "fl_paged_attn_get_work_items")
+    return buf[:n.value]
+
+
+def make_config(num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
+                dtype: str, max_batch: int, max_qo_rows: int, max_kv_pages: int,
+                num_cus: int = 0, split_items_per_cu: int = 0,
+                min_split_tokens: int = 0) -> fl_config:
+    return fl_config(num_qo_heads, num_kv_heads, head_dim, page_size, DTYPE_CODES[dtype],
+                     max_batch, max_qo_rows, max_kv_pages, num_cus, split_items_per_cu,
+                     min_split_tokens, 0)
+
+
+class PagedAttention:
+    """A handle plus torch plumbing: tensors in, pointers and the current stream out."""
+
+    def __init__(self, cfg: fl_config, device: int = 0):
+        self.cfg = cfg
+        self.device = device
+        self.handle = fl_paged_attn_create(cfg, device)
+
+    def close(self):
+        if self.handle is not None:
+            fl_paged_attn_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _stream(self, stream):
+        if stream is not None:
+            return int(stream)
+        if self.device < 0:
+            return 0
+        import torch
+        return torch.cuda.current_stream(self.device).cuda_stream
+
+    def plan(self, qo_indptr, kv_indptr, kv_indices, last_page_len, num_pages: int,
+             causal: bool = True, sm_scale: float = 0.0, num_splits: int = 0, stream=None):
+        batch = len(kv_indptr) - 1
+        fl_paged_attn_plan(self.handle, batch, qo_indptr, kv_indptr, kv_indices, last_page_len,
+                           num_pages, causal, sm_scale, num_splits, self._stream(stream))
+
+    def run(self, q, k_pool, v_pool, out, lse=None, stream=None):
+        fl_paged_attn_run(self.handle, q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                          out.data_ptr(), None if lse is None else lse.data_ptr(),
+                          self._stream(stream))
+
+    def info(self):
+        return fl_paged_attn_plan_info(self.handle)
+
+    def work_items(self) -> np.ndarray:
+        return fl_paged_attn_get_work_items(self.handle)

@@ -1,0 +1,321 @@
+// C interface of the paged GQA attention library: handles, plan staging and launches.
+//
+// A handle owns persistent device buffers for the per-step metadata (work list, merge
+// list, a copy of the page table) that plan() refreshes in place and run() reads, so every
+// run() launches with the same arguments (flashlet README, design bullets: metadata in
+// persistent device buffers, updated in place each step; pinned-to-device metadata path).
+// The host side stages each plan into one of two pinned buffers and copies it with one
+// asynchronous transfer on the caller's stream; an event per staging buffer keeps a new
+// plan from overwriting a buffer whose copy is still in flight.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "fl_internal.h"
+
+using fl::Plan;
+using fl::PlanLimits;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fl_status set_err(fl_status st, const std::string &msg) {
+    g_last_error = msg;
+    return st;
+}
+
+fl_status hip_err(hipError_t e, const char *what) {
+    return set_err(FL_ERR_HIP, std::string(what) + ": " + hipGetErrorName(e) + " (" +
+                                   hipGetErrorString(e) + ")");
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+struct fl_paged_attn {
+    fl_config cfg{};
+    PlanLimits lim{};
+    int device = -1;
+    bool host_only = true;
+    int32_t group = 1;
+    int32_t log2_page = 0;
+
+    // device buffers
+    char *d_meta = nullptr;      // [items | merges | page table]
+    float *d_part_o = nullptr;   // [part_rows_cap, head_dim]
+    float *d_part_lse = nullptr; // [part_rows_cap]
+    int64_t off_merges = 0, off_pages = 0, meta_bytes = 0;
+
+    // pinned staging, double-buffered
+    char *h_stage[2] = {nullptr, nullptr};
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    bool ev_live[2] = {false, false};
+    int cur = 0;
+
+    // current plan
+    bool planned = false;
+    Plan plan;
+    int32_t causal = 1;
+    float scale_log2 = 0.f;
+};
+
+namespace {
+
+fl_status check_config(const fl_config *c) {
+    if (!c) return set_err(FL_ERR_INVALID_ARG, "config is NULL");
+    if (c->num_kv_heads < 1 || c->num_qo_heads < 1 || c->num_qo_heads % c->num_kv_heads)
+        return set_err(FL_ERR_INVALID_ARG,
+                       "num_qo_heads must be a positive multiple of num_kv_heads >= 1");
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return set_err(FL_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    const int p = c->page_size;
+    if (p < 16 || p > 256 || (p & (p - 1)))
+        return set_err(FL_ERR_UNSUPPORTED, "page_size must be a power of two in [16, 256]");
+    if (c->dtype != FL_F16 && c->dtype != FL_BF16 && c->dtype != FL_F32)
+        return set_err(FL_ERR_UNSUPPORTED, "dtype must be FL_F16, FL_BF16 or FL_F32");
+    if (c->max_batch < 0 || c->max_qo_rows < 0 || c->max_kv_pages < 0)
+        return set_err(FL_ERR_INVALID_ARG, "capacities must be >= 0");
+    if (c->num_cus < 0 || c->split_items_per_cu < 0 || c->min_split_tokens < 0 || c->reserved)
+        return set_err(FL_ERR_INVALID_ARG, "num_cus / split knobs must be >= 0, reserved 0");
+    return FL_OK;
+}
+
+void release(fl_paged_attn *h) {
+    if (!h) return;
+    if (!h->host_only) {
+        (void)hipSetDevice(h->device);
+        for (int i = 0; i < 2; ++i) {
+            if (h->ev[i]) {
+                (void)hipEventSynchronize(h->ev[i]);
+                (void)hipEventDestroy(h->ev[i]);
+            }
+            if (h->h_stage[i]) (void)hipHostFree(h->h_stage[i]);
+        }
+        (void)hipDeviceSynchronize();
+        if (h->d_meta) (void)hipFree(h->d_meta);
+        if (h->d_part_o) (void)hipFree(h->d_part_o);
+        if (h->d_part_lse) (void)hipFree(h->d_part_lse);
+    }
+    delete h;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *fl_last_error(void) { return g_last_error.c_str(); }
+
+fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out) {
+    g_last_error.clear();
+    if (!out) return set_err(FL_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    fl_status st = check_config(cfg);
+    if (st != FL_OK) return st;
+    if (device < -1) return set_err(FL_ERR_INVALID_ARG, "device must be >= -1");
+
+    fl_paged_attn *h = new (std::nothrow) fl_paged_attn();
+    if (!h) return set_err(FL_ERR_INVALID_ARG, "out of host memory");
+    h->cfg = *cfg;
+    h->device = device;
+    h->host_only = device < 0;
+    h->group = cfg->num_qo_heads / cfg->num_kv_heads;
+    while ((1 << h->log2_page) < cfg->page_size) ++h->log2_page;
+
+    int num_cus = cfg->num_cus;
+    if (!h->host_only) {
+        hipError_t e = hipSetDevice(device);
+        if (e != hipSuccess) {
+            release(h);
+            return hip_err(e, "hipSetDevice");
+        }
+        if (num_cus == 0) {
+            int n = 0;
+            e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device);
+            if (e != hipSuccess) {
+                release(h);
+                return hip_err(e, "hipDeviceGetAttribute(CU count)");
+            }
+            num_cus = n;
+        }
+    }
+    if (num_cus == 0) num_cus = 256;
+
+    PlanLimits &L = h->lim;
+    L.num_qo_heads = cfg->num_qo_heads;
+    L.num_kv_heads = cfg->num_kv_heads;
+    L.head_dim = cfg->head_dim;
+    L.page_size = cfg->page_size;
+    L.max_batch = cfg->max_batch;
+    L.max_qo_rows = cfg->max_qo_rows;
+    L.max_kv_pages = cfg->max_kv_pages;
+    L.num_cus = num_cus;
+    L.split_items_per_cu = cfg->split_items_per_cu > 0 ? cfg->split_items_per_cu : 2;
+    L.min_split_tokens =
+        cfg->min_split_tokens > 0 ? (int32_t)align_up(cfg->min_split_tokens, 16) : 256;
+    const int64_t blocks = fl::row_block_bound(L);
+    L.item_cap = blocks + std::max<int64_t>(8192, 8LL * num_cus * L.split_items_per_cu);
+    L.part_rows_cap = L.item_cap * fl::kBlockRows;
+    if (L.item_cap > INT32_MAX / FL_WORK_ITEM_INTS) {
+        release(h);
+        return set_err(FL_ERR_CAPACITY, "capacities too large");
+    }
+
+    const int64_t item_bytes = L.item_cap * FL_WORK_ITEM_INTS * 4;
+    const int64_t merge_bytes = blocks * fl::kMergeInts * 4;
+    h->off_merges = align_up(item_bytes, 256);
+    h->off_pages = align_up(h->off_merges + merge_bytes, 256);
+    h->meta_bytes = align_up(h->off_pages + std::max<int64_t>(1, L.max_kv_pages) * 4, 256);
+
+    if (!h->host_only) {
+        hipError_t e;
+        if ((e = hipMalloc((void **)&h->d_meta, h->meta_bytes)) != hipSuccess ||
+            (e = hipMalloc((void **)&h->d_part_o, L.part_rows_cap * cfg->head_dim * 4)) !=
+                hipSuccess ||
+            (e = hipMalloc((void **)&h->d_part_lse, L.part_rows_cap * 4)) != hipSuccess) {
+            release(h);
+            return hip_err(e, "hipMalloc (handle buffers)");
+        }
+        for (int i = 0; i < 2; ++i) {
+            if ((e = hipHostMalloc((void **)&h->h_stage[i], h->meta_bytes, hipHostMallocDefault)) !=
+                    hipSuccess ||
+                (e = hipEventCreateWithFlags(&h->ev[i], hipEventDisableTiming)) != hipSuccess) {
+                release(h);
+                return hip_err(e, "pinned staging / event");
+            }
+        }
+    }
+    *out = h;
+    return FL_OK;
+}
+
+fl_status fl_paged_attn_destroy(fl_handle h) {
+    g_last_error.clear();
+    release(h);
+    return FL_OK;
+}
+
+fl_status fl_paged_attn_plan(fl_handle h, int32_t batch, const int32_t *qo_indptr,
+                             const int32_t *kv_indptr, const int32_t *kv_indices,
+                             const int32_t *last_page_len, int64_t num_pages, int32_t causal,
+                             float sm_scale, int32_t num_splits, void *stream) {
+    g_last_error.clear();
+    if (!h) return set_err(FL_ERR_INVALID_ARG, "handle is NULL");
+    h->planned = false;
+    if (!(sm_scale == sm_scale) || std::isinf(sm_scale))
+        return set_err(FL_ERR_INVALID_ARG, "sm_scale must be finite");
+    fl::PlanInput in{batch, qo_indptr, kv_indptr, kv_indices, last_page_len,
+                     num_pages, causal ? 1 : 0, num_splits};
+    std::string err;
+    fl_status st = fl::build_plan(h->lim, in, h->plan, &err);
+    if (st != FL_OK) return set_err(st, err);
+    const double scale = sm_scale > 0.f ? (double)sm_scale : 1.0 / std::sqrt((double)h->cfg.head_dim);
+    h->scale_log2 = (float)(scale * 1.4426950408889634);
+    h->causal = causal ? 1 : 0;
+
+    if (!h->host_only && batch > 0) {
+        hipError_t e = hipSetDevice(h->device);
+        if (e != hipSuccess) return hip_err(e, "hipSetDevice");
+        const int slot = h->cur;
+        h->cur ^= 1;
+        if (h->ev_live[slot]) {
+            // the copy that last used this staging buffer must have finished reading it
+            if ((e = hipEventSynchronize(h->ev[slot])) != hipSuccess)
+                return hip_err(e, "hipEventSynchronize (staging)");
+        }
+        char *st_buf = h->h_stage[slot];
+        const Plan &p = h->plan;
+        std::memcpy(st_buf, p.items.data(), p.items.size() * 4);
+        if (!p.merges.empty())
+            std::memcpy(st_buf + h->off_merges, p.merges.data(), p.merges.size() * 4);
+        if (p.nnz > 0) std::memcpy(st_buf + h->off_pages, kv_indices, (size_t)p.nnz * 4);
+        // one transfer covers [items .. end of page table]
+        const int64_t bytes = h->off_pages + p.nnz * 4;
+        hipStream_t s = (hipStream_t)stream;
+        if ((e = hipMemcpyAsync(h->d_meta, st_buf, bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
+            return hip_err(e, "hipMemcpyAsync (plan)");
+        if ((e = hipEventRecord(h->ev[slot], s)) != hipSuccess)
+            return hip_err(e, "hipEventRecord (plan)");
+        h->ev_live[slot] = true;
+    }
+    h->planned = true;
+    return FL_OK;
+}
+
+fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, const void *v_pool,
+                            void *out, float *lse, void *stream) {
+    g_last_error.clear();
+    if (!h) return set_err(FL_ERR_INVALID_ARG, "handle is NULL");
+    if (h->host_only) return set_err(FL_ERR_UNSUPPORTED, "run() on a host-only handle");
+    if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "run() before a successful plan()");
+    const Plan &p = h->plan;
+    if (p.num_items == 0) return FL_OK;
+    if (!q || !k_pool || !v_pool || !out)
+        return set_err(FL_ERR_INVALID_ARG, "q, k_pool, v_pool and out must not be NULL");
+    if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)out) & 15)
+        return set_err(FL_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
+
+    fl::AttnArgs a{};
+    a.items = (const int32_t *)h->d_meta;
+    a.kv_indices = (const int32_t *)(h->d_meta + h->off_pages);
+    a.q = q;
+    a.k = k_pool;
+    a.v = v_pool;
+    a.out = out;
+    a.lse = lse;
+    a.part_o = h->d_part_o;
+    a.part_lse = h->d_part_lse;
+    a.num_qo_heads = h->cfg.num_qo_heads;
+    a.num_kv_heads = h->cfg.num_kv_heads;
+    a.group = h->group;
+    a.log2_page = h->log2_page;
+    a.causal = h->causal;
+    a.scale_log2 = h->scale_log2;
+    int e = fl::launch_attention(h->cfg.dtype, h->cfg.head_dim, p.num_items, a, stream);
+    if (e != (int)hipSuccess) return hip_err((hipError_t)e, "attention launch");
+    if (p.num_merges > 0) {
+        fl::MergeArgs m{};
+        m.merges = (const int32_t *)(h->d_meta + h->off_merges);
+        m.part_o = h->d_part_o;
+        m.part_lse = h->d_part_lse;
+        m.out = out;
+        m.lse = lse;
+        m.num_qo_heads = h->cfg.num_qo_heads;
+        m.group = h->group;
+        e = fl::launch_merge(h->cfg.dtype, h->cfg.head_dim, p.num_merges, m, stream);
+        if (e != (int)hipSuccess) return hip_err((hipError_t)e, "merge launch");
+    }
+    return FL_OK;
+}
+
+fl_status fl_paged_attn_plan_info(fl_handle h, int32_t *num_work_items, int32_t *max_splits,
+                                  int64_t *workspace_bytes) {
+    g_last_error.clear();
+    if (!h) return set_err(FL_ERR_INVALID_ARG, "handle is NULL");
+    if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "no plan");
+    if (num_work_items) *num_work_items = h->plan.num_items;
+    if (max_splits) *max_splits = h->plan.max_splits;
+    if (workspace_bytes) *workspace_bytes = h->plan.part_rows * ((int64_t)h->cfg.head_dim + 1) * 4;
+    return FL_OK;
+}
+
+fl_status fl_paged_attn_get_work_items(fl_handle h, int32_t *items, int32_t capacity,
+                                       int32_t *num_items) {
+    g_last_error.clear();
+    if (!h) return set_err(FL_ERR_INVALID_ARG, "handle is NULL");
+    if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "no plan");
+    if (capacity < 0 || (capacity > 0 && !items))
+        return set_err(FL_ERR_INVALID_ARG, "items is NULL or capacity < 0");
+    const int32_t n = std::min(capacity, h->plan.num_items);
+    if (n > 0) std::memcpy(items, h->plan.items.data(), (size_t)n * FL_WORK_ITEM_INTS * 4);
+    if (num_items) *num_items = h->plan.num_items;
+    return FL_OK;
+}
+
+}  // extern "C"

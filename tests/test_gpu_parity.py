@@ -1,0 +1,280 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C interface.
+
+Tolerances (max-abs against the unrounded fp64 oracle): 4e-3 for bf16/fp16 outputs and
+1e-5 for fp32; where the output type's own half-ulp at a cell's magnitude is larger than
+4e-3 (bf16 |o| >= 2), half an ulp plus 1e-4 (see gpu_helpers.tolerance). Page-table indexing is checked bit-exactly with needle keys, and page
+permutation, repeated runs and single-key histories give bit-identical results.
+Unused slots and pages of every pool hold NaN.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_gqa_plan_amd as fl
+import workloads as W
+from gpu_helpers import DeviceBatch, announce, compare, to_host_bits, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(b, num_splits=0, what="", **cfg_kw):
+    announce(f"{what or b.name}: dtype={b.dtype} B={b.batch_size} rows={b.rows} "
+             f"D={b.head_dim} P={b.page_size} G={b.group} splits={num_splits}")
+    ref_out, ref_lse = oracle.attention(b)
+    d = DeviceBatch(b, num_splits=num_splits, **cfg_kw)
+    out, lse = d.run()
+    compare(b, out, lse, ref_out, ref_lse, what or b.name)
+    return d, ref_out
+
+
+# ---- the five workloads at full size, planner defaults (the benchmark's launch setup) ----
+def test_tiny_decode():
+    _check(W.tiny_decode())
+
+
+def test_saturated_decode_full():
+    _check(W.saturated_decode())
+
+
+def test_mixed_length_decode_full():
+    _check(W.mixed_length_decode())
+
+
+def test_long_context_skew_full():
+    _check(W.long_context_skew())
+
+
+def test_ragged_mixed_step_full():
+    _check(W.ragged_mixed_step())
+
+
+# ---- forced slice counts: the merge path ------------------------------------------------
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 1000])
+def test_split_counts(splits):
+    b = W.make_batch([1, 17, 100, 300, 777], [1, 1, 1, 40, 1], num_qo_heads=14, num_kv_heads=2,
+                     head_dim=64, page_size=16, dtype="bf16", seed=21, num_pages=120)
+    _check(b, num_splits=splits, what=f"splits{splits}")
+
+
+# ---- dtype / head_dim / page_size / group coverage ----------------------------------------
+VARIANTS = [
+    dict(dtype="bf16", D=64, P=16, Hq=14, Hkv=2),
+    dict(dtype="bf16", D=128, P=64, Hq=12, Hkv=2),
+    dict(dtype="f16", D=64, P=32, Hq=14, Hkv=2),
+    dict(dtype="f16", D=128, P=256, Hq=12, Hkv=2),
+    dict(dtype="f32", D=64, P=16, Hq=14, Hkv=2),
+    dict(dtype="f32", D=128, P=256, Hq=12, Hkv=2),
+    dict(dtype="bf16", D=64, P=16, Hq=2, Hkv=2),      # G = 1
+    dict(dtype="f16", D=128, P=128, Hq=16, Hkv=1),    # G = 16: a full 16-row block
+    dict(dtype="bf16", D=64, P=16, Hq=32, Hkv=1),     # G = 32: two row blocks per decode row
+    dict(dtype="f32", D=64, P=64, Hq=8, Hkv=8),       # MHA
+]
+
+
+@pytest.mark.parametrize("v", VARIANTS, ids=lambda v: f"{v['dtype']}-D{v['D']}-P{v['P']}-G{v['Hq']//v['Hkv']}")
+@pytest.mark.parametrize("ragged", [False, True])
+def test_variants(v, ragged):
+    kv = [1, 15, 16, 17, 255, 256, 257, 1000]
+    qo = [1, 1, 9, 1, 1, 100, 1, 33] if ragged else None
+    P = v["P"]
+    b = W.make_batch(kv, qo, num_qo_heads=v["Hq"], num_kv_heads=v["Hkv"], head_dim=v["D"],
+                     page_size=P, dtype=v["dtype"], seed=31,
+                     num_pages=sum(-(-k // P) for k in kv) + 7)
+    _check(b, what=f"variant-{v}-ragged{ragged}")
+
+
+def test_fp32_long_context_skew_reduced():
+    b = W.make_batch(W.long_context_lengths(0, long_len=8192), num_qo_heads=12, num_kv_heads=2,
+                     head_dim=128, page_size=256, dtype="f32", seed=0)
+    _check(b, what="f32-long-context-skew-8192")
+
+
+def test_fp32_saturated_decode():
+    _check(W.saturated_decode(dtype="f32"), what="f32-saturated")
+
+
+def test_non_causal_prefill():
+    b = W.make_batch([60, 9, 300], [7, 3, 20], num_qo_heads=4, num_kv_heads=2, head_dim=64,
+                     page_size=16, dtype="f32", causal=False, seed=3)
+    _check(b, what="non-causal")
+
+
+def test_request_with_no_query_rows():
+    b = W.make_batch([40, 70, 5], [3, 0, 1], num_qo_heads=14, num_kv_heads=2, head_dim=64,
+                     page_size=16, dtype="bf16", seed=4)
+    _check(b, what="zero-row request")
+
+
+def test_custom_scale():
+    b = W.make_batch([33, 200], num_qo_heads=14, num_kv_heads=2, head_dim=64, page_size=16,
+                     dtype="bf16", seed=5, sm_scale=0.05)
+    _check(b, what="scale 0.05")
+
+
+# ---- bit-exact facts ----------------------------------------------------------------------
+def _needle_batch(kv_lens, qo_lens, P, dtype):
+    b = W.make_batch(kv_lens, qo_lens, num_qo_heads=14, num_kv_heads=2, head_dim=64, page_size=P,
+                     dtype=dtype, seed=11, num_pages=sum(-(-k // P) for k in kv_lens) + 9)
+    zero = W.to_storage(np.zeros(1, np.float32), dtype)[0]
+    for r, kl in enumerate(kv_lens):
+        pages = b.kv_indices[b.kv_indptr[r]:b.kv_indptr[r + 1]]
+        for t in range(kl):
+            pg, sl = pages[t // P], t % P
+            b.k_pool[pg, sl] = zero
+            row = np.zeros((2, 64), np.float32)
+            row[:, 0] = r + 1
+            row[:, 1] = t % 256
+            row[:, 2] = t // 256
+            row[:, 3] = np.array([1, 2])
+            row[:, 4:] = ((np.arange(60) * 7 + t + 3 * r) % 251) - 125
+            b.v_pool[pg, sl] = W.to_storage(row, dtype)
+    b.q[:] = zero
+    return b
+
+
+def _plant(b, r, t, rows=None):
+    P = b.page_size
+    pg = b.kv_indices[b.kv_indptr[r] + t // P]
+    b.k_pool[pg, t % P, :, 0] = W.to_storage(np.array([256.0], np.float32), b.dtype)[0]
+    q0, q1 = int(b.qo_indptr[r]), int(b.qo_indptr[r + 1])
+    sel = slice(q0, q1) if rows is None else rows
+    b.q[sel, :, 0] = W.to_storage(np.array([32.0], np.float32), b.dtype)[0]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("P", [16, 64, 256])
+@pytest.mark.parametrize("splits", [0, 1, 4])
+def test_needles_bit_exact(dtype, P, splits):
+    kv = [1, P, P + 1, 3 * P - 1, 300, 1000]
+    spots = [0, P - 1, P, 3 * P - 2, 299, 517]
+    b = _needle_batch(kv, None, P, dtype)
+    for r, t in enumerate(spots):
+        _plant(b, r, t)
+    announce(f"needles dtype={dtype} P={P} splits={splits}")
+    d = DeviceBatch(b, num_splits=splits)
+    out, _ = d.run()
+    got = to_host_bits(out, dtype)
+    for r, t in enumerate(spots):
+        pg = b.kv_indices[b.kv_indptr[r] + t // P]
+        for h in range(14):
+            want = b.v_pool[pg, t % P, h // 7]
+            assert np.array_equal(got[r, h].view(np.uint8), np.ascontiguousarray(want).view(np.uint8)), (r, t, h)
+
+
+def test_causal_limit_needles_bit_exact():
+    P = 16
+    b = _needle_batch([70, 300], [20, 1], P, "bf16")
+    i = 9
+    lim = 70 - 20 + i
+    pg = b.kv_indices[lim // P]
+    b.k_pool[pg, lim % P, :, 0] = W.to_storage(np.array([256.0], np.float32), "bf16")[0]
+    b.q[i, :, 0] = W.to_storage(np.array([32.0], np.float32), "bf16")[0]
+    # row i+1 plants nothing but sees the needle too; rows < i do not see it
+    announce("causal-limit needles")
+    ref, _ = oracle.attention(b)
+    d = DeviceBatch(b)
+    out, lse = d.run()
+    got = to_host_bits(out, "bf16")
+    assert np.array_equal(got[i, 0], b.v_pool[pg, lim % P, 0])
+    compare(b, out, lse, ref, oracle.attention(b)[1], "causal-limit needles")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_single_key_history_is_exact(dtype):
+    b = W.make_batch([1] * 5, num_qo_heads=12, num_kv_heads=2, head_dim=128, page_size=16,
+                     dtype=dtype, seed=6, keep_dense=True)
+    announce(f"single-key {dtype}")
+    d = DeviceBatch(b)
+    out, _ = d.run()
+    got = to_host_bits(out, dtype)
+    for r in range(5):
+        for h in range(12):
+            assert np.array_equal(np.ascontiguousarray(got[r, h]).view(np.uint8),
+                                  np.ascontiguousarray(b.dense_v[r][0, h // 6]).view(np.uint8))
+
+
+def test_page_permutation_bit_identical():
+    b = W.mixed_length_decode()
+    b2 = W.relabel_pages(b, W.rng_for(77, 0, 0).permutation(b.num_pages))
+    announce("page permutation")
+    o1, l1 = DeviceBatch(b).run()
+    o2, l2 = DeviceBatch(b2).run()
+    assert np.array_equal(to_host_bits(o1, "f16").view(np.uint16), to_host_bits(o2, "f16").view(np.uint16))
+    assert np.array_equal(l1.cpu().numpy().view(np.uint32), l2.cpu().numpy().view(np.uint32))
+
+
+def test_repeated_runs_bit_identical():
+    b = W.ragged_mixed_step()
+    announce("determinism")
+    d = DeviceBatch(b)
+    o1 = to_host_bits(d.run()[0], "bf16").copy()
+    for _ in range(3):
+        assert np.array_equal(to_host_bits(d.run()[0], "bf16"), o1)
+
+
+def test_page_size_relayout_within_tolerance():
+    outs = []
+    for P in (16, 64, 256):
+        kv = [1, 17, 100, 300, 513]
+        b = W.make_batch(kv, [1, 1, 1, 9, 1], num_qo_heads=14, num_kv_heads=2, head_dim=64,
+                         page_size=P, dtype="bf16", seed=8, num_pages=sum(-(-k // P) for k in kv) + 3)
+        announce(f"relayout P={P}")
+        d, ref = _check(b, what=f"relayout P{P}")
+        outs.append(to_host_f64(d.out))
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 8e-3
+
+
+# ---- one plan, many layers; re-planning ---------------------------------------------------
+def test_one_plan_many_layers_and_replanning():
+    import dataclasses
+
+    import torch
+    b1 = W.tiny_decode(seed=1)
+    # a second layer: same page table, different pool contents (K and V swapped)
+    b2 = dataclasses.replace(b1, k_pool=b1.v_pool.copy(), v_pool=b1.k_pool.copy())
+    announce("layers + replanning")
+    d1 = DeviceBatch(b1)
+    d2 = DeviceBatch(b2, handle=d1.h)
+    r1, r2 = oracle.attention(b1), oracle.attention(b2)
+    for _ in range(3):
+        d1.plan(); o, l = d1.run(); compare(b1, o, l, *r1, "layer A")
+        o, l = d2.run(); compare(b2, o, l, *r2, "layer B under the same plan")
+    b3 = W.saturated_decode(seed=3)
+    d3 = DeviceBatch(b3, handle=fl.PagedAttention(
+        fl.make_config(14, 2, 64, 16, "bf16", 256, 256, 8192), device=0))
+    r3 = oracle.attention(b3)
+    b4 = W.make_batch([5, 700, 40], num_qo_heads=14, num_kv_heads=2, head_dim=64, page_size=16,
+                      dtype="bf16", seed=4, num_pages=60)
+    d4 = DeviceBatch(b4, handle=d3.h)
+    r4 = oracle.attention(b4)
+    for _ in range(3):                            # alternate plans: staging buffers rotate
+        d3.plan(); o, l = d3.run(); compare(b3, o, l, *r3, "plan 3")
+        d4.plan(); o, l = d4.run(); compare(b4, o, l, *r4, "plan 4")
+    torch.cuda.synchronize()
+
+
+def test_empty_batch_run_is_noop():
+    import torch
+    h = fl.PagedAttention(fl.make_config(14, 2, 64, 16, "bf16", 4, 4, 16), device=0)
+    h.plan(np.zeros(1, np.int32), np.zeros(1, np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32), 1)
+    x = torch.zeros(16, device="cuda:0")
+    h.run(x, x, x, x)
+    torch.cuda.synchronize()
+
+
+def test_run_errors():
+    import torch
+    h = fl.PagedAttention(fl.make_config(14, 2, 64, 16, "bf16", 4, 4, 64), device=0)
+    x = torch.zeros(1024, device="cuda:0")
+    with pytest.raises(fl.FlError) as e:
+        h.run(x, x, x, x)
+    assert e.value.status == fl.FL_ERR_NOT_PLANNED
+    b = W.tiny_decode()
+    h.plan(b.qo_indptr, b.kv_indptr, b.kv_indices, b.last_page_len, b.num_pages)
+    with pytest.raises(fl.FlError) as e:
+        fl.fl_paged_attn_run(h.handle, x.data_ptr() + 2, x.data_ptr(), x.data_ptr(), x.data_ptr())
+    assert e.value.status == fl.FL_ERR_INVALID_ARG
+    with pytest.raises(fl.FlError) as e:
+        fl.fl_paged_attn_run(h.handle, 0, x.data_ptr(), x.data_ptr(), x.data_ptr())
+    assert e.value.status == fl.FL_ERR_INVALID_ARG

@@ -1,0 +1,229 @@
+"""Host-side checks of the C interface: exported symbols and the planner (no GPU needed).
+
+The planner is exercised through host-only handles (device = -1), which validate the
+metadata and build the work list without any HIP call.
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_gqa_plan_amd as fl
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fl_paged_attn.h")
+
+
+def test_library_exports_every_declared_function():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:fl_status|const char \*)\s*(fl_\w+)\s*\(", text, re.M))
+    assert declared == set(fl.EXPORTED)
+    lib = fl.load_library()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def host_handle(Hq=14, Hkv=2, D=64, P=16, dtype="bf16", max_batch=256, max_rows=4096,
+                max_pages=1 << 20, **kw):
+    return fl.PagedAttention(fl.make_config(Hq, Hkv, D, P, dtype, max_batch, max_rows, max_pages,
+                                            **kw), device=-1)
+
+
+def plan_batch(h, b, num_splits=0, causal=None):
+    h.plan(b.qo_indptr, b.kv_indptr, b.kv_indices, b.last_page_len, b.num_pages,
+           causal=b.causal if causal is None else causal, num_splits=num_splits)
+    return h.work_items()
+
+
+def check_coverage(items, b, causal=True):
+    """Every (request, kv head, flattened row) sees exactly its causal key range, once, in
+    16-aligned non-empty slices; split items own disjoint partial rows."""
+    G = b.group
+    idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
+    col = lambda n: items[:, idx[n]]
+    assert (col("num_rows") >= 1).all() and (col("num_rows") <= 16).all()
+    assert (col("tok_end") > col("tok_begin")).all()
+    assert (col("tok_begin") % 16 == 0).all()
+    cover = {}
+    for it in items:
+        key = (it[idx["request"]], it[idx["kv_head"]], it[idx["row_begin"]], it[idx["num_rows"]])
+        cover.setdefault(key, []).append((it[idx["tok_begin"]], it[idx["tok_end"]], it[idx["split"]],
+                                          it[idx["num_splits"]], it[idx["part_row"]]))
+    seen_rows = {}
+    part_used = set()
+    for (r, h, f0, nr), sl in cover.items():
+        kl, ql = int(b.kv_lens[r]), int(b.qo_lens[r])
+        i_last = (f0 + nr - 1) // G
+        kv_end = kl - ql + i_last + 1 if causal else kl
+        sl.sort()
+        assert sl[0][0] == 0 and sl[-1][1] == kv_end
+        for a, c in zip(sl, sl[1:]):
+            assert a[1] == c[0]
+        ns = sl[0][3]
+        assert len(sl) == ns and sorted(s[2] for s in sl) == list(range(ns))
+        if ns == 1:
+            assert sl[0][4] == -1
+        else:
+            for s in sl:
+                rows = set(range(s[4], s[4] + nr))
+                assert not (rows & part_used)
+                part_used |= rows
+        for f in range(f0, f0 + nr):
+            seen_rows[(r, h, f)] = seen_rows.get((r, h, f), 0) + 1
+    for r in range(b.batch_size):
+        for h in range(b.num_kv_heads):
+            for f in range(int(b.qo_lens[r]) * G):
+                assert seen_rows.get((r, h, f)) == 1, (r, h, f)
+    # the items carry the right request facts
+    for it in items:
+        r = it[idx["request"]]
+        assert it[idx["q_start"]] == b.qo_indptr[r] and it[idx["qo_len"]] == b.qo_lens[r]
+        assert it[idx["kv_len"]] == b.kv_lens[r] and it[idx["page_base"]] == b.kv_indptr[r]
+
+
+SHAPES = {
+    "tiny_decode": lambda: W.tiny_decode(),
+    "saturated_decode": lambda: W.saturated_decode(),
+    "mixed_length_decode": lambda: W.make_batch(W.mixed_length_lengths(0), num_qo_heads=12, num_kv_heads=2,
+                                                head_dim=64, page_size=256, dtype="f16", num_pages=1024),
+    "long_context_skew": lambda: W.make_batch(W.long_context_lengths(0, long_len=4096), num_qo_heads=12,
+                                              num_kv_heads=2, head_dim=64, page_size=256, dtype="f16"),
+    "ragged_mixed_step": lambda: W.make_batch(*W.ragged_mixed_lengths(0), num_qo_heads=14, num_kv_heads=2,
+                                              head_dim=64, page_size=16, dtype="bf16", num_pages=8192),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SHAPES))
+@pytest.mark.parametrize("splits", [0, 1, 3, 1000])
+def test_plan_covers_every_row_and_key_once(name, splits):
+    b = SHAPES[name]()
+    h = host_handle(Hq=b.num_qo_heads, Hkv=b.num_kv_heads, D=64, P=b.page_size, dtype=b.dtype)
+    if name == "ragged_mixed_step" and splits == 1000:
+        # every 16-key tile its own slice: beyond the handle's item capacity, reported as such
+        assert "work items" in _expect(fl.FL_ERR_CAPACITY, plan_batch, h, b, num_splits=splits)
+        return
+    items = plan_batch(h, b, num_splits=splits)
+    check_coverage(items, b)
+    n, ms, ws = h.info()
+    assert n == len(items)
+    if splits == 1:
+        assert ms == 1 and ws == 0
+
+
+def test_plan_non_causal_prefill_covers_whole_history():
+    b = W.make_batch([60, 9, 300], [7, 3, 20], num_qo_heads=4, num_kv_heads=2, head_dim=64,
+                     page_size=16, dtype="f32", causal=False)
+    h = host_handle(Hq=4, Hkv=2, P=16, dtype="f32")
+    items = plan_batch(h, b)
+    check_coverage(items, b, causal=False)
+
+
+def test_plan_depends_only_on_lengths():
+    b = W.saturated_decode()
+    b2 = W.relabel_pages(b, W.rng_for(5, 0, 0).permutation(b.num_pages))
+    h = host_handle()
+    i1 = plan_batch(h, b)
+    i2 = plan_batch(h, b2)
+    assert np.array_equal(i1, i2)
+    assert np.array_equal(plan_batch(h, b), i1)   # and deterministic
+
+
+def test_long_histories_are_spread_and_short_ones_kept_whole():
+    lens = W.long_context_lengths(0)
+    b = W.make_batch(lens, num_qo_heads=12, num_kv_heads=2, head_dim=64, page_size=256,
+                     dtype="f16", num_pages=1200, poison=False)
+    h = host_handle(Hq=12, Hkv=2, P=256, dtype="f16", max_pages=4096)
+    items = plan_batch(h, b)
+    idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
+    kvl = items[:, idx["kv_len"]]
+    ns = items[:, idx["num_splits"]]
+    assert ns[kvl == 32768].min() >= 16        # one long history runs on many CUs
+    assert ns[kvl == 512].max() <= 2
+    assert len(items) >= 256                    # enough workgroups to fill the chip
+    # launch order: longest slices first
+    span = items[:, idx["tok_end"]] - items[:, idx["tok_begin"]]
+    assert (np.diff(span) <= 0).all()
+
+
+def test_forced_splits_are_capped_by_tiles():
+    b = W.tiny_decode()
+    h = host_handle()
+    items = plan_batch(h, b, num_splits=1000)
+    idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
+    for it in items:
+        assert it[idx["num_splits"]] == -(-int(b.kv_lens[it[idx["request"]]]) // 16)
+
+
+def _expect(status, fn, *a, **kw):
+    with pytest.raises(fl.FlError) as e:
+        fn(*a, **kw)
+    assert e.value.status == status, str(e.value)
+    return str(e.value)
+
+
+def test_plan_rejects_bad_metadata_with_codes():
+    b = W.tiny_decode()
+    h = host_handle()
+    good = dict(qo_indptr=b.qo_indptr, kv_indptr=b.kv_indptr, kv_indices=b.kv_indices,
+                last_page_len=b.last_page_len, num_pages=b.num_pages)
+
+    def plan(**kw):
+        a = {**good, **kw}
+        h.plan(a["qo_indptr"], a["kv_indptr"], a["kv_indices"], a["last_page_len"], a["num_pages"])
+
+    bad = b.kv_indices.copy(); bad[5] = b.num_pages
+    assert "kv_indices" in _expect(fl.FL_ERR_INVALID_ARG, plan, kv_indices=bad)
+    bad = b.kv_indices.copy(); bad[0] = -1
+    _expect(fl.FL_ERR_INVALID_ARG, plan, kv_indices=bad)
+    last = b.last_page_len.copy(); last[2] = 0
+    assert "last_page_len" in _expect(fl.FL_ERR_INVALID_ARG, plan, last_page_len=last)
+    last[2] = 17
+    _expect(fl.FL_ERR_INVALID_ARG, plan, last_page_len=last)
+    kvp = b.kv_indptr.copy(); kvp[2] = kvp[1]                    # a request with no pages
+    _expect(fl.FL_ERR_INVALID_ARG, plan, kv_indptr=kvp)
+    kvp = b.kv_indptr.copy(); kvp[0] = 1
+    _expect(fl.FL_ERR_INVALID_ARG, plan, kv_indptr=kvp)
+    qo = np.array([0, 1, 2, 1, 2], np.int32)                      # decreasing
+    _expect(fl.FL_ERR_INVALID_ARG, plan, qo_indptr=qo)
+    qo = np.array([0, 1, 3, 4, 5], np.int32)                      # 2 rows on a 17... fine
+    plan(qo_indptr=qo)
+    qo = np.array([0, 2, 3, 4, 5], np.int32)                      # 2 causal rows on 1 token
+    assert "causal" in _expect(fl.FL_ERR_INVALID_ARG, plan, qo_indptr=qo)
+    _expect(fl.FL_ERR_INVALID_ARG, plan, num_pages=0)
+    # a failed plan leaves the handle un-planned
+    assert "no plan" in _expect(fl.FL_ERR_NOT_PLANNED, h.info)
+    with pytest.raises(fl.FlError):
+        h.work_items()
+
+
+def test_capacity_limits():
+    b = W.tiny_decode()
+    h = host_handle(max_batch=3)
+    _expect(fl.FL_ERR_CAPACITY, plan_batch, h, b)
+    h = host_handle(max_rows=3)
+    _expect(fl.FL_ERR_CAPACITY, plan_batch, h, b)
+    h = host_handle(max_pages=20)
+    _expect(fl.FL_ERR_CAPACITY, plan_batch, h, b)
+
+
+def test_empty_batch_plans_to_nothing():
+    h = host_handle()
+    h.plan(np.zeros(1, np.int32), np.zeros(1, np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32), 1)
+    assert h.info()[0] == 0
+
+
+def test_create_rejects_unsupported_configs():
+    for kw in (dict(D=96), dict(D=32), dict(P=8), dict(P=512), dict(P=48)):
+        _expect(fl.FL_ERR_UNSUPPORTED, host_handle, **kw)
+    _expect(fl.FL_ERR_INVALID_ARG, host_handle, Hq=14, Hkv=4)
+    cfg = fl.make_config(14, 2, 64, 16, "bf16", 8, 8, 64)
+    cfg.dtype = 7
+    _expect(fl.FL_ERR_UNSUPPORTED, fl.fl_paged_attn_create, cfg, -1)
+
+
+def test_run_needs_a_device_handle_and_a_plan():
+    h = host_handle()
+    msg = _expect(fl.FL_ERR_UNSUPPORTED, fl.fl_paged_attn_run, h.handle, 16, 16, 16, 16)
+    assert "host-only" in msg
