@@ -116,8 +116,9 @@ def main(argv=None):
     ap.add_argument("--layers", type=int, default=0, help="per-layer pools (0: 24 or 28 by workload)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0, help="planner slice override (0 = automatic)")
-    ap.add_argument("--items-per-cu", type=int, default=0)
-    ap.add_argument("--min-split-tokens", type=int, default=0)
+    ap.add_argument("--groups-per-cu", type=int, default=0)
+    ap.add_argument("--min-group-tokens", type=int, default=0)
+    ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (4 or 8; 0 = default)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -158,7 +159,8 @@ def main(argv=None):
 
     cfg = fl.make_config(b.num_qo_heads, b.num_kv_heads, b.head_dim, b.page_size, b.dtype,
                          b.batch_size, b.rows, int(b.kv_indptr[-1]),
-                         split_items_per_cu=args.items_per_cu, min_split_tokens=args.min_split_tokens)
+                         groups_per_cu=args.groups_per_cu, min_group_tokens=args.min_group_tokens,
+                         waves_per_group=args.waves)
     h = fl.PagedAttention(cfg, device=0)
     stream = torch.cuda.current_stream()
 
@@ -178,7 +180,7 @@ def main(argv=None):
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
-    n_items, max_splits, ws_bytes = h.info()
+    n_items, n_groups, max_splits, ws_bytes = h.info()
 
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(L)] for _ in range(args.steps)]
@@ -220,7 +222,8 @@ def main(argv=None):
                    "kv_tokens": int(b.kv_lens.sum()), "num_qo_heads": b.num_qo_heads,
                    "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
                    "page_size": b.page_size, "pool_pages": b.num_pages, "layers": L,
-                   "seed": args.seed, "splits": args.splits, "parallelism": "single GPU"},
+                   "seed": args.seed, "splits": args.splits, "waves": args.waves,
+                   "parallelism": "single GPU"},
         "us_per_call": round(us_call, 3),
         "us_per_call_median": round(us_call_med, 3),
         "kv_bytes_per_call": kv_bytes,
@@ -228,6 +231,7 @@ def main(argv=None):
         "attention_us_per_step": round(us_call * L, 2),
         "plan_host_us": round(plan_us, 2),
         "work_items": n_items,
+        "workgroups": n_groups,
         "max_splits": max_splits,
         "workspace_bytes": ws_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

@@ -80,10 +80,13 @@ typedef struct {
     int64_t max_kv_pages;      /* most page-table entries one plan may hold              */
     int32_t num_cus;           /* compute units to plan for; 0 = ask the device
                                   (a host-only handle then plans for 256)                */
-    int32_t split_items_per_cu;/* target slices per compute unit when splitting long
-                                  histories; 0 = library default                         */
-    int32_t min_split_tokens;  /* shortest slice the planner makes; 0 = library default  */
-    int32_t reserved;          /* must be 0                                              */
+    int32_t groups_per_cu;     /* workgroups per compute unit the plan spreads work over;
+                                  0 = library default (1)                                */
+    int32_t min_group_tokens;  /* fewest keys (per row block piece) a workgroup's share
+                                  may hold before fewer workgroups are used; 0 = default */
+    int32_t waves_per_group;   /* wavefronts per workgroup, 4 or 8; 0 = library default  */
+    int64_t max_tiles;         /* most 16-key tiles (over all row blocks) one plan may
+                                  hold; 0 = a bound derived from the other capacities     */
 } fl_config;
 
 /*
@@ -111,9 +114,9 @@ fl_status fl_paged_attn_destroy(fl_handle h);
  *   num_pages        pool size, the bound for page ids
  *   causal           nonzero: bottom-right causal mask (a no-op for single decode rows)
  *   sm_scale         softmax scale; <= 0 means 1/sqrt(head_dim)
- *   num_splits       0: the planner picks the slices from the lengths and the compute
- *                    unit count; > 0: cut every row block's keys into that many slices
- *                    (fewer when the history has fewer 16-token tiles)
+ *   num_splits       0: the planner spreads all row blocks' tiles evenly over the compute
+ *                    units; > 0: cut every row block's keys into that many pieces (fewer
+ *                    when the history has fewer 16-token tiles), one workgroup each
  *   stream           hipStream_t for the host-to-device copy (NULL: the null stream)
  * The work list depends only on the lengths, never on page ids, so two plans over the
  * same lengths give bit-identical results for any page assignment.
@@ -124,7 +127,9 @@ fl_status fl_paged_attn_plan(fl_handle h, int32_t batch, const int32_t *qo_indpt
                              float sm_scale, int32_t num_splits, void *stream);
 
 /*
- * Compute attention for one layer with the current plan. Device pointers:
+ * Compute attention for one layer with the current plan: one kernel launch. Row blocks
+ * cut into several pieces are merged inside the same launch by the piece that finishes
+ * last. Device pointers:
  *   q       [rows, num_qo_heads, head_dim]
  *   k_pool  [num_pages, page_size, num_kv_heads, head_dim]
  *   v_pool  same layout as k_pool
@@ -137,16 +142,21 @@ fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, cons
                             void *out, float *lse, void *stream);
 
 /*
- * Facts about the current plan: work items (workgroups of the attention launch), the
- * largest number of slices any row block was cut into, and the partial-result bytes the
- * plan uses. Any output pointer may be NULL.
+ * Facts about the current plan: the number of work items (segments, see below), the
+ * number of workgroups of the attention launch, the largest number of pieces any row block
+ * was cut into, and the fp32 partial-result bytes the plan uses. Outputs may be NULL.
  */
-fl_status fl_paged_attn_plan_info(fl_handle h, int32_t *num_work_items, int32_t *max_splits,
-                                  int64_t *workspace_bytes);
+fl_status fl_paged_attn_plan_info(fl_handle h, int32_t *num_work_items, int32_t *num_groups,
+                                  int32_t *max_splits, int64_t *workspace_bytes);
 
 /*
- * Copy the current plan's work list to host memory: FL_WORK_ITEM_INTS int32 per item in
- * launch order, fields as named by FL_WI_* below. *num_items receives the item count;
+ * Copy the current plan's work items to host memory: FL_WORK_ITEM_INTS int32 per item,
+ * fields as named by FL_WI_* below, ordered by workgroup. A work item (segment) is one
+ * piece of a row block: up to 16 flattened query rows (query row * G + head in group) of
+ * one request and kv head, over one range of keys. The plan lays every row block's 16-key
+ * tiles in one sequence and gives each workgroup an equal contiguous share, so a
+ * workgroup runs a few segments back to back and a long row block may span several
+ * workgroups (its pieces are merged by log-sum-exp). *num_items receives the item count;
  * at most `capacity` items are written.
  */
 #define FL_WORK_ITEM_INTS 16
@@ -156,14 +166,17 @@ enum {
     FL_WI_KV_LEN = 2,    /* cached tokens of the request                                */
     FL_WI_PAGE_BASE = 3, /* kv_indptr[request]                                          */
     FL_WI_KV_HEAD = 4,
-    FL_WI_ROW_BEGIN = 5, /* first row of the block in (query row * G + head in group)   */
+    FL_WI_ROW_BEGIN = 5, /* first flattened row of the block                            */
     FL_WI_NUM_ROWS = 6,  /* rows in the block (<= 16)                                   */
-    FL_WI_TOK_BEGIN = 7, /* key slice [tok_begin, tok_end)                               */
+    FL_WI_TOK_BEGIN = 7, /* key range [tok_begin, tok_end)                               */
     FL_WI_TOK_END = 8,
     FL_WI_PART_ROW = 9,  /* -1: writes the final output; else its rows in the workspace */
     FL_WI_REQUEST = 10,
-    FL_WI_SPLIT = 11,    /* slice index within its row block                            */
-    FL_WI_NUM_SPLITS = 12
+    FL_WI_SPLIT = 11,    /* piece index within its row block                            */
+    FL_WI_NUM_SPLITS = 12,
+    FL_WI_MERGE = 13,    /* row block's merge ticket (-1 when the block is one piece)   */
+    FL_WI_GROUP = 14,    /* workgroup that runs this item                               */
+    FL_WI_POS_BEGIN = 15 /* first step of the item in its workgroup's per-wave sequence   */
 };
 fl_status fl_paged_attn_get_work_items(fl_handle h, int32_t *items, int32_t capacity,
                                        int32_t *num_items);

@@ -25,7 +25,7 @@ FL_F16, FL_BF16, FL_F32 = 1, 2, 3
 FL_WORK_ITEM_INTS = 16
 WORK_ITEM_FIELDS = ("q_start", "qo_len", "kv_len", "page_base", "kv_head", "row_begin",
                     "num_rows", "tok_begin", "tok_end", "part_row", "request", "split",
-                    "num_splits")
+                    "num_splits", "merge", "group", "pos_begin")
 STATUS_NAMES = {0: "FL_OK", -1: "FL_ERR_INVALID_ARG", -2: "FL_ERR_UNSUPPORTED",
                 -3: "FL_ERR_CAPACITY", -4: "FL_ERR_NOT_PLANNED", -5: "FL_ERR_HIP"}
 DTYPE_CODES = {"f16": FL_F16, "bf16": FL_BF16, "f32": FL_F32}
@@ -36,8 +36,9 @@ class fl_config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_qo_rows", ctypes.c_int32), ("max_kv_pages", ctypes.c_int64),
-                ("num_cus", ctypes.c_int32), ("split_items_per_cu", ctypes.c_int32),
-                ("min_split_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("num_cus", ctypes.c_int32), ("groups_per_cu", ctypes.c_int32),
+                ("min_group_tokens", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
+                ("max_tiles", ctypes.c_int64)]
 
 
 class FlError(RuntimeError):
@@ -69,7 +70,7 @@ def load_library(path: Optional[str] = None):
     lib.fl_paged_attn_plan.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, ctypes.c_float, i32, vp]
     lib.fl_paged_attn_run.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.fl_paged_attn_plan_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
-                                            ctypes.POINTER(i64)]
+                                            ctypes.POINTER(i32), ctypes.POINTER(i64)]
     lib.fl_paged_attn_get_work_items.argtypes = [vp, vp, i32, ctypes.POINTER(i32)]
     for name in EXPORTED[:-1]:
         getattr(lib, name).restype = ctypes.c_int
@@ -129,11 +130,13 @@ def fl_paged_attn_run(h, q: int, k_pool: int, v_pool: int, out: int, lse: Option
            "fl_paged_attn_run")
 
 
-def fl_paged_attn_plan_info(h) -> Tuple[int, int, int]:
-    n, s, b = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
-    _check(load_library().fl_paged_attn_plan_info(h, ctypes.byref(n), ctypes.byref(s),
-                                                  ctypes.byref(b)), "fl_paged_attn_plan_info")
-    return n.value, s.value, b.value
+def fl_paged_attn_plan_info(h) -> Tuple[int, int, int, int]:
+    """(work items, workgroups, largest pieces per row block, workspace bytes)."""
+    n, g, s, b = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(load_library().fl_paged_attn_plan_info(h, ctypes.byref(n), ctypes.byref(g),
+                                                  ctypes.byref(s), ctypes.byref(b)),
+           "fl_paged_attn_plan_info")
+    return n.value, g.value, s.value, b.value
 
 
 def fl_paged_attn_get_work_items(h) -> np.ndarray:
@@ -150,11 +153,11 @@ def fl_paged_attn_get_work_items(h) -> np.ndarray:
 
 def make_config(num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
                 dtype: str, max_batch: int, max_qo_rows: int, max_kv_pages: int,
-                num_cus: int = 0, split_items_per_cu: int = 0,
-                min_split_tokens: int = 0) -> fl_config:
+                num_cus: int = 0, groups_per_cu: int = 0, min_group_tokens: int = 0,
+                waves_per_group: int = 0, max_tiles: int = 0) -> fl_config:
     return fl_config(num_qo_heads, num_kv_heads, head_dim, page_size, DTYPE_CODES[dtype],
-                     max_batch, max_qo_rows, max_kv_pages, num_cus, split_items_per_cu,
-                     min_split_tokens, 0)
+                     max_batch, max_qo_rows, max_kv_pages, num_cus, groups_per_cu,
+                     min_group_tokens, waves_per_group, max_tiles)
 
 
 class PagedAttention:

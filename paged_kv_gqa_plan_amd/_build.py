@@ -12,8 +12,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfl_paged_attn.so")
 SOURCES = ["plan.cpp", "api.cpp", "attn_kernels.hip"]
 ARCH = "gfx950"
-# Packed fp32 VALU forms are kept out of every kernel.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU forms are kept out of every kernel; MFMA accumulators live in ordinary
+# VGPRs (the accumulator-register form costs a copy each time the VALU touches them).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def hipcc() -> str:
@@ -23,11 +25,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build_library(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+def build_library(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-function", *DEVICE_FLAGS, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           "-Wall", "-Wno-unused-function", *DEVICE_FLAGS, *[f"-D{d}" for d in defines],
+           "-I", INCLUDE, "-I", CSRC, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -37,8 +39,8 @@ def build_library(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

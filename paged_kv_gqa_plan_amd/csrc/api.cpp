@@ -48,10 +48,11 @@ struct fl_paged_attn {
     int32_t log2_page = 0;
 
     // device buffers
-    char *d_meta = nullptr;      // [items | merges | page table]
+    char *d_meta = nullptr;      // [segments | wg_segs | wg_pos | merge tickets | step rows]
     float *d_part_o = nullptr;   // [part_rows_cap, head_dim]
     float *d_part_lse = nullptr; // [part_rows_cap]
-    int64_t off_merges = 0, off_pages = 0, meta_bytes = 0;
+    int64_t off_wg_segs = 0, off_wg_pos = 0, off_tickets = 0, off_steps = 0, meta_bytes = 0;
+    int32_t waves = 4;
 
     // pinned staging, double-buffered
     char *h_stage[2] = {nullptr, nullptr};
@@ -82,8 +83,11 @@ fl_status check_config(const fl_config *c) {
         return set_err(FL_ERR_UNSUPPORTED, "dtype must be FL_F16, FL_BF16 or FL_F32");
     if (c->max_batch < 0 || c->max_qo_rows < 0 || c->max_kv_pages < 0)
         return set_err(FL_ERR_INVALID_ARG, "capacities must be >= 0");
-    if (c->num_cus < 0 || c->split_items_per_cu < 0 || c->min_split_tokens < 0 || c->reserved)
-        return set_err(FL_ERR_INVALID_ARG, "num_cus / split knobs must be >= 0, reserved 0");
+    if (c->num_cus < 0 || c->groups_per_cu < 0 || c->min_group_tokens < 0 || c->max_tiles < 0)
+        return set_err(FL_ERR_INVALID_ARG, "num_cus, groups_per_cu, min_group_tokens and "
+                                           "max_tiles must be >= 0");
+    if (c->waves_per_group != 0 && c->waves_per_group != 4 && c->waves_per_group != 8)
+        return set_err(FL_ERR_UNSUPPORTED, "waves_per_group must be 0, 4 or 8");
     return FL_OK;
 }
 
@@ -126,6 +130,7 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
     h->device = device;
     h->host_only = device < 0;
     h->group = cfg->num_qo_heads / cfg->num_kv_heads;
+    h->waves = cfg->waves_per_group ? cfg->waves_per_group : 4;
     while ((1 << h->log2_page) < cfg->page_size) ++h->log2_page;
 
     int num_cus = cfg->num_cus;
@@ -156,22 +161,29 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
     L.max_qo_rows = cfg->max_qo_rows;
     L.max_kv_pages = cfg->max_kv_pages;
     L.num_cus = num_cus;
-    L.split_items_per_cu = cfg->split_items_per_cu > 0 ? cfg->split_items_per_cu : 2;
-    L.min_split_tokens =
-        cfg->min_split_tokens > 0 ? (int32_t)align_up(cfg->min_split_tokens, 16) : 256;
+    L.groups_per_cu = cfg->groups_per_cu > 0 ? cfg->groups_per_cu : 1;
+    L.waves = h->waves;
+    L.min_group_tiles =
+        cfg->min_group_tokens > 0 ? (int32_t)((cfg->min_group_tokens + 15) / 16) : 8;
     const int64_t blocks = fl::row_block_bound(L);
-    L.item_cap = blocks + std::max<int64_t>(8192, 8LL * num_cus * L.split_items_per_cu);
-    L.part_rows_cap = L.item_cap * fl::kBlockRows;
-    if (L.item_cap > INT32_MAX / FL_WORK_ITEM_INTS) {
+    L.group_cap = std::max<int64_t>((int64_t)num_cus * L.groups_per_cu, 16384);
+    L.seg_cap = blocks + L.group_cap;
+    // steps: every row block may read at most all of the plan's pages; each work item adds
+    // at most one ring group of padding per wave
+    const int64_t tiles_bound = blocks * ((L.max_kv_pages * L.page_size + 15) / 16 + 1) +
+                                L.seg_cap * fl::kRingDepth * h->waves;
+    L.max_tiles = cfg->max_tiles > 0 ? cfg->max_tiles : std::min<int64_t>(tiles_bound, 1LL << 24);
+    L.part_rows_cap = L.seg_cap * fl::kBlockRows;
+    if (L.seg_cap > INT32_MAX / FL_WORK_ITEM_INTS || L.max_tiles > INT32_MAX) {
         release(h);
         return set_err(FL_ERR_CAPACITY, "capacities too large");
     }
 
-    const int64_t item_bytes = L.item_cap * FL_WORK_ITEM_INTS * 4;
-    const int64_t merge_bytes = blocks * fl::kMergeInts * 4;
-    h->off_merges = align_up(item_bytes, 256);
-    h->off_pages = align_up(h->off_merges + merge_bytes, 256);
-    h->meta_bytes = align_up(h->off_pages + std::max<int64_t>(1, L.max_kv_pages) * 4, 256);
+    h->off_wg_segs = align_up(L.seg_cap * FL_WORK_ITEM_INTS * 4, 256);
+    h->off_wg_pos = align_up(h->off_wg_segs + (L.group_cap + 1) * 4, 256);
+    h->off_tickets = align_up(h->off_wg_pos + (L.group_cap + 1) * 4, 256);
+    h->off_steps = align_up(h->off_tickets + blocks * 4, 256);
+    h->meta_bytes = align_up(h->off_steps + std::max<int64_t>(1, L.max_tiles) * 4, 256);
 
     if (!h->host_only) {
         hipError_t e;
@@ -231,12 +243,15 @@ fl_status fl_paged_attn_plan(fl_handle h, int32_t batch, const int32_t *qo_indpt
         }
         char *st_buf = h->h_stage[slot];
         const Plan &p = h->plan;
-        std::memcpy(st_buf, p.items.data(), p.items.size() * 4);
-        if (!p.merges.empty())
-            std::memcpy(st_buf + h->off_merges, p.merges.data(), p.merges.size() * 4);
-        if (p.nnz > 0) std::memcpy(st_buf + h->off_pages, kv_indices, (size_t)p.nnz * 4);
-        // one transfer covers [items .. end of page table]
-        const int64_t bytes = h->off_pages + p.nnz * 4;
+        std::memcpy(st_buf, p.segs.data(), p.segs.size() * 4);
+        std::memcpy(st_buf + h->off_wg_segs, p.wg_segs.data(), p.wg_segs.size() * 4);
+        std::memcpy(st_buf + h->off_wg_pos, p.wg_pos.data(), p.wg_pos.size() * 4);
+        // merge tickets start at zero for every plan (the kernel keeps them at zero between
+        // runs: the piece that merges a row block resets its ticket)
+        std::memset(st_buf + h->off_tickets, 0, (size_t)p.num_merges * 4);
+        std::memcpy(st_buf + h->off_steps, p.step_rows.data(), p.step_rows.size() * 4);
+        // one transfer covers [segments .. end of the step rows]
+        const int64_t bytes = h->off_steps + (int64_t)p.step_rows.size() * 4;
         hipStream_t s = (hipStream_t)stream;
         if ((e = hipMemcpyAsync(h->d_meta, st_buf, bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
             return hip_err(e, "hipMemcpyAsync (plan)");
@@ -255,15 +270,18 @@ fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, cons
     if (h->host_only) return set_err(FL_ERR_UNSUPPORTED, "run() on a host-only handle");
     if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "run() before a successful plan()");
     const Plan &p = h->plan;
-    if (p.num_items == 0) return FL_OK;
+    if (p.num_groups == 0) return FL_OK;
     if (!q || !k_pool || !v_pool || !out)
         return set_err(FL_ERR_INVALID_ARG, "q, k_pool, v_pool and out must not be NULL");
     if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)out) & 15)
         return set_err(FL_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
 
     fl::AttnArgs a{};
-    a.items = (const int32_t *)h->d_meta;
-    a.kv_indices = (const int32_t *)(h->d_meta + h->off_pages);
+    a.segs = (const int32_t *)h->d_meta;
+    a.wg_segs = (const int32_t *)(h->d_meta + h->off_wg_segs);
+    a.wg_pos = (const int32_t *)(h->d_meta + h->off_wg_pos);
+    a.step_rows = (const int32_t *)(h->d_meta + h->off_steps);
+    a.tickets = (int32_t *)(h->d_meta + h->off_tickets);
     a.q = q;
     a.k = k_pool;
     a.v = v_pool;
@@ -274,32 +292,21 @@ fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, cons
     a.num_qo_heads = h->cfg.num_qo_heads;
     a.num_kv_heads = h->cfg.num_kv_heads;
     a.group = h->group;
-    a.log2_page = h->log2_page;
     a.causal = h->causal;
     a.scale_log2 = h->scale_log2;
-    int e = fl::launch_attention(h->cfg.dtype, h->cfg.head_dim, p.num_items, a, stream);
+    const int e = fl::launch_attention(h->cfg.dtype, h->cfg.head_dim, h->waves, p.num_groups, a,
+                                       stream);
     if (e != (int)hipSuccess) return hip_err((hipError_t)e, "attention launch");
-    if (p.num_merges > 0) {
-        fl::MergeArgs m{};
-        m.merges = (const int32_t *)(h->d_meta + h->off_merges);
-        m.part_o = h->d_part_o;
-        m.part_lse = h->d_part_lse;
-        m.out = out;
-        m.lse = lse;
-        m.num_qo_heads = h->cfg.num_qo_heads;
-        m.group = h->group;
-        e = fl::launch_merge(h->cfg.dtype, h->cfg.head_dim, p.num_merges, m, stream);
-        if (e != (int)hipSuccess) return hip_err((hipError_t)e, "merge launch");
-    }
     return FL_OK;
 }
 
-fl_status fl_paged_attn_plan_info(fl_handle h, int32_t *num_work_items, int32_t *max_splits,
-                                  int64_t *workspace_bytes) {
+fl_status fl_paged_attn_plan_info(fl_handle h, int32_t *num_work_items, int32_t *num_groups,
+                                  int32_t *max_splits, int64_t *workspace_bytes) {
     g_last_error.clear();
     if (!h) return set_err(FL_ERR_INVALID_ARG, "handle is NULL");
     if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "no plan");
-    if (num_work_items) *num_work_items = h->plan.num_items;
+    if (num_work_items) *num_work_items = h->plan.num_segs;
+    if (num_groups) *num_groups = h->plan.num_groups;
     if (max_splits) *max_splits = h->plan.max_splits;
     if (workspace_bytes) *workspace_bytes = h->plan.part_rows * ((int64_t)h->cfg.head_dim + 1) * 4;
     return FL_OK;
@@ -312,9 +319,9 @@ fl_status fl_paged_attn_get_work_items(fl_handle h, int32_t *items, int32_t capa
     if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "no plan");
     if (capacity < 0 || (capacity > 0 && !items))
         return set_err(FL_ERR_INVALID_ARG, "items is NULL or capacity < 0");
-    const int32_t n = std::min(capacity, h->plan.num_items);
-    if (n > 0) std::memcpy(items, h->plan.items.data(), (size_t)n * FL_WORK_ITEM_INTS * 4);
-    if (num_items) *num_items = h->plan.num_items;
+    const int32_t n = std::min(capacity, h->plan.num_segs);
+    if (n > 0) std::memcpy(items, h->plan.segs.data(), (size_t)n * FL_WORK_ITEM_INTS * 4);
+    if (num_items) *num_items = h->plan.num_segs;
     return FL_OK;
 }
 

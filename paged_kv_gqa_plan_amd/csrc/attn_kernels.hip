@@ -1,13 +1,20 @@
-// gfx950 kernels for paged grouped-query attention: split-KV partial attention over
-// 16-key tiles and the log-sum-exp merge of partials.
+// gfx950 kernel for paged grouped-query attention: split-KV partial attention over
+// 16-key tiles with the log-sum-exp merge of partials done in the same launch.
 //
-// One workgroup runs one work item: a row block (up to 16 flattened query rows of one
-// request and kv head, all sharing one K/V stream) over one key slice. Its waves take the
-// slice's 16-key tiles round-robin, each keeping an online softmax state, and fold their
-// states together in LDS at the end. A slice that covers its block's whole key range
-// writes the final output; otherwise it writes an fp32 partial (o, lse) that the merge
-// kernel combines ("A library kernel for decode", What changed: per-slice partial
-// results merged into one).
+// A row block is up to 16 flattened query rows of one request and kv head, all sharing
+// one K/V stream; its keys form 16-key tiles. Long histories are cut into pieces on
+// several compute units and the partial results merged ("A library kernel for decode",
+// What changed: per-slice partial results merged into one).
+//
+// Work layout. The plan gives each workgroup an equal contiguous share of all row blocks'
+// tiles: a list of segments (pieces of row blocks) whose tiles the waves take round-robin
+// across the whole share. Each tile's pool row was resolved by the plan, so the loads need
+// no page table and no segment state: each wave keeps PF tiles of K and V in flight in a
+// register ring across segment boundaries, refilling a slot as soon as its tile is
+// consumed. Segment headers arrive two segments ahead and Q one segment ahead; at each
+// segment's end the waves fold their softmax states in LDS and write the output rows, or,
+// for a row block cut by a share boundary, fp32 partial rows. The piece of a cut block that
+// finishes last merges the partials by log-sum-exp.
 //
 // Per 16-key tile, a wave computes
 //   S^T[16 keys x 16 rows]  = K_tile . Q^T      (MFMA 16x16x32, 16-bit; 16x16x4, fp32)
@@ -22,11 +29,12 @@
 // 16-byte piece of a K row and the matching piece of the q row, and the output columns
 // are permuted the same way, so every global load and store is a 16-byte vector access.
 //
-// Memory is read straight from the pool: token t of the slice lives in page
-// kv_indices[page_base + t / P], slot t % P, at ((page * P + slot) * Hkv + kv_head) * D.
+// Memory is read straight from the pool: token t of a request lives in page
+// kv_indices[page_base + t / P], slot t % P, at pool row (page * P + slot) * Hkv + kv_head.
 // Tiles start at multiples of 16 tokens and P is a multiple of 16, so one tile never
-// crosses a page. Keys at or past the slice end are neither read nor scored; unused
-// slots of a page may hold anything, NaN included.
+// crosses a page and every slot a tile touches exists. Keys at or past a segment's end are
+// loaded (in bounds) but never scored, and their V rows are replaced by zeros before
+// use, so unused slots of a page may hold anything, NaN included.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -103,40 +111,52 @@ __device__ __forceinline__ T ld_global(const void *p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// work item fields (scalar loads; every lane of the workgroup reads the same item)
+// segment headers: lanes 0..15 of one vector register hold the FL_WORK_ITEM_INTS fields
 // ---------------------------------------------------------------------------------------
-struct Item {
-    int q_start, qo_len, kv_len, page_base, kv_head, row_begin, num_rows, tok_begin, tok_end,
-        part_row;
-};
+__device__ __forceinline__ int load_header(const int32_t *segs, int seg, int lane) {
+    return lane < FL_WORK_ITEM_INTS ? ld_global<int>(segs + (size_t)seg * FL_WORK_ITEM_INTS + lane) : 0;
+}
+__device__ __forceinline__ int hfield(int hv, int f) { return __builtin_amdgcn_readlane(hv, f); }
 
-__device__ __forceinline__ Item load_item(const int32_t *items) {
-    const int32_t *it = items + (size_t)blockIdx.x * FL_WORK_ITEM_INTS;
-    Item w;
-    w.q_start = it[FL_WI_Q_START];
-    w.qo_len = it[FL_WI_QO_LEN];
-    w.kv_len = it[FL_WI_KV_LEN];
-    w.page_base = it[FL_WI_PAGE_BASE];
-    w.kv_head = it[FL_WI_KV_HEAD];
-    w.row_begin = it[FL_WI_ROW_BEGIN];
-    w.num_rows = it[FL_WI_NUM_ROWS];
-    w.tok_begin = it[FL_WI_TOK_BEGIN];
-    w.tok_end = it[FL_WI_TOK_END];
-    w.part_row = it[FL_WI_PART_ROW];
-    return w;
+struct Seg {  // wave-uniform fields of the segment being computed
+    int q_start, qo_len, kv_len, kv_head, row_begin, num_rows, tok_begin, tok_end, part_row,
+        split, num_splits, merge, pos_begin;
+};
+__device__ __forceinline__ Seg seg_fields(int hv) {
+    Seg s;
+    s.q_start = hfield(hv, FL_WI_Q_START);
+    s.qo_len = hfield(hv, FL_WI_QO_LEN);
+    s.kv_len = hfield(hv, FL_WI_KV_LEN);
+    s.kv_head = hfield(hv, FL_WI_KV_HEAD);
+    s.row_begin = hfield(hv, FL_WI_ROW_BEGIN);
+    s.num_rows = hfield(hv, FL_WI_NUM_ROWS);
+    s.tok_begin = hfield(hv, FL_WI_TOK_BEGIN);
+    s.tok_end = hfield(hv, FL_WI_TOK_END);
+    s.part_row = hfield(hv, FL_WI_PART_ROW);
+    s.split = hfield(hv, FL_WI_SPLIT);
+    s.num_splits = hfield(hv, FL_WI_NUM_SPLITS);
+    s.merge = hfield(hv, FL_WI_MERGE);
+    s.pos_begin = hfield(hv, FL_WI_POS_BEGIN);
+    return s;
 }
 
 // ---------------------------------------------------------------------------------------
-// output stores: n fp32 results -> n elements of the output type at out + idx
+// output stores: N fp32 results -> N elements of the output type at out + idx
 // ---------------------------------------------------------------------------------------
 template <int DT, int N>
 __device__ __forceinline__ void store_out(void *out, int64_t idx, const float *res) {
+    static_assert(N % 2 == 0, "even element count");
     if constexpr (DT == FL_F32) {
         float *dst = (float *)out + idx;
-        static_assert(N % 2 == 0, "even element count");
+        if constexpr (N % 4 == 0) {
 #pragma unroll
-        for (int e = 0; e < N; e += 2)
-            *reinterpret_cast<float2 *>(dst + e) = make_float2(res[e], res[e + 1]);
+            for (int e = 0; e < N; e += 4)
+                *reinterpret_cast<float4 *>(dst + e) = make_float4(res[e], res[e + 1], res[e + 2], res[e + 3]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < N; e += 2)
+                *reinterpret_cast<float2 *>(dst + e) = make_float2(res[e], res[e + 1]);
+        }
     } else {
         using H = Half<DT>;
         uint16_t *dst = (uint16_t *)out + idx;
@@ -159,65 +179,18 @@ __device__ __forceinline__ void store_out(void *out, int64_t idx, const float *r
     }
 }
 
-// ---------------------------------------------------------------------------------------
-// epilogue shared by all element types: fold the waves' softmax states in LDS and write
-// either the final rows or the slice's partial rows.
-//   o[w][row][d]  unnormalised accumulator of wave w; m / l its running max and sum
-// ---------------------------------------------------------------------------------------
-template <int D, int NW>
-struct Smem {
-    float o[NW][kBlockRows][D + 4];
-    float m[NW][kBlockRows];
-    float l[NW][kBlockRows];
-};
-
-template <int DT, int D, int NW>
-__device__ __forceinline__ void fold_and_store(const Smem<D, NW> &sm, const Item &w,
-                                               const AttnArgs &a) {
-    constexpr int TPR = NW * 64 / kBlockRows;  // threads per row
-    constexpr int EPT = D / TPR;               // elements per thread
-    static_assert(D % TPR == 0 && EPT % 2 == 0, "bad epilogue split");
-    const int r = threadIdx.x / TPR;
-    const int c0 = (threadIdx.x % TPR) * EPT;
-    if (r >= w.num_rows) return;
-    float M = kNegInf;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) M = fmaxf(M, sm.m[v][r]);
-    float wt[NW];
-    float L = 0.f;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-        wt[v] = (M == kNegInf) ? 0.f : fast_exp2(sm.m[v][r] - M);
-        L += sm.l[v][r] * wt[v];
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    float res[EPT];
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        float acc = 0.f;
-#pragma unroll
-        for (int v = 0; v < NW; ++v) acc += sm.o[v][r][c0 + e] * wt[v];
-        res[e] = acc * inv;
-    }
-    const float lse2 = L > 0.f ? M + fast_log2(L) : kNegInf;  // log2 domain
-    if (w.part_row < 0) {
-        const int f = w.row_begin + r;
-        const int qi = f / a.group;
-        const int qh = f - qi * a.group;
-        const int64_t row = (int64_t)(w.q_start + qi) * a.num_qo_heads + w.kv_head * a.group + qh;
-        store_out<DT, EPT>(a.out, row * D + c0, res);
-        if (a.lse && c0 == 0) a.lse[row] = lse2 * kLn2;
-    } else {
-        store_out<FL_F32, EPT>(a.part_o, (int64_t)(w.part_row + r) * D + c0, res);
-        if (c0 == 0) a.part_lse[w.part_row + r] = lse2;
-    }
-}
-
 // Online softmax update for one 16-key tile. s holds S^T for keys t0 + 4*grp + e of the
-// lane's row; returns P (against the new running max) and the rescale factor alpha.
+// lane's row; returns P (against the running max) and the rescale factor alpha.
+// The running max moves only when a tile's max exceeds it by more than kSlack (log2
+// units): P then stays below 2^kSlack, harmless in fp32, and most tiles need no rescale
+// of the accumulator (rescaled reports whether any row of the wave moved). Any reference
+// value gives the same result once the final sum divides it out.
+constexpr float kSlack = 8.f;
+
 __device__ __forceinline__ void softmax_tile(const f32x4 &s, int t0, int grp, int tok_end,
                                              int limit, float scale_log2, float &m_run,
-                                             float &l_run, float p[4], float &alpha) {
+                                             float &l_run, float p[4], float &alpha,
+                                             bool &rescaled) {
     float sv[4];
     float mt = kNegInf;
 #pragma unroll
@@ -229,9 +202,11 @@ __device__ __forceinline__ void softmax_tile(const f32x4 &s, int t0, int grp, in
     }
     mt = fmaxf(mt, shfl_xor(mt, 16));
     mt = fmaxf(mt, shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
+    const bool move = mt > m_run + kSlack;  // false while both are -inf
+    const float m_new = move ? mt : m_run;
+    rescaled = __builtin_amdgcn_ballot_w64(move) != 0;
+    alpha = move ? fast_exp2(m_run - m_new) : 1.f;
     const float base = (m_new == kNegInf) ? 0.f : m_new;
-    alpha = fast_exp2(m_run - base);
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -248,7 +223,7 @@ struct RowInfo {
     bool ok;
 };
 
-__device__ __forceinline__ RowInfo row_info(const Item &w, const AttnArgs &a, int col) {
+__device__ __forceinline__ RowInfo row_info(const Seg &w, const AttnArgs &a, int col) {
     RowInfo ri;
     const int f = w.row_begin + col;
     ri.ok = col < w.num_rows;
@@ -258,74 +233,68 @@ __device__ __forceinline__ RowInfo row_info(const Item &w, const AttnArgs &a, in
     return ri;
 }
 
+__device__ __forceinline__ int64_t q_row_offset(const Seg &w, const AttnArgs &a, const RowInfo &ri) {
+    return ((int64_t)(w.q_start + ri.qi) * a.num_qo_heads + w.kv_head * a.group + ri.qh);
+}
+
 // ---------------------------------------------------------------------------------------
-// bf16 / fp16 kernel
+// tile policy, bf16 / fp16 (MFMA 16x16x32 for QK^T and PV, 16x16x16 for the transpose)
 // Lane l: col = l % 16 (row of the block for Q/P/O, key of the tile for K/V), grp = l / 16.
 //   K and Q pieces: element d = 32c + 8grp + i (chunk c < D/32, i < 8).
 //   PV block j (j < D/16) holds output d = 32(j/2) + 8grp + 4(j%2) + e in element e.
 // ---------------------------------------------------------------------------------------
-template <int DT, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_half_kernel(const AttnArgs a) {
+template <int DT, int D>
+struct HalfTile {
     using H = Half<DT>;
-    constexpr int NC = D / 32;
-    constexpr int NJ = D / 16;
-    __shared__ Smem<D, NW> sm;
+    static constexpr int NC = D / 32;
+    static constexpr int NJ = D / 16;
+    struct Frag {
+        u32x4 k[NC], v[NC];
+    };
+    struct QOp {
+        u32x4 q[NC];
+        u32x2 ident;
+    };
 
-    const Item w = load_item(a.items);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int col = lane & 15;
-    const int grp = lane >> 4;
-    const int P = 1 << a.log2_page;
-    const RowInfo ri = row_info(w, a, col);
-
-    u32x4 qf[NC];
-    {
-        const uint16_t *qp =
-            (const uint16_t *)a.q +
-            ((int64_t)(w.q_start + ri.qi) * a.num_qo_heads + w.kv_head * a.group + ri.qh) * D +
-            8 * grp;
+    __device__ static QOp load_q(const AttnArgs &a, const Seg &w, const RowInfo &ri, int col, int grp) {
+        QOp op;
+        const uint16_t *qp = (const uint16_t *)a.q + q_row_offset(w, a, ri) * D + 8 * grp;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-            qf[c] = ri.ok ? ld_global<u32x4>(qp + 32 * c) : u32x4{0, 0, 0, 0};
-    }
-    // identity operand: element e of lane l is 1 where 4*grp + e == col
-    u32x2 ident;
-    {
+        for (int c = 0; c < NC; ++c) op.q[c] = ri.ok ? ld_global<u32x4>(qp + 32 * c) : u32x4{0, 0, 0, 0};
+        // identity operand: element e of lane l is 1 where 4*grp + e == col
         const uint32_t e0 = (4 * grp + 0 == col) ? H::kOne : 0u;
         const uint32_t e1 = (4 * grp + 1 == col) ? H::kOne : 0u;
         const uint32_t e2 = (4 * grp + 2 == col) ? H::kOne : 0u;
         const uint32_t e3 = (4 * grp + 3 == col) ? H::kOne : 0u;
-        ident = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+        op.ident = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+        return op;
     }
 
-    float m_run = kNegInf, l_run = 0.f;
-    f32x4 o[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int64_t slot_stride = (int64_t)a.num_kv_heads * D;
-    const uint16_t *kb = (const uint16_t *)a.k + (int64_t)w.kv_head * D + 8 * grp;
-    const uint16_t *vb = (const uint16_t *)a.v + (int64_t)w.kv_head * D + 8 * grp;
-    const int ntiles = (w.tok_end - w.tok_begin + kTileTokens - 1) / kTileTokens;
-
-    for (int tile = wave; tile < ntiles; tile += NW) {
-        const int t0 = w.tok_begin + tile * kTileTokens;
-        const int page = a.kv_indices[w.page_base + (t0 >> a.log2_page)];
-        const bool tv = t0 + col < w.tok_end;
-        const int64_t off = ((int64_t)page * P + (t0 & (P - 1)) + col) * slot_stride;
-        u32x4 kf[NC], vf[NC];
+    // row0: pool row of the tile's first key; consecutive keys are hkv rows apart.
+    __device__ static void load(Frag &f, const void *k, const void *v, int row0, int hkv, int col,
+                                int grp) {
+        const int64_t off = (int64_t)(row0 + col * hkv) * D + 8 * grp;
+        const uint16_t *kp = (const uint16_t *)k + off;
+        const uint16_t *vp = (const uint16_t *)v + off;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            kf[c] = tv ? ld_global<u32x4>(kb + off + 32 * c) : u32x4{0, 0, 0, 0};
-            vf[c] = tv ? ld_global<u32x4>(vb + off + 32 * c) : u32x4{0, 0, 0, 0};
+            f.k[c] = ld_global<u32x4>(kp + 32 * c);
+            f.v[c] = ld_global<u32x4>(vp + 32 * c);
         }
+    }
+
+    __device__ static void compute(const Frag &f, const QOp &q, int t0, int col, int grp, int tok_end,
+                                   int limit, float scale_log2, float &m_run, float &l_run, f32x4 *o) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) s = H::mma_k32(kf[c], qf[c], s);
-
+        for (int c = 0; c < NC; ++c) s = H::mma_k32(f.k[c], q.q[c], s);
         float p[4], alpha;
-        softmax_tile(s, t0, grp, w.tok_end, ri.limit, a.scale_log2, m_run, l_run, p, alpha);
+        bool rescaled;
+        softmax_tile(s, t0, grp, tok_end, limit, scale_log2, m_run, l_run, p, alpha, rescaled);
+        if (rescaled) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) o[j] = o[j] * alpha;
+        }
         // P = P_hi + P_lo, both in the 16-bit type: the pair carries p to ~16 bits more
         // than one rounding would, so the product with the exact 16-bit V loses nothing
         // measurable. One K=32 instruction contracts [V^T V^T] with [P_hi; P_lo].
@@ -333,227 +302,435 @@ __global__ __launch_bounds__(NW * 64) void attn_half_kernel(const AttnArgs a) {
         const uint32_t l01 = H::pack(p[0] - H::lo_f(h01), p[1] - H::hi_f(h01));
         const uint32_t l23 = H::pack(p[2] - H::lo_f(h23), p[3] - H::hi_f(h23));
         const u32x4 pk = {h01, h23, l01, l23};
+        const bool kv_ok = t0 + col < tok_end;  // this lane's V row is a real key
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const u32x4 ch = vf[j >> 1];
+            const u32x4 ch = kv_ok ? f.v[j >> 1] : u32x4{0, 0, 0, 0};
             const u32x2 va = (j & 1) ? u32x2{ch[2], ch[3]} : u32x2{ch[0], ch[1]};
-            const f32x4 vt = H::mma_k16(va, ident, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 vt = H::mma_k16(va, q.ident, f32x4{0.f, 0.f, 0.f, 0.f});
             const uint32_t v01 = H::pack(vt[0], vt[1]), v23 = H::pack(vt[2], vt[3]);
-            o[j] = H::mma_k32(u32x4{v01, v23, v01, v23}, pk, o[j] * alpha);
+            o[j] = H::mma_k32(u32x4{v01, v23, v01, v23}, pk, o[j]);
         }
     }
-    l_run += shfl_xor(l_run, 16);
-    l_run += shfl_xor(l_run, 32);
 
+    // accumulator element (block j, element e) of lane (col, grp) -> output column d
+    __device__ static void to_smem(const f32x4 *o, float *row, int grp) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int d0 = 32 * (j >> 1) + 8 * grp + 4 * (j & 1);
-        *reinterpret_cast<f32x4 *>(&sm.o[wave][col][d0]) = o[j];
+        for (int j = 0; j < NJ; ++j)
+            *reinterpret_cast<f32x4 *>(row + 32 * (j >> 1) + 8 * grp + 4 * (j & 1)) = o[j];
     }
-    if (grp == 0) {
-        sm.m[wave][col] = m_run;
-        sm.l[wave][col] = l_run;
+    __device__ static void from_smem(f32x4 *o, const float *row, int grp) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            o[j] = *reinterpret_cast<const f32x4 *>(row + 32 * (j >> 1) + 8 * grp + 4 * (j & 1));
     }
-    __syncthreads();
-    fold_and_store<DT, D, NW>(sm, w, a);
-}
+};
 
 // ---------------------------------------------------------------------------------------
-// fp32 kernel (MFMA 16x16x4 f32: one element per lane per instruction)
-//   K and Q: lane holds d = grp*(D/4) + s, s < D/4 (contiguous, 16-byte loads).
+// tile policy, fp32 (MFMA 16x16x4 f32: one element per lane per instruction)
+//   K and Q: lane holds d = grp*(D/4) + s, s < D/4.
 //   V for key 4grp+e of the tile: lane holds d = (D/16)*col + j, j < D/16.
 //   PV block j holds output d = (D/16)*(4grp + e) + j in element e.
 // ---------------------------------------------------------------------------------------
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_f32_kernel(const AttnArgs a) {
-    constexpr int NS = D / 4;
-    constexpr int NJ = D / 16;
-    __shared__ Smem<D, NW> sm;
+template <int D>
+struct F32Tile {
+    static constexpr int NS = D / 4;
+    static constexpr int NJ = D / 16;
+    struct Frag {
+        float4 k[NS / 4];
+        float4 v[4][NJ / 4];
+    };
+    struct QOp {
+        float q[NS];
+    };
 
-    const Item w = load_item(a.items);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int col = lane & 15;
-    const int grp = lane >> 4;
-    const int P = 1 << a.log2_page;
-    const RowInfo ri = row_info(w, a, col);
-
-    float qf[NS];
-    {
-        const float *qp =
-            (const float *)a.q +
-            ((int64_t)(w.q_start + ri.qi) * a.num_qo_heads + w.kv_head * a.group + ri.qh) * D +
-            grp * NS;
+    __device__ static QOp load_q(const AttnArgs &a, const Seg &w, const RowInfo &ri, int, int grp) {
+        QOp op;
+        const float *qp = (const float *)a.q + q_row_offset(w, a, ri) * D + grp * NS;
 #pragma unroll
         for (int s4 = 0; s4 < NS; s4 += 4) {
             const float4 v = ri.ok ? ld_global<float4>(qp + s4) : make_float4(0.f, 0.f, 0.f, 0.f);
-            qf[s4] = v.x;
-            qf[s4 + 1] = v.y;
-            qf[s4 + 2] = v.z;
-            qf[s4 + 3] = v.w;
+            op.q[s4] = v.x;
+            op.q[s4 + 1] = v.y;
+            op.q[s4 + 2] = v.z;
+            op.q[s4 + 3] = v.w;
         }
+        return op;
     }
-    float m_run = kNegInf, l_run = 0.f;
-    f32x4 o[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int64_t slot_stride = (int64_t)a.num_kv_heads * D;
-    const float *kb = (const float *)a.k + (int64_t)w.kv_head * D + grp * NS;
-    const float *vb = (const float *)a.v + (int64_t)w.kv_head * D + NJ * col;
-    const int ntiles = (w.tok_end - w.tok_begin + kTileTokens - 1) / kTileTokens;
-
-    for (int tile = wave; tile < ntiles; tile += NW) {
-        const int t0 = w.tok_begin + tile * kTileTokens;
-        const int page = a.kv_indices[w.page_base + (t0 >> a.log2_page)];
-        const int64_t slot0 = (int64_t)page * P + (t0 & (P - 1));
-        float kf[NS];
-        {
-            const bool tv = t0 + col < w.tok_end;
-            const float *kp = kb + (slot0 + col) * slot_stride;
+    __device__ static void load(Frag &f, const void *k, const void *v, int row0, int hkv, int col,
+                                int grp) {
+        const float *kp = (const float *)k + (int64_t)(row0 + col * hkv) * D + grp * NS;
 #pragma unroll
-            for (int s4 = 0; s4 < NS; s4 += 4) {
-                const float4 v = tv ? ld_global<float4>(kp + s4) : make_float4(0.f, 0.f, 0.f, 0.f);
-                kf[s4] = v.x;
-                kf[s4 + 1] = v.y;
-                kf[s4 + 2] = v.z;
-                kf[s4 + 3] = v.w;
-            }
-        }
-        float vf[4][NJ];
+        for (int c = 0; c < NS / 4; ++c) f.k[c] = ld_global<float4>(kp + 4 * c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int key = 4 * grp + e;
-            const bool tv = t0 + key < w.tok_end;
-            const float *vp = vb + (slot0 + key) * slot_stride;
+            const float *vp = (const float *)v + (int64_t)(row0 + (4 * grp + e) * hkv) * D + NJ * col;
 #pragma unroll
-            for (int j4 = 0; j4 < NJ; j4 += 4) {
-                const float4 v = tv ? ld_global<float4>(vp + j4) : make_float4(0.f, 0.f, 0.f, 0.f);
-                vf[e][j4] = v.x;
-                vf[e][j4 + 1] = v.y;
-                vf[e][j4 + 2] = v.z;
-                vf[e][j4 + 3] = v.w;
-            }
+            for (int c = 0; c < NJ / 4; ++c) f.v[e][c] = ld_global<float4>(vp + 4 * c);
         }
+    }
+
+    __device__ static void compute(const Frag &f, const QOp &q, int t0, int, int grp, int tok_end,
+                                   int limit, float scale_log2, float &m_run, float &l_run, f32x4 *o) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < NS; ++st) s = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[st], qf[st], s, 0, 0, 0);
-
+        for (int c = 0; c < NS / 4; ++c) {
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(f.k[c].x, q.q[4 * c], s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(f.k[c].y, q.q[4 * c + 1], s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(f.k[c].z, q.q[4 * c + 2], s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(f.k[c].w, q.q[4 * c + 3], s, 0, 0, 0);
+        }
         float p[4], alpha;
-        softmax_tile(s, t0, grp, w.tok_end, ri.limit, a.scale_log2, m_run, l_run, p, alpha);
+        bool rescaled;
+        softmax_tile(s, t0, grp, tok_end, limit, scale_log2, m_run, l_run, p, alpha, rescaled);
+        if (rescaled) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) o[j] = o[j] * alpha;
+            for (int j = 0; j < NJ; ++j) o[j] = o[j] * alpha;
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; ++e) {
+            const bool ok = t0 + 4 * grp + e < tok_end;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                o[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[e][j], p[e], o[j], 0, 0, 0);
+            for (int c = 0; c < NJ / 4; ++c) {
+                const float4 v = ok ? f.v[e][c] : make_float4(0.f, 0.f, 0.f, 0.f);
+                o[4 * c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.x, p[e], o[4 * c], 0, 0, 0);
+                o[4 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.y, p[e], o[4 * c + 1], 0, 0, 0);
+                o[4 * c + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.z, p[e], o[4 * c + 2], 0, 0, 0);
+                o[4 * c + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.w, p[e], o[4 * c + 3], 0, 0, 0);
+            }
+        }
     }
-    l_run += shfl_xor(l_run, 16);
-    l_run += shfl_xor(l_run, 32);
 
+    __device__ static void to_smem(const f32x4 *o, float *row, int grp) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.o[wave][col][NJ * (4 * grp + e) + j] = o[j][e];
-    if (grp == 0) {
-        sm.m[wave][col] = m_run;
-        sm.l[wave][col] = l_run;
+            for (int e = 0; e < 4; ++e) row[NJ * (4 * grp + e) + j] = o[j][e];
     }
-    __syncthreads();
-    fold_and_store<FL_F32, D, NW>(sm, w, a);
-}
+    __device__ static void from_smem(f32x4 *o, const float *row, int grp) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[j][e] = row[NJ * (4 * grp + e) + j];
+    }
+};
 
 // ---------------------------------------------------------------------------------------
-// merge of a row block's slices:  M = max_s lse_s,  w_s = 2^(lse_s - M),
-//   out = sum_s w_s o_s / sum_s w_s,  lse = M + log2(sum_s w_s)     (log2 domain)
-// 256 threads: 16 per row, D/16 elements each.
+// LDS for the per-segment fold: four wave states (8-wave groups fold pairwise first)
 // ---------------------------------------------------------------------------------------
-template <int DT, int D>
-__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
-    constexpr int EPT = D / 16;
-    const int32_t *mi = a.merges + (size_t)blockIdx.x * kMergeInts;
-    const int q_start = mi[MI_Q_START];
-    const int kv_head = mi[MI_KV_HEAD];
-    const int row_begin = mi[MI_ROW_BEGIN];
-    const int nrows = mi[MI_NUM_ROWS];
-    const int part_row = mi[MI_PART_ROW];
-    const int ns = mi[MI_NUM_SPLITS];
-    const int r = threadIdx.x >> 4;
-    const int c0 = (threadIdx.x & 15) * EPT;
-    if (r >= nrows) return;
+template <int D>
+struct Smem {
+    float o[4][kBlockRows][D + 4];
+    float m[4][kBlockRows];
+    float l[4][kBlockRows];
+    int last[2];
+};
+
+// Merge of a row block's pieces by the piece that finished last:
+//   M = max_s lse_s,  w_s = 2^(lse_s - M),  out = sum_s w_s o_s / sum_s w_s.
+// The partial rows were written with device-scope stores; they are read the same way.
+template <int DT, int D, int TPR>
+__device__ __forceinline__ void merge_pieces(const Seg &w, const AttnArgs &a, int r, int c0) {
+    constexpr int EPT = D / TPR;
+    const int nr = w.num_rows;
+    const int base = w.part_row - w.split * nr;
+    const int ns = w.num_splits;
     float M = kNegInf;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_lse[part_row + s * nrows + r]);
+    for (int s = 0; s < ns; ++s)
+        M = fmaxf(M, __hip_atomic_load(a.part_lse + base + s * nr + r, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT));
     float acc[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
     float L = 0.f;
+#pragma unroll 2
     for (int s = 0; s < ns; ++s) {
-        const int pr = part_row + s * nrows + r;
-        const float wt = fast_exp2(a.part_lse[pr] - M);
+        const int pr = base + s * nr + r;
+        const float wt = fast_exp2(
+            __hip_atomic_load(a.part_lse + pr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
         L += wt;
         const float *src = a.part_o + (int64_t)pr * D + c0;
 #pragma unroll
-        for (int e = 0; e < EPT; e += 4) {
-            const float4 v = ld_global<float4>(src + e);
-            acc[e] += wt * v.x;
-            acc[e + 1] += wt * v.y;
-            acc[e + 2] += wt * v.z;
-            acc[e + 3] += wt * v.w;
-        }
+        for (int e = 0; e < EPT; ++e)
+            acc[e] += wt * __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     const float inv = 1.f / L;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) acc[e] *= inv;
-    const int f = row_begin + r;
+    const int f = w.row_begin + r;
     const int qi = f / a.group;
     const int qh = f - qi * a.group;
-    const int64_t row = (int64_t)(q_start + qi) * a.num_qo_heads + kv_head * a.group + qh;
+    const int64_t row = (int64_t)(w.q_start + qi) * a.num_qo_heads + w.kv_head * a.group + qh;
     store_out<DT, EPT>(a.out, row * D + c0, acc);
     if (a.lse && c0 == 0) a.lse[row] = (M + fast_log2(L)) * kLn2;
 }
 
-constexpr int kWaves = 4;
+// Fold of one segment across the waves (all waves call it at the same step), then the
+// output rows: final rows for a whole row block, device-scope fp32 partial rows for a piece.
+template <class T, int DT, int D, int NW>
+__device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, const Seg &cs, int k,
+                                             float &m_run, float &l_run, f32x4 *o, int &pend0,
+                                             int &pend1, int wave, int col, int grp) {
+    constexpr int NJ = D / 16;
+    constexpr int TPR = NW * 64 / kBlockRows;
+    constexpr int EPT = D / TPR;
+    l_run += shfl_xor(l_run, 16);
+    l_run += shfl_xor(l_run, 32);
+    if constexpr (NW == 8) {
+        if (wave >= 4) {
+            T::to_smem(o, sm.o[wave - 4][col], grp);
+            if (grp == 0) {
+                sm.m[wave - 4][col] = m_run;
+                sm.l[wave - 4][col] = l_run;
+            }
+        }
+        __syncthreads();
+        if (wave < 4) {
+            f32x4 o2[NJ];
+            T::from_smem(o2, sm.o[wave][col], grp);
+            const float m2 = sm.m[wave][col], l2 = sm.l[wave][col];
+            const float M = fmaxf(m_run, m2);
+            const float a1 = M == kNegInf ? 0.f : fast_exp2(m_run - M);
+            const float a2 = M == kNegInf ? 0.f : fast_exp2(m2 - M);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) o[j] = o[j] * a1 + o2[j] * a2;
+            l_run = l_run * a1 + l2 * a2;
+            m_run = M;
+        }
+        __syncthreads();
+    }
+    if (wave < 4) {
+        T::to_smem(o, sm.o[wave][col], grp);
+        if (grp == 0) {
+            sm.m[wave][col] = m_run;
+            sm.l[wave][col] = l_run;
+        }
+    }
+    __syncthreads();
+    const int r = threadIdx.x / TPR;
+    const int c0 = (threadIdx.x % TPR) * EPT;
+    if (r < cs.num_rows) {
+        float M = kNegInf;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) M = fmaxf(M, sm.m[v][r]);
+        float wt[4];
+        float L = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            wt[v] = (M == kNegInf) ? 0.f : fast_exp2(sm.m[v][r] - M);
+            L += sm.l[v][r] * wt[v];
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        float res[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            float acc = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc += sm.o[v][r][c0 + e] * wt[v];
+            res[e] = acc * inv;
+        }
+        const float lse2 = L > 0.f ? M + fast_log2(L) : kNegInf;  // log2 domain
+        if (cs.part_row < 0) {
+            const int f = cs.row_begin + r;
+            const int qi = f / a.group;
+            const int qh = f - qi * a.group;
+            const int64_t row = (int64_t)(cs.q_start + qi) * a.num_qo_heads + cs.kv_head * a.group + qh;
+            store_out<DT, EPT>(a.out, row * D + c0, res);
+            if (a.lse && c0 == 0) a.lse[row] = lse2 * kLn2;
+        } else {
+            float *dst = a.part_o + (int64_t)(cs.part_row + r) * D + c0;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                __hip_atomic_store(dst + e, res[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (c0 == 0)
+                __hip_atomic_store(a.part_lse + cs.part_row + r, lse2, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (cs.part_row >= 0) {
+        if (pend0 < 0)
+            pend0 = k;
+        else
+            pend1 = k;
+    }
+    __syncthreads();  // the LDS slots are free again
+    m_run = kNegInf;
+    l_run = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Pool rows of this wave's steps win .. win+63 (lane i <- step win + i).
+__device__ __forceinline__ int load_step_rows(const int32_t *rows, int win, int lane, int nsteps) {
+    const int i = win + lane;
+    return i < nsteps ? rows[i] : 0;
+}
+
+// ---------------------------------------------------------------------------------------
+// the kernel: one workgroup per equal share of the plan's tiles
+// ---------------------------------------------------------------------------------------
+template <class T, int DT, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+    constexpr int PF = kRingDepth;
+    constexpr int NJ = D / 16;
+    constexpr int TPR = NW * 64 / kBlockRows;  // fold: threads per row
+    constexpr int EPT = D / TPR;               // fold: elements per thread
+    static_assert(D % TPR == 0 && EPT % 2 == 0, "bad fold split");
+    __shared__ Smem<D> sm;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+    const int gid = blockIdx.x;
+    const int seg_b = a.wg_segs[gid], seg_e = a.wg_segs[gid + 1];
+    const int pos0 = a.wg_pos[gid];
+    const int nsteps = (a.wg_pos[gid + 1] - pos0) / NW;  // steps per wave (multiple of PF)
+    const int32_t *rows = a.step_rows + pos0 + wave * nsteps;
+
+    // segment headers two ahead, Q one ahead
+    int hv0 = load_header(a.segs, seg_b, lane);
+    int hv1 = seg_b + 1 < seg_e ? load_header(a.segs, seg_b + 1, lane) : 0;
+    int hv2 = seg_b + 2 < seg_e ? load_header(a.segs, seg_b + 2, lane) : 0;
+    int rows_cur = load_step_rows(rows, 0, lane, nsteps);
+    int rows_nxt = load_step_rows(rows, 64, lane, nsteps);
+    int k = seg_b;
+    Seg cs = seg_fields(hv0);
+    RowInfo ri = row_info(cs, a, col);
+    typename T::QOp qc = T::load_q(a, cs, ri, col, grp);
+    typename T::QOp qn = qc;
+    int seg_end = k + 1 < seg_e ? hfield(hv1, FL_WI_POS_BEGIN) : nsteps;
+    int ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
+
+    float m_run = kNegInf, l_run = 0.f;
+    f32x4 o[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int pend0 = -1, pend1 = -1;  // pieces whose merge ticket is still to be drawn
+
+    // ---- the step stream: PF tiles of K and V in flight per wave -------------------------
+    // Every slot of the ring is always in flight (padding steps re-read a real tile and are
+    // never scored), so the outstanding-load count is the same on every path and each tile
+    // waits only for its own data.
+    int win_issue = 0;
+    typename T::Frag buf[PF];
+    auto issue = [&](typename T::Frag &f, int p) {  // p < nsteps
+        if ((p & ~63) != win_issue) {              // next 64-step window of pool rows
+            win_issue = p & ~63;
+            rows_cur = rows_nxt;
+            rows_nxt = load_step_rows(rows, win_issue + 64, lane, nsteps);
+        }
+        T::load(f, a.k, a.v, __builtin_amdgcn_readlane(rows_cur, p & 63), a.num_kv_heads, col, grp);
+    };
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+        issue(buf[s], s);
+        __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
+    }
+    for (int p0 = 0; p0 < nsteps; p0 += PF) {
+        if (p0 == seg_end) {  // the same step in every wave: segment k is done
+            fold_segment<T, DT, D, NW>(sm, a, cs, k, m_run, l_run, o, pend0, pend1, wave, col, grp);
+            ++k;
+            hv0 = hv1;
+            hv1 = hv2;
+            hv2 = k + 2 < seg_e ? load_header(a.segs, k + 2, lane) : 0;
+            cs = seg_fields(hv0);
+            ri = row_info(cs, a, col);
+            qc = qn;
+            seg_end = k + 1 < seg_e ? hfield(hv1, FL_WI_POS_BEGIN) : nsteps;
+            ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
+        }
+        if (p0 + PF == seg_end && k + 1 < seg_e) {
+            // the last step group of segment k: Q of segment k + 1 goes out before the
+            // tiles of k + 1 this group issues, so it is complete before they are
+            const Seg ns = seg_fields(hv1);
+            qn = T::load_q(a, ns, row_info(ns, a, col), col, grp);
+        }
+#pragma unroll
+        for (int s = 0; s < PF; ++s) {
+            const int p = p0 + s;
+            const int j = (p - cs.pos_begin) * NW + wave;  // tile of the segment
+            if (j < ntile) {
+                const int t0 = cs.tok_begin + j * kTileTokens;
+                T::compute(buf[s], qc, t0, col, grp, cs.tok_end, ri.limit, a.scale_log2, m_run,
+                           l_run, o);
+            }
+            issue(buf[s], min(p + PF, nsteps - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    fold_segment<T, DT, D, NW>(sm, a, cs, k, m_run, l_run, o, pend0, pend1, wave, col, grp);
+
+    // ---- merge tickets of the partial pieces (at most the first and the last) -----------
+    // The partial rows went out as device-scope stores; each wave waits for their
+    // acknowledgement before the workgroup draws its tickets with device-scope atomics, so
+    // the piece that draws a row block's last ticket finds every other piece complete.
+    if (pend0 >= 0) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int pend[2] = {pend0, pend1};
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                sm.last[i] = 0;
+                if (pend[i] < 0) continue;
+                const int32_t *hp = a.segs + (size_t)pend[i] * FL_WORK_ITEM_INTS;
+                const int tk = hp[FL_WI_MERGE], ns = hp[FL_WI_NUM_SPLITS];
+                const int done = __hip_atomic_fetch_add(a.tickets + tk, 1, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+                if (done == ns - 1) {
+                    __hip_atomic_store(a.tickets + tk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    sm.last[i] = 1;
+                }
+            }
+        }
+        __syncthreads();
+        const int r = threadIdx.x / TPR;
+        const int c0 = (threadIdx.x % TPR) * EPT;
+        const int pend[2] = {pend0, pend1};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (pend[i] < 0 || !sm.last[i]) continue;
+            const Seg ps = seg_fields(load_header(a.segs, pend[i], lane));
+            if (r < ps.num_rows) merge_pieces<DT, D, TPR>(ps, a, r, c0);
+        }
+    }
+}
 
 template <int DT, int D>
-hipError_t launch_attn_t(int n, const AttnArgs &a, hipStream_t s) {
-    if constexpr (DT == FL_F32)
-        hipLaunchKernelGGL((attn_f32_kernel<D, kWaves>), dim3(n), dim3(kWaves * 64), 0, s, a);
-    else
-        hipLaunchKernelGGL((attn_half_kernel<DT, D, kWaves>), dim3(n), dim3(kWaves * 64), 0, s, a);
+struct TileFor {
+    using type = HalfTile<DT, D>;
+};
+template <int D>
+struct TileFor<FL_F32, D> {
+    using type = F32Tile<D>;
+};
+
+template <int DT, int D, int NW>
+hipError_t launch_t(int n, const AttnArgs &a, hipStream_t s) {  // n: workgroups
+    using T = typename TileFor<DT, D>::type;
+    hipLaunchKernelGGL((attn_kernel<T, DT, D, NW>), dim3(n), dim3(NW * 64), 0, s, a);
     return hipGetLastError();
 }
 
 template <int DT, int D>
-hipError_t launch_merge_t(int n, const MergeArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((merge_kernel<DT, D>), dim3(n), dim3(256), 0, s, a);
-    return hipGetLastError();
+hipError_t launch_w(int waves, int n, const AttnArgs &a, hipStream_t s) {
+    return waves == 8 ? launch_t<DT, D, 8>(n, a, s) : launch_t<DT, D, 4>(n, a, s);
 }
 
 }  // namespace
 
-int launch_attention(int dtype, int head_dim, int n, const AttnArgs &a, void *stream) {
+int launch_attention(int dtype, int head_dim, int waves, int n, const AttnArgs &a, void *stream) {
     hipStream_t s = (hipStream_t)stream;
     switch (dtype * 1000 + head_dim) {
-    case FL_BF16 * 1000 + 64: return (int)launch_attn_t<FL_BF16, 64>(n, a, s);
-    case FL_BF16 * 1000 + 128: return (int)launch_attn_t<FL_BF16, 128>(n, a, s);
-    case FL_F16 * 1000 + 64: return (int)launch_attn_t<FL_F16, 64>(n, a, s);
-    case FL_F16 * 1000 + 128: return (int)launch_attn_t<FL_F16, 128>(n, a, s);
-    case FL_F32 * 1000 + 64: return (int)launch_attn_t<FL_F32, 64>(n, a, s);
-    case FL_F32 * 1000 + 128: return (int)launch_attn_t<FL_F32, 128>(n, a, s);
-    default: return (int)hipErrorInvalidValue;
-    }
-}
-
-int launch_merge(int dtype, int head_dim, int n, const MergeArgs &a, void *stream) {
-    hipStream_t s = (hipStream_t)stream;
-    switch (dtype * 1000 + head_dim) {
-    case FL_BF16 * 1000 + 64: return (int)launch_merge_t<FL_BF16, 64>(n, a, s);
-    case FL_BF16 * 1000 + 128: return (int)launch_merge_t<FL_BF16, 128>(n, a, s);
-    case FL_F16 * 1000 + 64: return (int)launch_merge_t<FL_F16, 64>(n, a, s);
-    case FL_F16 * 1000 + 128: return (int)launch_merge_t<FL_F16, 128>(n, a, s);
-    case FL_F32 * 1000 + 64: return (int)launch_merge_t<FL_F32, 64>(n, a, s);
-    case FL_F32 * 1000 + 128: return (int)launch_merge_t<FL_F32, 128>(n, a, s);
+    case FL_BF16 * 1000 + 64: return (int)launch_w<FL_BF16, 64>(waves, n, a, s);
+    case FL_BF16 * 1000 + 128: return (int)launch_w<FL_BF16, 128>(waves, n, a, s);
+    case FL_F16 * 1000 + 64: return (int)launch_w<FL_F16, 64>(waves, n, a, s);
+    case FL_F16 * 1000 + 128: return (int)launch_w<FL_F16, 128>(waves, n, a, s);
+    case FL_F32 * 1000 + 64: return (int)launch_w<FL_F32, 64>(waves, n, a, s);
+    case FL_F32 * 1000 + 128: return (int)launch_w<FL_F32, 128>(waves, n, a, s);
     default: return (int)hipErrorInvalidValue;
     }
 }

@@ -1,5 +1,5 @@
-// Host planner: validates one step's page-table metadata and cuts the attention work into
-// items for the gfx950 kernels. Integer arithmetic only; no HIP calls.
+// Host planner: validates one step's page-table metadata and lays the attention work out
+// for the gfx950 kernel. Integer arithmetic only; no HIP calls.
 //
 // Work decomposition.
 //   * A row block is up to 16 flattened query rows of one request and one kv head, the
@@ -7,14 +7,22 @@
 //     one block of G rows per kv head; a prefill chunk of qo_len rows gives
 //     ceil(qo_len * G / 16) blocks. All rows of a block share the block's K/V stream.
 //   * A block's keys are [0, kv_end): kv_end = kv_len, or with the causal mask the last
-//     key its final row may see plus one (kv_len - qo_len + i_last + 1).
-//   * Long key ranges are cut into slices that run as separate workgroups, and their
-//     partial results are merged by log-sum-exp afterwards ("A library kernel for decode",
-//     What changed: slices of one history spread over many processor groups). The slice
-//     length is chosen from the total work and the compute-unit count so that the
-//     longest histories, which set the step's cost (same write-up, What I expected), are
-//     spread over the whole chip, while short histories stay in one slice.
-//   * The plan depends on the lengths only, never on page ids.
+//     key its final row may see plus one (kv_len - qo_len + i_last + 1); they form
+//     ceil(kv_end / 16) tiles.
+//   * Every block's tiles are laid in one sequence (request, kv head, row block order) and
+//     the sequence is cut into equal contiguous shares, one per workgroup, about one
+//     workgroup per compute unit. Long histories thereby spread over many compute units
+//     and short ones pack together, so every unit streams the same number of tiles
+//     ("A library kernel for decode", What changed: one history's slices run on many
+//     processor groups; What I expected: the longest histories set the step's cost).
+//     A block cut by a share boundary becomes several pieces whose partial results are
+//     merged by log-sum-exp; only the first and last piece of a share can be partial.
+//   * Within a share's segment, tile j runs on wave j % NW as that wave's step j / NW, and
+//     each segment's per-wave step count is padded to a multiple of the ring depth, so
+//     segment boundaries fall on the same step in every wave. For each wave and step the
+//     plan records the pool row of the tile's first key, (page * P + slot) * Hkv + kv_head,
+//     so the kernel addresses K and V without reading the page table.
+//   * The plan depends on the lengths only; page ids enter only the recorded pool rows.
 #include <algorithm>
 #include <cstdio>
 #include <numeric>
@@ -68,6 +76,10 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         return fail(err, FL_ERR_INVALID_ARG, "qo_indptr[0] = %lld, expected 0", in.qo_indptr[0]);
     if (in.num_pages <= 0 || in.num_pages > INT32_MAX)
         return fail(err, FL_ERR_INVALID_ARG, "num_pages %lld outside [1, 2^31)", in.num_pages);
+    if (in.num_pages * P * Hkv > INT32_MAX)
+        return fail(err, FL_ERR_UNSUPPORTED,
+                    "pool of %lld pages x %lld slots x %lld kv heads exceeds 2^31 rows", in.num_pages,
+                    P, Hkv);
 
     // ---- validate every request -----------------------------------------------------
     for (int32_t r = 0; r < B; ++r) {
@@ -106,7 +118,7 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
             return fail(err, FL_ERR_INVALID_ARG, "kv_indices[%lld] = %lld outside [0, %lld)", j,
                         pg, in.num_pages);
     }
-    out.nnz = nnz;
+
 
     // ---- row blocks -------------------------------------------------------------------
     std::vector<Block> blocks;
@@ -124,104 +136,143 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
             }
     }
     const int64_t nblocks = (int64_t)blocks.size();
-    std::vector<int64_t> tiles(nblocks);
-    int64_t total_tiles = 0;
+    std::vector<int64_t> tiles(nblocks), first_tile(nblocks + 1, 0);
     for (int64_t b = 0; b < nblocks; ++b) {
         tiles[b] = ceil_div(blocks[b].kv_end, kTileTokens);
-        total_tiles += tiles[b];
+        first_tile[b + 1] = first_tile[b] + tiles[b];
     }
+    const int64_t T = first_tile[nblocks];
 
-    // ---- slices per block ----------------------------------------------------------------
-    // tiles per slice for block b given a slice budget; balanced so no slice is empty.
-    std::vector<int64_t> nsplit(nblocks), per(nblocks);
-    auto assign = [&](int64_t chunk_tiles, int64_t fixed) {
-        int64_t items = 0, prows = 0;
-        for (int64_t b = 0; b < nblocks; ++b) {
-            int64_t s = fixed > 0 ? std::min<int64_t>(fixed, tiles[b]) : ceil_div(tiles[b], chunk_tiles);
-            s = std::max<int64_t>(1, s);
-            const int64_t p = ceil_div(tiles[b], s);
-            s = ceil_div(tiles[b], p);
-            nsplit[b] = s;
-            per[b] = p;
-            items += s;
-            if (s > 1) prows += s * blocks[b].nrows;
-        }
-        return std::make_pair(items, prows);
+    // ---- pieces: (block, tile range), grouped by workgroup -----------------------------
+    struct Piece {
+        int64_t block, lo, hi, group;
     };
-    std::pair<int64_t, int64_t> use;
+    std::vector<Piece> pieces;
+    int64_t G_wg = 0;
     if (in.num_splits > 0) {
-        use = assign(0, in.num_splits);
-        if (use.first > lim.item_cap || use.second > lim.part_rows_cap)
-            return fail(err, FL_ERR_CAPACITY,
-                        "num_splits %lld needs %lld work items (cap %lld); lower it or raise "
-                        "split_items_per_cu", in.num_splits, use.first, lim.item_cap);
+        // every block in num_splits balanced pieces (fewer for short blocks), one workgroup each
+        for (int64_t b = 0; b < nblocks; ++b) {
+            int64_t s = std::max<int64_t>(1, std::min<int64_t>(in.num_splits, tiles[b]));
+            const int64_t per = ceil_div(tiles[b], s);
+            s = ceil_div(tiles[b], per);
+            for (int64_t j = 0; j < s; ++j)
+                pieces.push_back({b, j * per, std::min<int64_t>((j + 1) * per, tiles[b]), G_wg++});
+        }
     } else {
-        const int64_t target = (int64_t)lim.num_cus * lim.split_items_per_cu;
-        const int64_t min_tiles = std::max<int64_t>(1, lim.min_split_tokens / kTileTokens);
-        int64_t chunk = std::max(min_tiles, ceil_div(total_tiles, std::max<int64_t>(1, target)));
-        use = assign(chunk, 0);
-        while (use.first > lim.item_cap || use.second > lim.part_rows_cap) {
-            chunk *= 2;
-            use = assign(chunk, 0);
+        // equal contiguous shares of the tile sequence
+        const int64_t want = (int64_t)lim.num_cus * lim.groups_per_cu;
+        G_wg = std::max<int64_t>(1, std::min(want, ceil_div(T, lim.min_group_tiles)));
+        G_wg = std::min(G_wg, T);
+        int64_t b = 0;
+        for (int64_t g = 0; g < G_wg; ++g) {
+            const int64_t a0 = T * g / G_wg, a1 = T * (g + 1) / G_wg;
+            int64_t pos = a0;
+            while (pos < a1) {
+                while (first_tile[b + 1] <= pos) ++b;
+                const int64_t hi = std::min(a1, first_tile[b + 1]);
+                pieces.push_back({b, pos - first_tile[b], hi - first_tile[b], g});
+                pos = hi;
+            }
         }
     }
-    if (use.first > INT32_MAX)
-        return fail(err, FL_ERR_CAPACITY, "too many work items (%lld)", use.first);
+    if ((int64_t)pieces.size() > lim.seg_cap || G_wg > lim.group_cap)
+        return fail(err, FL_ERR_CAPACITY, "%lld work items / %lld workgroups exceed the handle's "
+                    "capacity (%lld); lower num_splits", (long long)pieces.size(), G_wg, lim.seg_cap);
 
-    // ---- emit items: longest slices first, so the tail of the launch holds short work --
-    struct Pending {
-        int64_t block, split, tok_begin, tok_end, part_row;
-    };
-    std::vector<Pending> pend;
-    pend.reserve((size_t)use.first);
+    // pieces per block, partial rows and merge tickets
+    std::vector<int32_t> npieces(nblocks, 0), piece_idx(pieces.size());
+    for (size_t k = 0; k < pieces.size(); ++k) piece_idx[k] = npieces[pieces[k].block]++;
+    std::vector<int64_t> part_base(nblocks, -1);
+    std::vector<int32_t> merge_of(nblocks, -1);
     int64_t part_next = 0;
+    int32_t merges = 0;
     for (int64_t b = 0; b < nblocks; ++b) {
-        const Block &bl = blocks[b];
-        const int64_t s = nsplit[b];
-        const int64_t base = s > 1 ? part_next : -1;
-        if (s > 1) {
-            out.merges.insert(out.merges.end(), kMergeInts, 0);
-            int32_t *m = &out.merges[out.merges.size() - kMergeInts];
-            m[MI_Q_START] = in.qo_indptr ? in.qo_indptr[bl.req] : bl.req;
-            m[MI_KV_HEAD] = bl.kvh;
-            m[MI_ROW_BEGIN] = bl.row_begin;
-            m[MI_NUM_ROWS] = bl.nrows;
-            m[MI_PART_ROW] = (int32_t)base;
-            m[MI_NUM_SPLITS] = (int32_t)s;
-            part_next += s * bl.nrows;
+        out.max_splits = std::max(out.max_splits, npieces[b]);
+        if (npieces[b] > 1) {
+            part_base[b] = part_next;
+            part_next += (int64_t)npieces[b] * blocks[b].nrows;
+            merge_of[b] = merges++;
         }
-        for (int64_t j = 0; j < s; ++j) {
-            const int64_t t0 = j * per[b] * kTileTokens;
-            const int64_t t1 = std::min<int64_t>((j + 1) * per[b] * kTileTokens, bl.kv_end);
-            pend.push_back({b, j, t0, t1, s > 1 ? base + j * bl.nrows : -1});
+    }
+    if (part_next > lim.part_rows_cap)
+        return fail(err, FL_ERR_CAPACITY, "%lld partial rows exceed the workspace (%lld rows)",
+                    part_next, lim.part_rows_cap);
+
+    // ---- emit segments, workgroup tables and per-wave step rows --------------------------
+    // Within a segment, tile j goes to wave j % NW as that wave's step j / NW; every
+    // segment's per-wave step count is rounded up to a multiple of the ring depth, the
+    // same in all waves. Padding steps repeat a real tile of the segment (never scored).
+    const int NW = lim.waves;
+    out.segs.assign(pieces.size() * FL_WORK_ITEM_INTS, 0);
+    out.wg_segs.assign(G_wg + 1, 0);
+    out.wg_pos.assign(G_wg + 1, 0);
+    out.step_rows.clear();
+    std::vector<int64_t> seg_steps(pieces.size());
+    int64_t total = 0;
+    for (size_t k = 0; k < pieces.size(); ++k) {
+        const int64_t nt = pieces[k].hi - pieces[k].lo;
+        seg_steps[k] = ceil_div(ceil_div(nt, NW), kRingDepth) * kRingDepth;
+        total += seg_steps[k] * NW;
+    }
+    if (total > lim.max_tiles)
+        return fail(err, FL_ERR_CAPACITY, "%lld tile steps exceed max_tiles %lld", total,
+                    lim.max_tiles);
+    out.step_rows.assign((size_t)total, 0);
+    size_t k = 0;
+    int64_t off = 0;
+    for (int64_t g = 0; g < G_wg; ++g) {
+        out.wg_segs[g] = (int32_t)k;
+        out.wg_pos[g] = (int32_t)off;
+        size_t k_end = k;
+        int64_t steps = 0;
+        while (k_end < pieces.size() && pieces[k_end].group == g) steps += seg_steps[k_end++];
+        int64_t pos = 0;
+        for (; k < k_end; ++k) {
+            const Piece &pc = pieces[k];
+            const Block &bl = blocks[pc.block];
+            const int32_t np = in.kv_indptr[bl.req + 1] - in.kv_indptr[bl.req];
+            const int32_t kv_len = (np - 1) * P + in.last_page_len[bl.req];
+            const int64_t t0 = pc.lo * kTileTokens;
+            const int64_t t1 = std::min<int64_t>(pc.hi * kTileTokens, bl.kv_end);
+            int32_t *it = &out.segs[k * FL_WORK_ITEM_INTS];
+            it[FL_WI_Q_START] = in.qo_indptr ? in.qo_indptr[bl.req] : bl.req;
+            it[FL_WI_QO_LEN] = in.qo_indptr ? in.qo_indptr[bl.req + 1] - in.qo_indptr[bl.req] : 1;
+            it[FL_WI_KV_LEN] = kv_len;
+            it[FL_WI_PAGE_BASE] = in.kv_indptr[bl.req];
+            it[FL_WI_KV_HEAD] = bl.kvh;
+            it[FL_WI_ROW_BEGIN] = bl.row_begin;
+            it[FL_WI_NUM_ROWS] = bl.nrows;
+            it[FL_WI_TOK_BEGIN] = (int32_t)t0;
+            it[FL_WI_TOK_END] = (int32_t)t1;
+            it[FL_WI_PART_ROW] =
+                npieces[pc.block] > 1
+                    ? (int32_t)(part_base[pc.block] + (int64_t)piece_idx[k] * bl.nrows)
+                    : -1;
+            it[FL_WI_REQUEST] = bl.req;
+            it[FL_WI_SPLIT] = piece_idx[k];
+            it[FL_WI_NUM_SPLITS] = npieces[pc.block];
+            it[FL_WI_MERGE] = merge_of[pc.block];
+            it[FL_WI_GROUP] = (int32_t)g;
+            it[FL_WI_POS_BEGIN] = (int32_t)pos;
+            const int32_t *pages = in.kv_indices + in.kv_indptr[bl.req];
+            const int64_t nt = pc.hi - pc.lo;
+            for (int64_t q = 0; q < seg_steps[k]; ++q)
+                for (int w = 0; w < NW; ++w) {
+                    int64_t j = q * NW + w;
+                    if (j >= nt) j = (nt - 1 - w >= 0) ? nt - 1 - ((nt - 1 - w) % NW) : 0;
+                    const int64_t t = t0 + j * kTileTokens;
+                    const int64_t slot = (int64_t)pages[t / P] * P + t % P;
+                    out.step_rows[off + w * steps + pos + q] = (int32_t)(slot * Hkv + bl.kvh);
+                }
+            pos += seg_steps[k];
         }
-        out.max_splits = std::max<int32_t>(out.max_splits, (int32_t)s);
+        off += steps * NW;
     }
-    std::stable_sort(pend.begin(), pend.end(), [](const Pending &a, const Pending &b) {
-        return (a.tok_end - a.tok_begin) > (b.tok_end - b.tok_begin);
-    });
-    out.items.assign(pend.size() * FL_WORK_ITEM_INTS, 0);
-    for (size_t k = 0; k < pend.size(); ++k) {
-        const Pending &p = pend[k];
-        const Block &bl = blocks[p.block];
-        int32_t *it = &out.items[k * FL_WORK_ITEM_INTS];
-        const int32_t np = in.kv_indptr[bl.req + 1] - in.kv_indptr[bl.req];
-        it[FL_WI_Q_START] = in.qo_indptr ? in.qo_indptr[bl.req] : bl.req;
-        it[FL_WI_QO_LEN] = in.qo_indptr ? in.qo_indptr[bl.req + 1] - in.qo_indptr[bl.req] : 1;
-        it[FL_WI_KV_LEN] = (np - 1) * P + in.last_page_len[bl.req];
-        it[FL_WI_PAGE_BASE] = in.kv_indptr[bl.req];
-        it[FL_WI_KV_HEAD] = bl.kvh;
-        it[FL_WI_ROW_BEGIN] = bl.row_begin;
-        it[FL_WI_NUM_ROWS] = bl.nrows;
-        it[FL_WI_TOK_BEGIN] = (int32_t)p.tok_begin;
-        it[FL_WI_TOK_END] = (int32_t)p.tok_end;
-        it[FL_WI_PART_ROW] = (int32_t)p.part_row;
-        it[FL_WI_REQUEST] = bl.req;
-        it[FL_WI_SPLIT] = (int32_t)p.split;
-        it[FL_WI_NUM_SPLITS] = (int32_t)nsplit[p.block];
-    }
-    out.num_items = (int32_t)pend.size();
-    out.num_merges = (int32_t)(out.merges.size() / kMergeInts);
+    out.wg_segs[G_wg] = (int32_t)k;
+    out.wg_pos[G_wg] = (int32_t)off;
+    out.num_groups = (int32_t)G_wg;
+    out.num_segs = (int32_t)pieces.size();
+    out.num_merges = merges;
     out.part_rows = part_next;
     return FL_OK;
 }

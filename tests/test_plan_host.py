@@ -106,8 +106,9 @@ def test_plan_covers_every_row_and_key_once(name, splits):
         return
     items = plan_batch(h, b, num_splits=splits)
     check_coverage(items, b)
-    n, ms, ws = h.info()
+    n, ng, ms, ws = h.info()
     assert n == len(items)
+    assert ng == items[:, fl.WORK_ITEM_FIELDS.index("group")].max() + 1
     if splits == 1:
         assert ms == 1 and ws == 0
 
@@ -130,21 +131,42 @@ def test_plan_depends_only_on_lengths():
     assert np.array_equal(plan_batch(h, b), i1)   # and deterministic
 
 
-def test_long_histories_are_spread_and_short_ones_kept_whole():
+def tiles_per_group(items):
+    idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
+    g = items[:, idx["group"]]
+    t = -(-(items[:, idx["tok_end"]] - items[:, idx["tok_begin"]]) // 16)
+    return np.bincount(g, weights=t).astype(int)
+
+
+def test_long_histories_are_spread_and_shares_are_equal():
     lens = W.long_context_lengths(0)
     b = W.make_batch(lens, num_qo_heads=12, num_kv_heads=2, head_dim=64, page_size=256,
                      dtype="f16", num_pages=1200, poison=False)
-    h = host_handle(Hq=12, Hkv=2, P=256, dtype="f16", max_pages=4096)
+    h = host_handle(Hq=12, Hkv=2, P=256, dtype="f16", max_pages=4096, num_cus=256)
     items = plan_batch(h, b)
     idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
     kvl = items[:, idx["kv_len"]]
     ns = items[:, idx["num_splits"]]
-    assert ns[kvl == 32768].min() >= 16        # one long history runs on many CUs
-    assert ns[kvl == 512].max() <= 2
-    assert len(items) >= 256                    # enough workgroups to fill the chip
-    # launch order: longest slices first
-    span = items[:, idx["tok_end"]] - items[:, idx["tok_begin"]]
-    assert (np.diff(span) <= 0).all()
+    assert ns[kvl == 32768].min() >= 8          # one long history runs on many CUs
+    assert ns[kvl == 512].max() <= 2            # short ones stay (nearly) whole
+    tpg = tiles_per_group(items)
+    assert len(tpg) == 256                      # one share per compute unit
+    assert tpg.max() - tpg.min() <= 1           # equal shares
+    # a share cuts at most its first and last segment out of a longer row block
+    g = items[:, idx["group"]]
+    for gg in range(256):
+        sel = np.where(g == gg)[0]
+        inner = sel[1:-1]
+        assert (items[inner, idx["num_splits"]] == 1).all()
+
+
+def test_decode_batch_of_equal_histories_is_not_split():
+    b = W.saturated_decode()
+    h = host_handle(num_cus=256)
+    items = plan_batch(h, b)
+    idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
+    assert (items[:, idx["num_splits"]] == 1).all()
+    assert len(items) == 256 and (tiles_per_group(items) == 19).all()
 
 
 def test_forced_splits_are_capped_by_tiles():
@@ -211,7 +233,7 @@ def test_capacity_limits():
 def test_empty_batch_plans_to_nothing():
     h = host_handle()
     h.plan(np.zeros(1, np.int32), np.zeros(1, np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32), 1)
-    assert h.info()[0] == 0
+    assert h.info()[:2] == (0, 0)
 
 
 def test_create_rejects_unsupported_configs():
