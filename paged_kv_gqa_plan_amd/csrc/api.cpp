@@ -173,7 +173,9 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
     const int64_t tiles_bound = blocks * ((L.max_kv_pages * L.page_size + 15) / 16 + 1) +
                                 L.seg_cap * fl::kRingDepth * h->waves;
     L.max_tiles = cfg->max_tiles > 0 ? cfg->max_tiles : std::min<int64_t>(tiles_bound, 1LL << 24);
-    L.part_rows_cap = L.seg_cap * fl::kBlockRows;
+    // partial rows are addressed with 32-bit byte offsets: keep the workspace under 2 GiB
+    L.part_rows_cap = std::min<int64_t>(L.seg_cap * fl::kBlockRows,
+                                        (INT32_MAX / 4) / (cfg->head_dim + 1));
     if (L.seg_cap > INT32_MAX / FL_WORK_ITEM_INTS || L.max_tiles > INT32_MAX) {
         release(h);
         return set_err(FL_ERR_CAPACITY, "capacities too large");

@@ -417,6 +417,55 @@ struct F32Tile {
 };
 
 // ---------------------------------------------------------------------------------------
+// device-scope (cache policy SC1) accesses to the fp32 partial rows: stores write through
+// to the point of coherence shared by all XCDs, loads read from it. Buffer instructions
+// carry the policy bit on 8- and 16-byte accesses.
+// ---------------------------------------------------------------------------------------
+constexpr int kDeviceScope = 16;  // SC1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const float *base) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, 0x7fffffff, 0x00020000);
+}
+template <int N>
+__device__ __forceinline__ void part_store(__amdgpu_buffer_rsrc_t rs, int byte_off, const float *v) {
+    static_assert(N % 2 == 0, "even");
+#pragma unroll
+    for (int e = 0; e < N; e += (N % 4 == 0 ? 4 : 2)) {
+        if constexpr (N % 4 == 0)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{__float_as_uint(v[e]), __float_as_uint(v[e + 1]), __float_as_uint(v[e + 2]),
+                      __float_as_uint(v[e + 3])},
+                rs, byte_off + 4 * e, 0, kDeviceScope);
+        else
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(v[e]), __float_as_uint(v[e + 1])},
+                                                  rs, byte_off + 4 * e, 0, kDeviceScope);
+    }
+}
+template <int N>
+__device__ __forceinline__ void part_load(__amdgpu_buffer_rsrc_t rs, int byte_off, float *v) {
+    static_assert(N % 2 == 0, "even");
+#pragma unroll
+    for (int e = 0; e < N; e += (N % 4 == 0 ? 4 : 2)) {
+        if constexpr (N % 4 == 0) {
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off + 4 * e, 0, kDeviceScope);
+            v[e] = __uint_as_float(x[0]);
+            v[e + 1] = __uint_as_float(x[1]);
+            v[e + 2] = __uint_as_float(x[2]);
+            v[e + 3] = __uint_as_float(x[3]);
+        } else {
+            const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, byte_off + 4 * e, 0, kDeviceScope);
+            v[e] = __uint_as_float(x[0]);
+            v[e + 1] = __uint_as_float(x[1]);
+        }
+    }
+}
+__device__ __forceinline__ float part_load1(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, byte_off, 0, kDeviceScope));
+}
+__device__ __forceinline__ void part_store1(__amdgpu_buffer_rsrc_t rs, int byte_off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, byte_off, 0, kDeviceScope);
+}
+
+// ---------------------------------------------------------------------------------------
 // LDS for the per-segment fold: four wave states (8-wave groups fold pairwise first)
 // ---------------------------------------------------------------------------------------
 template <int D>
@@ -429,31 +478,47 @@ struct Smem {
 
 // Merge of a row block's pieces by the piece that finished last:
 //   M = max_s lse_s,  w_s = 2^(lse_s - M),  out = sum_s w_s o_s / sum_s w_s.
-// The partial rows were written with device-scope stores; they are read the same way.
+// The partial rows were written with device-scope stores and are read the same way, eight
+// pieces at a time with every load of a batch issued before any is used (the running max
+// carries across batches by rescaling, as in the online softmax). Partial-row byte
+// offsets fit in 32 bits: the workspace is sized from the handle's capacities.
 template <int DT, int D, int TPR>
 __device__ __forceinline__ void merge_pieces(const Seg &w, const AttnArgs &a, int r, int c0) {
     constexpr int EPT = D / TPR;
+    constexpr int MB = 8;
     const int nr = w.num_rows;
     const int base = w.part_row - w.split * nr;
     const int ns = w.num_splits;
-    float M = kNegInf;
-    for (int s = 0; s < ns; ++s)
-        M = fmaxf(M, __hip_atomic_load(a.part_lse + base + s * nr + r, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT));
+    float M = kNegInf, L = 0.f;
     float acc[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
-    float L = 0.f;
-#pragma unroll 2
-    for (int s = 0; s < ns; ++s) {
-        const int pr = base + s * nr + r;
-        const float wt = fast_exp2(
-            __hip_atomic_load(a.part_lse + pr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
-        L += wt;
-        const float *src = a.part_o + (int64_t)pr * D + c0;
+    const __amdgpu_buffer_rsrc_t ro = part_rsrc(a.part_o), rl = part_rsrc(a.part_lse);
+    for (int s0 = 0; s0 < ns; s0 += MB) {
+        float ls[MB];
+        float ov[MB][EPT];
 #pragma unroll
-        for (int e = 0; e < EPT; ++e)
-            acc[e] += wt * __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = 0; i < MB; ++i) {
+            const int pr = base + min(s0 + i, ns - 1) * nr + r;  // a repeat past the end is unused
+            ls[i] = part_load1(rl, pr * 4);
+            part_load<EPT>(ro, (pr * D + c0) * 4, ov[i]);
+        }
+        float bm = M;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+            if (s0 + i < ns) bm = fmaxf(bm, ls[i]);
+        const float sc = M == kNegInf ? 0.f : fast_exp2(M - bm);
+        L *= sc;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) acc[e] *= sc;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const float wt = s0 + i < ns ? fast_exp2(ls[i] - bm) : 0.f;
+            L += wt;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) acc[e] += wt * ov[i][e];
+        }
+        M = bm;
     }
     const float inv = 1.f / L;
 #pragma unroll
@@ -539,13 +604,8 @@ __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, con
             store_out<DT, EPT>(a.out, row * D + c0, res);
             if (a.lse && c0 == 0) a.lse[row] = lse2 * kLn2;
         } else {
-            float *dst = a.part_o + (int64_t)(cs.part_row + r) * D + c0;
-#pragma unroll
-            for (int e = 0; e < EPT; ++e)
-                __hip_atomic_store(dst + e, res[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (c0 == 0)
-                __hip_atomic_store(a.part_lse + cs.part_row + r, lse2, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            part_store<EPT>(part_rsrc(a.part_o), ((cs.part_row + r) * D + c0) * 4, res);
+            if (c0 == 0) part_store1(part_rsrc(a.part_lse), (cs.part_row + r) * 4, lse2);
         }
     }
     if (cs.part_row >= 0) {
