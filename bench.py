@@ -3,13 +3,16 @@
 A step is one pass of the whole hot path over one synthetic batch: one plan (host
 validation and partitioning plus the metadata copy) and one run per layer, each layer
 reading its own K/V pool, so consecutive calls never hit data a previous call left in the
-caches. Inputs are resident in device memory before the timed region starts.
+caches. Inputs are resident in device memory before the timed region starts. The layer
+runs of a step are captured once into a HIP graph and replayed after each plan (the plan
+refreshes the handle's persistent metadata in place, so the graph stays valid); --eager
+launches them one by one from Python instead.
 
 Reported (one JSON line):
   value        whole-job KV read rate in GB/s: algorithmic K+V bytes of all timed calls
                divided by the wall time of the timed steps (plans included)
-  us_per_call  mean duration of one layer's run() measured with HIP events on the stream
-               the kernels are launched on
+  us_per_call  HIP-event time of the step's layer runs on the launch stream, divided by
+               the number of layers
   roofline     the attention kernel against the 8 TB/s HBM peak
   cpu_baseline the CPU oracle on the host's cores, on the same batch
 
@@ -95,6 +98,81 @@ def cpu_baseline(b, gpu_out0, budget_s: float):
             "gpu_vs_oracle_max_abs": err}
 
 
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_per_dispatch(dir_, name_has: str, counter: str):
+    """Mean per-dispatch value of a rocprofv3 counter (KiB) for kernels whose name contains
+    name_has, from <dir>/run_counter_collection.csv."""
+    import glob
+    vals = []
+    for path in glob.glob(os.path.join(dir_, "**", "*counter_collection.csv"), recursive=True):
+        for r in _csv_rows(path):
+            if name_has in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {name_has!r} under {dir_}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_profiles(workload: str, kt: str, pf: str, pw: str, cf: str, cw: str, calib_mib: int,
+                       commands: str):
+    """Write profiles/attn_kernel_<workload>.md and profiles/traffic_<workload>.txt from
+    rocprofv3 CSV output: a kernel-trace run (kt) and FETCH_SIZE / WRITE_SIZE passes of the
+    benchmark (pf, pw) and of a plain copy of known size (cf, cw)."""
+    import glob
+    stats = None
+    for path in glob.glob(os.path.join(kt, "**", "*kernel_stats.csv"), recursive=True):
+        for r in _csv_rows(path):
+            if "attn_kernel" in r["Name"]:
+                stats = r
+    if stats is None:
+        raise SystemExit(f"no attention kernel in the kernel stats under {kt}")
+    fetch, nf = _counter_per_dispatch(pf, "attn_kernel", "FETCH_SIZE")
+    write, nw = _counter_per_dispatch(pw, "attn_kernel", "WRITE_SIZE")
+    cfetch, _ = _counter_per_dispatch(cf, "copyBuffer", "FETCH_SIZE")
+    cwrite, _ = _counter_per_dispatch(cw, "copyBuffer", "WRITE_SIZE")
+    known_kib = calib_mib * 1024.0
+    fscale, wscale = known_kib / cfetch, known_kib / cwrite
+    hbm_bytes = (fetch * fscale + write * wscale) * 1024.0
+    import workloads as W
+    b = W.WORKLOADS[workload]()
+    algo = b.kv_bytes()
+    avg_ns = float(stats["AverageNs"])
+    d = {"workload": workload, "source_hash": source_hash(),
+         "hbm_bytes_per_launch": round(hbm_bytes),
+         "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+         "fetch_scale": fscale, "write_scale": wscale,
+         "calibration": f"plain device copy of {calib_mib} MiB: FETCH_SIZE {cfetch:.1f} KiB, "
+                        f"WRITE_SIZE {cwrite:.1f} KiB per dispatch",
+         "kernel_avg_us": avg_ns / 1e3, "algorithmic_kv_bytes": algo}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.txt"), "w") as f:
+        f.write(json.dumps(d, indent=1) + "\n")
+    md = [f"# attention kernel, {workload} ({b.batch_size} requests, {int(b.kv_lens.sum())} cached "
+          f"tokens, {b.num_qo_heads}/{b.num_kv_heads} heads, d {b.head_dim}, {b.dtype}, "
+          f"page size {b.page_size})", "",
+          "Commands (from the repository root on the GPU host):", "", "```", commands.strip(), "```", "",
+          "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+          "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|",
+          f"| {stats['Name'][:80]} | {stats['Calls']} | {avg_ns / 1e3:.3f} | "
+          f"{float(stats['MinNs']) / 1e3:.3f} | {float(stats['MaxNs']) / 1e3:.3f} |", "",
+          f"Algorithmic K+V bytes per call: {algo} -> {algo / avg_ns:.1f} GB/s at the average "
+          f"duration ({algo / avg_ns / 8000.0 * 100:.1f}% of 8 TB/s).", "",
+          "## HBM traffic (rocprofv3 --pmc, one counter per run)", "",
+          f"* FETCH_SIZE {fetch:.1f} KiB per dispatch ({nf} dispatches), scale {fscale:.4f}",
+          f"* WRITE_SIZE {write:.1f} KiB per dispatch ({nw} dispatches), scale {wscale:.4f}",
+          f"* calibration: {d['calibration']} (the copy reads and writes {calib_mib} MiB each)",
+          f"* HBM bytes per launch: {hbm_bytes:.0f} ({hbm_bytes / algo:.3f} x the algorithmic "
+          f"K+V bytes)", ""]
+    with open(os.path.join(ROOT, "profiles", f"attn_kernel_{workload}.md"), "w") as f:
+        f.write("\n".join(md))
+    print(json.dumps(d))
+
+
 def copy_calibration(mib: int):
     """A plain device copy of known size (for scaling the HBM byte counters)."""
     import torch
@@ -121,9 +199,19 @@ def main(argv=None):
     ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (4 or 8; 0 = default)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch layer runs without a HIP graph")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-profiles", nargs=5, metavar=("KT", "PF", "PW", "CF", "CW"),
+                    help="write profiles/ summaries from rocprofv3 CSV directories (kernel "
+                         "trace; FETCH_SIZE and WRITE_SIZE of the bench; the same of a copy)")
+    ap.add_argument("--calib-mib", type=int, default=1024)
+    ap.add_argument("--commands", default="", help="commands recorded in the summary")
     args = ap.parse_args(argv)
+
+    if args.summarize_profiles:
+        summarize_profiles(args.workload, *args.summarize_profiles, args.calib_mib, args.commands)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -168,30 +256,45 @@ def main(argv=None):
         h.plan(b.qo_indptr, b.kv_indptr, b.kv_indices, b.last_page_len, b.num_pages,
                causal=b.causal, sm_scale=b.sm_scale, num_splits=args.splits)
 
-    def step(evs=None):
-        plan()
+    def layers():
         for l in range(L):
-            if evs is not None:
-                evs[l][0].record(stream)
             h.run(q, ks[l], vs[l], outs[l])
-            if evs is not None:
-                evs[l][1].record(stream)
+
+    graph = None
+    if not args.eager:
+        plan()
+        layers()  # first launches outside the capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layers()
+
+    def step(ev=None):
+        plan()
+        if ev is not None:
+            ev[0].record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            layers()
+        if ev is not None:
+            ev[1].record(stream)
 
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
     n_items, n_groups, max_splits, ws_bytes = h.info()
 
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(L)] for _ in range(args.steps)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     plan_s = 0.0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
+    for s_ in range(args.steps):
+        step(evs[s_])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_ms = [a.elapsed_time(e) for row in evs for (a, e) in row]
+    call_ms = [a.elapsed_time(e) / L for (a, e) in evs]
     # plan host time, measured on its own after the timed region
     for _ in range(10):
         t1 = time.perf_counter()
@@ -229,6 +332,7 @@ def main(argv=None):
         "kv_bytes_per_call": kv_bytes,
         "hbm_peak_frac_per_call": round(achieved / HBM_PEAK_GBS, 4),
         "attention_us_per_step": round(us_call * L, 2),
+        "launch": "eager" if args.eager else "hip_graph",
         "plan_host_us": round(plan_us, 2),
         "work_items": n_items,
         "workgroups": n_groups,
