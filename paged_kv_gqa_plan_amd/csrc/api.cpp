@@ -48,10 +48,10 @@ struct fl_paged_attn {
     int32_t log2_page = 0;
 
     // device buffers
-    char *d_meta = nullptr;      // [segments | wg_segs | wg_pos | merge tickets | step rows]
+    char *d_meta = nullptr;      // [segments | workgroup records | merge tickets | step rows]
     float *d_part_o = nullptr;   // [part_rows_cap, head_dim]
     float *d_part_lse = nullptr; // [part_rows_cap]
-    int64_t off_wg_segs = 0, off_wg_pos = 0, off_tickets = 0, off_steps = 0, meta_bytes = 0;
+    int64_t off_wg_rec = 0, off_tickets = 0, off_steps = 0, meta_bytes = 0;
     int32_t waves = 4;
 
     // pinned staging, double-buffered
@@ -181,9 +181,8 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
         return set_err(FL_ERR_CAPACITY, "capacities too large");
     }
 
-    h->off_wg_segs = align_up(L.seg_cap * FL_WORK_ITEM_INTS * 4, 256);
-    h->off_wg_pos = align_up(h->off_wg_segs + (L.group_cap + 1) * 4, 256);
-    h->off_tickets = align_up(h->off_wg_pos + (L.group_cap + 1) * 4, 256);
+    h->off_wg_rec = align_up(L.seg_cap * FL_WORK_ITEM_INTS * 4, 256);
+    h->off_tickets = align_up(h->off_wg_rec + L.group_cap * fl::kRecInts * 4, 256);
     h->off_steps = align_up(h->off_tickets + blocks * 4, 256);
     h->meta_bytes = align_up(h->off_steps + std::max<int64_t>(1, L.max_tiles) * 4, 256);
 
@@ -246,8 +245,7 @@ fl_status fl_paged_attn_plan(fl_handle h, int32_t batch, const int32_t *qo_indpt
         char *st_buf = h->h_stage[slot];
         const Plan &p = h->plan;
         std::memcpy(st_buf, p.segs.data(), p.segs.size() * 4);
-        std::memcpy(st_buf + h->off_wg_segs, p.wg_segs.data(), p.wg_segs.size() * 4);
-        std::memcpy(st_buf + h->off_wg_pos, p.wg_pos.data(), p.wg_pos.size() * 4);
+        std::memcpy(st_buf + h->off_wg_rec, p.wg_rec.data(), p.wg_rec.size() * 4);
         // merge tickets start at zero for every plan (the kernel keeps them at zero between
         // runs: the piece that merges a row block resets its ticket)
         std::memset(st_buf + h->off_tickets, 0, (size_t)p.num_merges * 4);
@@ -280,8 +278,7 @@ fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, cons
 
     fl::AttnArgs a{};
     a.segs = (const int32_t *)h->d_meta;
-    a.wg_segs = (const int32_t *)(h->d_meta + h->off_wg_segs);
-    a.wg_pos = (const int32_t *)(h->d_meta + h->off_wg_pos);
+    a.wg_rec = (const int32_t *)(h->d_meta + h->off_wg_rec);
     a.step_rows = (const int32_t *)(h->d_meta + h->off_steps);
     a.tickets = (int32_t *)(h->d_meta + h->off_tickets);
     a.q = q;

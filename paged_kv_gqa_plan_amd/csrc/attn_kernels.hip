@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fl_internal.h"
 
 namespace fl {
@@ -122,6 +124,24 @@ struct Seg {  // wave-uniform fields of the segment being computed
     int q_start, qo_len, kv_len, kv_head, row_begin, num_rows, tok_begin, tok_end, part_row,
         split, num_splits, merge, pos_begin;
 };
+// the same fields read from memory with wave-uniform (scalar) loads
+__device__ __forceinline__ Seg seg_fields_mem(const int32_t *h) {
+    Seg s;
+    s.q_start = h[FL_WI_Q_START];
+    s.qo_len = h[FL_WI_QO_LEN];
+    s.kv_len = h[FL_WI_KV_LEN];
+    s.kv_head = h[FL_WI_KV_HEAD];
+    s.row_begin = h[FL_WI_ROW_BEGIN];
+    s.num_rows = h[FL_WI_NUM_ROWS];
+    s.tok_begin = h[FL_WI_TOK_BEGIN];
+    s.tok_end = h[FL_WI_TOK_END];
+    s.part_row = h[FL_WI_PART_ROW];
+    s.split = h[FL_WI_SPLIT];
+    s.num_splits = h[FL_WI_NUM_SPLITS];
+    s.merge = h[FL_WI_MERGE];
+    s.pos_begin = h[FL_WI_POS_BEGIN];
+    return s;
+}
 __device__ __forceinline__ Seg seg_fields(int hv) {
     Seg s;
     s.q_start = hfield(hv, FL_WI_Q_START);
@@ -632,7 +652,9 @@ __device__ __forceinline__ int load_step_rows(const int32_t *rows, int win, int 
 // ---------------------------------------------------------------------------------------
 template <class T, int DT, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
-    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+    static_assert((NW == 4 || NW == 8) && NW <= kMaxWaves, "4 or 8 waves");
+    static_assert(REC_ROWS + kMaxWaves * kRingDepth <= REC_HEAD &&
+                  REC_HEAD + FL_WORK_ITEM_INTS <= kRecInts, "record layout");
     constexpr int PF = kRingDepth;
     constexpr int NJ = D / 16;
     constexpr int TPR = NW * 64 / kBlockRows;  // fold: threads per row
@@ -644,24 +666,33 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     const int wave = threadIdx.x >> 6;
     const int col = lane & 15;
     const int grp = lane >> 4;
-    const int gid = blockIdx.x;
-    const int seg_b = a.wg_segs[gid], seg_e = a.wg_segs[gid + 1];
-    const int pos0 = a.wg_pos[gid];
-    const int nsteps = (a.wg_pos[gid + 1] - pos0) / NW;  // steps per wave (multiple of PF)
-    const int32_t *rows = a.step_rows + pos0 + wave * nsteps;
-
-    // segment headers two ahead, Q one ahead
-    int hv0 = load_header(a.segs, seg_b, lane);
-    int hv1 = seg_b + 1 < seg_e ? load_header(a.segs, seg_b + 1, lane) : 0;
-    int hv2 = seg_b + 2 < seg_e ? load_header(a.segs, seg_b + 2, lane) : 0;
+    // The workgroup record (scalar loads) gives the share, the first segment and every
+    // wave's first rows: the step rows, Q and the first K/V tiles all go out at once.
+    const int32_t *rec = a.wg_rec + (size_t)blockIdx.x * kRecInts;
+    const int seg_b = rec[REC_SEG_BEGIN], seg_e = rec[REC_SEG_END];
+    const int pos0 = rec[REC_POS];
+    const int nsteps = rec[REC_STEPS];  // steps per wave (multiple of PF)
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int32_t *rows = a.step_rows + pos0 + wv * nsteps;
+    int k = seg_b;
+    Seg cs = seg_fields_mem(rec + REC_HEAD);
+    int seg_end = rec[REC_FIRST_END];
     int rows_cur = load_step_rows(rows, 0, lane, nsteps);
     int rows_nxt = load_step_rows(rows, 64, lane, nsteps);
-    int k = seg_b;
-    Seg cs = seg_fields(hv0);
     RowInfo ri = row_info(cs, a, col);
     typename T::QOp qc = T::load_q(a, cs, ri, col, grp);
     typename T::QOp qn = qc;
-    int seg_end = k + 1 < seg_e ? hfield(hv1, FL_WI_POS_BEGIN) : nsteps;
+    // the next two segment headers (clamped: always one load each, used only if they exist);
+    // issued ahead of the ring so that waiting for them never waits for a K/V tile
+    int hv1 = load_header(a.segs, min(seg_b + 1, seg_e - 1), lane);
+    int hv2 = load_header(a.segs, min(seg_b + 2, seg_e - 1), lane);
+    __builtin_amdgcn_sched_barrier(0);
+    typename T::Frag buf[PF];
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+        T::load(buf[s], a.k, a.v, rec[REC_ROWS + wv * PF + s], a.num_kv_heads, col, grp);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     int ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
 
     float m_run = kNegInf, l_run = 0.f;
@@ -675,7 +706,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     // never scored), so the outstanding-load count is the same on every path and each tile
     // waits only for its own data.
     int win_issue = 0;
-    typename T::Frag buf[PF];
     auto issue = [&](typename T::Frag &f, int p) {  // p < nsteps
         if ((p & ~63) != win_issue) {              // next 64-step window of pool rows
             win_issue = p & ~63;
@@ -684,19 +714,15 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
         }
         T::load(f, a.k, a.v, __builtin_amdgcn_readlane(rows_cur, p & 63), a.num_kv_heads, col, grp);
     };
-#pragma unroll
-    for (int s = 0; s < PF; ++s) {
-        issue(buf[s], s);
-        __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
-    }
-    for (int p0 = 0; p0 < nsteps; p0 += PF) {
+    // One group of PF steps. The last group issues no refills, so nothing is in flight when
+    // the final fold starts.
+    auto group = [&](int p0, auto refill) {
         if (p0 == seg_end) {  // the same step in every wave: segment k is done
             fold_segment<T, DT, D, NW>(sm, a, cs, k, m_run, l_run, o, pend0, pend1, wave, col, grp);
             ++k;
-            hv0 = hv1;
+            cs = seg_fields(hv1);
             hv1 = hv2;
-            hv2 = k + 2 < seg_e ? load_header(a.segs, k + 2, lane) : 0;
-            cs = seg_fields(hv0);
+            hv2 = load_header(a.segs, min(k + 2, seg_e - 1), lane);
             ri = row_info(cs, a, col);
             qc = qn;
             seg_end = k + 1 < seg_e ? hfield(hv1, FL_WI_POS_BEGIN) : nsteps;
@@ -717,10 +743,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
                 T::compute(buf[s], qc, t0, col, grp, cs.tok_end, ri.limit, a.scale_log2, m_run,
                            l_run, o);
             }
-            issue(buf[s], min(p + PF, nsteps - 1));
+            if constexpr (decltype(refill)::value) issue(buf[s], min(p + PF, nsteps - 1));
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
+    int p0 = 0;  // nsteps is a positive multiple of PF
+    for (; p0 + PF < nsteps; p0 += PF) group(p0, std::true_type{});
+    group(p0, std::false_type{});
     fold_segment<T, DT, D, NW>(sm, a, cs, k, m_run, l_run, o, pend0, pend1, wave, col, grp);
 
     // ---- merge tickets of the partial pieces (at most the first and the last) -----------

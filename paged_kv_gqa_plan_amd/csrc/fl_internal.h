@@ -18,7 +18,20 @@ constexpr int kTileTokens = 16;
 constexpr int kBlockRows = 16;
 // Tiles of K and V each wave keeps in flight. Every segment's per-wave step count is a
 // multiple of it, so segment boundaries fall on the same loop step in every wave.
-constexpr int kRingDepth = 2;
+#ifndef FL_RING_DEPTH
+#define FL_RING_DEPTH 2
+#endif
+constexpr int kRingDepth = FL_RING_DEPTH;
+// Per-workgroup record (int32): segment range, step range, the first segment's header and
+// end step, and the pool rows of every wave's first kRingDepth steps, so every load a
+// workgroup issues first (Q, K/V, step rows) depends on this record alone.
+constexpr int kRecInts = 64;
+constexpr int kMaxWaves = 8;
+enum {
+    REC_SEG_BEGIN = 0, REC_SEG_END = 1, REC_POS = 2, REC_STEPS = 3, REC_FIRST_END = 4,
+    REC_ROWS = 8,    // kMaxWaves * kRingDepth entries
+    REC_HEAD = 48,   // FL_WORK_ITEM_INTS entries
+};
 
 struct PlanLimits {
     int32_t num_qo_heads, num_kv_heads, head_dim, page_size;
@@ -47,8 +60,7 @@ struct PlanInput {
 
 struct Plan {
     std::vector<int32_t> segs;      // FL_WORK_ITEM_INTS per segment, grouped by workgroup
-    std::vector<int32_t> wg_segs;   // num_groups + 1: segments of workgroup g
-    std::vector<int32_t> wg_pos;    // num_groups + 1: workgroup g's entries in step_rows
+    std::vector<int32_t> wg_rec;    // kRecInts per workgroup
     std::vector<int32_t> step_rows; // per workgroup, per wave, per step: pool row
                                     // (page * P + slot) * Hkv + kv_head of the step's tile's
                                     // first key (padding steps repeat a real tile's row)
@@ -71,8 +83,7 @@ int64_t row_block_bound(const PlanLimits &lim);
 // ---------------------------------------------------------------------------------------
 struct AttnArgs {
     const int32_t *segs;       // FL_WORK_ITEM_INTS per segment
-    const int32_t *wg_segs;    // num_groups + 1
-    const int32_t *wg_pos;     // num_groups + 1
+    const int32_t *wg_rec;     // kRecInts per workgroup
     const int32_t *step_rows;  // per workgroup, wave and step
     int32_t *tickets;          // one per merged row block, zero between runs
     const void *q;

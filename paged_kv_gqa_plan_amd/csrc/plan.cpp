@@ -204,8 +204,7 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
     // same in all waves. Padding steps repeat a real tile of the segment (never scored).
     const int NW = lim.waves;
     out.segs.assign(pieces.size() * FL_WORK_ITEM_INTS, 0);
-    out.wg_segs.assign(G_wg + 1, 0);
-    out.wg_pos.assign(G_wg + 1, 0);
+    out.wg_rec.assign(G_wg * kRecInts, 0);
     out.step_rows.clear();
     std::vector<int64_t> seg_steps(pieces.size());
     int64_t total = 0;
@@ -221,11 +220,16 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
     size_t k = 0;
     int64_t off = 0;
     for (int64_t g = 0; g < G_wg; ++g) {
-        out.wg_segs[g] = (int32_t)k;
-        out.wg_pos[g] = (int32_t)off;
+        int32_t *rec = &out.wg_rec[g * kRecInts];
         size_t k_end = k;
         int64_t steps = 0;
         while (k_end < pieces.size() && pieces[k_end].group == g) steps += seg_steps[k_end++];
+        rec[REC_SEG_BEGIN] = (int32_t)k;
+        rec[REC_SEG_END] = (int32_t)k_end;
+        rec[REC_POS] = (int32_t)off;
+        rec[REC_STEPS] = (int32_t)steps;
+        rec[REC_FIRST_END] = (int32_t)seg_steps[k];
+        const size_t k_first = k;
         int64_t pos = 0;
         for (; k < k_end; ++k) {
             const Piece &pc = pieces[k];
@@ -266,10 +270,12 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
                 }
             pos += seg_steps[k];
         }
+        std::copy_n(&out.segs[k_first * FL_WORK_ITEM_INTS], FL_WORK_ITEM_INTS, rec + REC_HEAD);
+        for (int w = 0; w < NW; ++w)  // every share has >= kRingDepth steps per wave
+            for (int q = 0; q < kRingDepth; ++q)
+                rec[REC_ROWS + w * kRingDepth + q] = out.step_rows[off + w * steps + q];
         off += steps * NW;
     }
-    out.wg_segs[G_wg] = (int32_t)k;
-    out.wg_pos[G_wg] = (int32_t)off;
     out.num_groups = (int32_t)G_wg;
     out.num_segs = (int32_t)pieces.size();
     out.num_merges = merges;
