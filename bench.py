@@ -196,7 +196,7 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=0, help="planner slice override (0 = automatic)")
     ap.add_argument("--groups-per-cu", type=int, default=0)
     ap.add_argument("--min-group-tokens", type=int, default=0)
-    ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (4 or 8; 0 = default)")
+    ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (4; 0 = default)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch layer runs without a HIP graph")

@@ -84,7 +84,7 @@ typedef struct {
                                   0 = library default (1)                                */
     int32_t min_group_tokens;  /* fewest keys (per row block piece) a workgroup's share
                                   may hold before fewer workgroups are used; 0 = default */
-    int32_t waves_per_group;   /* wavefronts per workgroup, 4 or 8; 0 = library default  */
+    int32_t waves_per_group;   /* wavefronts per workgroup: 4 (0 = the same)              */
     int64_t max_tiles;         /* most 16-key tiles (over all row blocks) one plan may
                                   hold; 0 = a bound derived from the other capacities     */
 } fl_config;

@@ -86,8 +86,8 @@ fl_status check_config(const fl_config *c) {
     if (c->num_cus < 0 || c->groups_per_cu < 0 || c->min_group_tokens < 0 || c->max_tiles < 0)
         return set_err(FL_ERR_INVALID_ARG, "num_cus, groups_per_cu, min_group_tokens and "
                                            "max_tiles must be >= 0");
-    if (c->waves_per_group != 0 && c->waves_per_group != 4 && c->waves_per_group != 8)
-        return set_err(FL_ERR_UNSUPPORTED, "waves_per_group must be 0, 4 or 8");
+    if (c->waves_per_group != 0 && c->waves_per_group != 4)
+        return set_err(FL_ERR_UNSUPPORTED, "waves_per_group must be 0 or 4");
     return FL_OK;
 }
 

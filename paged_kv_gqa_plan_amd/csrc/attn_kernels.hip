@@ -54,6 +54,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -112,13 +113,52 @@ __device__ __forceinline__ T ld_global(const void *p) {
     return *reinterpret_cast<const T *>(p);
 }
 
-// ---------------------------------------------------------------------------------------
-// segment headers: lanes 0..15 of one vector register hold the FL_WORK_ITEM_INTS fields
-// ---------------------------------------------------------------------------------------
-__device__ __forceinline__ int load_header(const int32_t *segs, int seg, int lane) {
-    return lane < FL_WORK_ITEM_INTS ? ld_global<int>(segs + (size_t)seg * FL_WORK_ITEM_INTS + lane) : 0;
+// Wait until at most N vector-memory loads of this wave are outstanding (loads complete in
+// issue order). The memory clobber keeps the LDS reads that follow below the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-__device__ __forceinline__ int hfield(int hv, int f) { return __builtin_amdgcn_readlane(hv, f); }
+// Wait until this wave's LDS reads have returned (before a slot is refilled).
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Loads straight into LDS: lane l's 16 (4) bytes at base + voff land at LDS byte
+// lds + 16l (4l). base and lds are wave-uniform. They are issued from inline assembly, so
+// the compiler neither counts nor waits for them: every read of their data follows an
+// explicit wait_vm (loads complete in issue order), and the compiler's own waits for the
+// loads it does see only grow stricter with loads it does not.
+__device__ __forceinline__ void dma_b128(const void *base, uint32_t voff, const lds_char *lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+                 "s"((uint32_t)(uintptr_t)lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const void *base, uint32_t voff, const lds_char *lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base),
+                 "s"((uint32_t)(uintptr_t)lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ int lds_int(const lds_char *p) {
+    return __builtin_amdgcn_readfirstlane(*(const __attribute__((address_space(3))) int *)p);
+}
+
+// compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// segment headers (FL_WORK_ITEM_INTS fields): the first from the workgroup record, the
+// next ones copied into a per-wave LDS slot of 256 bytes (lanes 16..63 repeat the fields)
+// ---------------------------------------------------------------------------------------
+constexpr int kHdrSlot = 256;
+__device__ __forceinline__ void stage_header(const lds_char *slot, const int32_t *segs, int seg, int lane) {
+    dma_b32(segs + (size_t)seg * FL_WORK_ITEM_INTS, 4u * (uint32_t)(lane & (FL_WORK_ITEM_INTS - 1)), slot);
+}
 
 struct Seg {  // wave-uniform fields of the segment being computed
     int q_start, qo_len, kv_len, kv_head, row_begin, num_rows, tok_begin, tok_end, part_row,
@@ -142,21 +182,21 @@ __device__ __forceinline__ Seg seg_fields_mem(const int32_t *h) {
     s.pos_begin = h[FL_WI_POS_BEGIN];
     return s;
 }
-__device__ __forceinline__ Seg seg_fields(int hv) {
+__device__ __forceinline__ Seg seg_fields_lds(const lds_char *h) {
     Seg s;
-    s.q_start = hfield(hv, FL_WI_Q_START);
-    s.qo_len = hfield(hv, FL_WI_QO_LEN);
-    s.kv_len = hfield(hv, FL_WI_KV_LEN);
-    s.kv_head = hfield(hv, FL_WI_KV_HEAD);
-    s.row_begin = hfield(hv, FL_WI_ROW_BEGIN);
-    s.num_rows = hfield(hv, FL_WI_NUM_ROWS);
-    s.tok_begin = hfield(hv, FL_WI_TOK_BEGIN);
-    s.tok_end = hfield(hv, FL_WI_TOK_END);
-    s.part_row = hfield(hv, FL_WI_PART_ROW);
-    s.split = hfield(hv, FL_WI_SPLIT);
-    s.num_splits = hfield(hv, FL_WI_NUM_SPLITS);
-    s.merge = hfield(hv, FL_WI_MERGE);
-    s.pos_begin = hfield(hv, FL_WI_POS_BEGIN);
+    s.q_start = lds_int(h + 4 * FL_WI_Q_START);
+    s.qo_len = lds_int(h + 4 * FL_WI_QO_LEN);
+    s.kv_len = lds_int(h + 4 * FL_WI_KV_LEN);
+    s.kv_head = lds_int(h + 4 * FL_WI_KV_HEAD);
+    s.row_begin = lds_int(h + 4 * FL_WI_ROW_BEGIN);
+    s.num_rows = lds_int(h + 4 * FL_WI_NUM_ROWS);
+    s.tok_begin = lds_int(h + 4 * FL_WI_TOK_BEGIN);
+    s.tok_end = lds_int(h + 4 * FL_WI_TOK_END);
+    s.part_row = lds_int(h + 4 * FL_WI_PART_ROW);
+    s.split = lds_int(h + 4 * FL_WI_SPLIT);
+    s.num_splits = lds_int(h + 4 * FL_WI_NUM_SPLITS);
+    s.merge = lds_int(h + 4 * FL_WI_MERGE);
+    s.pos_begin = lds_int(h + 4 * FL_WI_POS_BEGIN);
     return s;
 }
 
@@ -253,8 +293,17 @@ __device__ __forceinline__ RowInfo row_info(const Seg &w, const AttnArgs &a, int
     return ri;
 }
 
-__device__ __forceinline__ int64_t q_row_offset(const Seg &w, const AttnArgs &a, const RowInfo &ri) {
-    return ((int64_t)(w.q_start + ri.qi) * a.num_qo_heads + w.kv_head * a.group + ri.qh);
+// Q rows of a block. Flattened row f = row_begin + r is query row f / G, head
+// kv_head * G + f % G. base: q row of the block's first query row and head kv_head * G;
+// the returned offset (in rows) of block row r from it is small (rows past num_rows use
+// row 0, whose data is never used).
+__device__ __forceinline__ int64_t q_block_base(const Seg &w, const AttnArgs &a) {
+    return ((int64_t)(w.q_start + w.row_begin / a.group) * a.num_qo_heads + w.kv_head * a.group);
+}
+__device__ __forceinline__ int q_block_row(const Seg &w, const AttnArgs &a, int r) {
+    const int f = w.row_begin + (r < w.num_rows ? r : 0);
+    const int qi = f / a.group;
+    return (qi - w.row_begin / a.group) * a.num_qo_heads + (f - qi * a.group);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -276,11 +325,50 @@ struct HalfTile {
         u32x2 ident;
     };
 
-    __device__ static QOp load_q(const AttnArgs &a, const Seg &w, const RowInfo &ri, int col, int grp) {
-        QOp op;
-        const uint16_t *qp = (const uint16_t *)a.q + q_row_offset(w, a, ri) * D + 8 * grp;
+    // ---- 16-byte pieces in LDS -------------------------------------------------------------
+    // A row of K, V or Q is S = D/8 pieces of 16 bytes. One 1 KB load writes LDS bytes
+    // [16l, 16l+16) from lane l, so lane l fetches whichever global piece belongs there:
+    // instruction c covers rows KPL*c .. KPL*c + KPL-1 in full (whole cache lines); lane l
+    // reads row KPL*c + l/S into position l % S, which holds piece (l % S) ^ swz(row). The
+    // MFMA operand reads take, for lane (row t, group g), piece 4c + g of row t from
+    // position (4c + g) ^ swz(t): over any 8 or 16 consecutive lanes (16 rows, one piece)
+    // the positions and row parities differ, so the 16-byte LDS reads do not collide on
+    // banks.
+    static constexpr int S = D / 8;
+    static constexpr int KPL = 64 / S;
+    static constexpr int kOpBytes = kTileTokens * 2 * D;  // 16 rows of K, V or Q
+    static constexpr int kSlotBytes = 2 * kOpBytes;        // K then V
+    static constexpr int kQBytes = kOpBytes;
+    static constexpr int kLoads = 2 * NC;                  // 1 KB loads per tile
+    static_assert(kOpBytes == NC * 1024, "one 1 KB load per 32 d of 16 rows");
+    template <int PF>
+    static constexpr int ring_bytes() { return PF * kSlotBytes; }
+
+    __device__ static __forceinline__ int swz(int row) {
+        return S == 16 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
+    }
+    // LDS byte offset of lane (row t, group g)'s operand piece c within 16 rows
+    __device__ static __forceinline__ uint32_t op_off(int c, int t, int g) {
+        return (uint32_t)(t * 2 * D + 16 * ((4 * c + g) ^ swz(t)));
+    }
+
+    // Q rows of block segment w into LDS (rows past num_rows repeat row 0)
+    __device__ static void q_stage(const lds_char *qb, const AttnArgs &a, const Seg &w, int lane) {
+        const char *base = (const char *)a.q + q_block_base(w, a) * (2 * D);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) op.q[c] = ri.ok ? ld_global<u32x4>(qp + 32 * c) : u32x4{0, 0, 0, 0};
+        for (int c = 0; c < NC; ++c) {
+            const int r = KPL * c + lane / S;
+            const int piece = (lane % S) ^ swz(r);
+            dma_b128(base, (uint32_t)(q_block_row(w, a, r) * 2 * D + 16 * piece), qb + 1024 * c);
+        }
+    }
+    __device__ static QOp q_fetch(const lds_char *qb, const RowInfo &ri, int col, int grp) {
+        QOp op;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)(qb + op_off(c, col, grp));
+            op.q[c] = ri.ok ? v : u32x4{0, 0, 0, 0};
+        }
         // identity operand: element e of lane l is 1 where 4*grp + e == col
         const uint32_t e0 = (4 * grp + 0 == col) ? H::kOne : 0u;
         const uint32_t e1 = (4 * grp + 1 == col) ? H::kOne : 0u;
@@ -290,18 +378,52 @@ struct HalfTile {
         return op;
     }
 
-    // row0: pool row of the tile's first key; consecutive keys are hkv rows apart.
-    __device__ static void load(Frag &f, const void *k, const void *v, int row0, int hkv, int col,
-                                int grp) {
-        const int64_t off = (int64_t)(row0 + col * hkv) * D + 8 * grp;
-        const uint16_t *kp = (const uint16_t *)k + off;
-        const uint16_t *vp = (const uint16_t *)v + off;
+    // ---- K/V ring: PF slots of one wave in LDS ---------------------------------------------
+    template <int PF>
+    struct Ring {
+        const lds_char *base;  // this wave's PF slots
+        uint32_t goff[NC];     // lane's byte offset in load c from the tile's first key row
+        uint32_t roff[NC];     // lane's LDS byte offset of operand piece c
+        Frag f;                // the tile being computed
+    };
+    template <int PF>
+    __device__ static void ring_init(Ring<PF> &r, const lds_char *base, int lane, int hkv) {
+        r.base = base;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            f.k[c] = ld_global<u32x4>(kp + 32 * c);
-            f.v[c] = ld_global<u32x4>(vp + 32 * c);
+            const int key = KPL * c + lane / S;
+            const int piece = (lane % S) ^ swz(key);
+            r.goff[c] = (uint32_t)(key * hkv * 2 * D + 16 * piece);
+            r.roff[c] = op_off(c, lane & 15, lane >> 4);
         }
     }
+    // row0: pool row of the tile's first key; consecutive keys are hkv rows apart.
+    template <int PF>
+    __device__ static void ring_issue(Ring<PF> &r, int slot, const void *k, const void *v, int row0) {
+        const int64_t rb = (int64_t)row0 * (2 * D);
+        const char *kp = (const char *)k + rb;
+        const char *vp = (const char *)v + rb;
+        const lds_char *dst = r.base + slot * kSlotBytes;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            dma_b128(kp, r.goff[c], dst + 1024 * c);
+            dma_b128(vp, r.goff[c], dst + kOpBytes + 1024 * c);
+        }
+    }
+    // LATER: tiles issued after this slot's tile that may still be in flight
+    template <int LATER, int PF>
+    __device__ static void ring_arrive(Ring<PF> &r, int slot) {
+        wait_vm<LATER * kLoads>();
+        const lds_char *src = r.base + slot * kSlotBytes;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            r.f.k[c] = *(const __attribute__((address_space(3))) u32x4 *)(src + r.roff[c]);
+            r.f.v[c] = *(const __attribute__((address_space(3))) u32x4 *)(src + kOpBytes + r.roff[c]);
+        }
+    }
+    template <int PF>
+    __device__ static const Frag &ring_frag(const Ring<PF> &r, int) { return r.f; }
+    __device__ static void ring_release() { wait_lds(); }
 
     __device__ static void compute(const Frag &f, const QOp &q, int t0, int col, int grp, int tok_end,
                                    int limit, float scale_log2, float &m_run, float &l_run, f32x4 *o) {
@@ -364,19 +486,58 @@ struct F32Tile {
         float q[NS];
     };
 
-    __device__ static QOp load_q(const AttnArgs &a, const Seg &w, const RowInfo &ri, int, int grp) {
+    // ---- Q rows through LDS (16 rows of 4D bytes, row-major) ------------------------------
+    static constexpr int P4 = D / 4;                      // 16-byte pieces per row
+    static constexpr int RPL = 64 / P4;                   // rows per 1 KB load
+    static constexpr int kQBytes = kBlockRows * 4 * D;
+    static constexpr int kLoads = D / 8;                  // 16-byte loads per lane per tile
+    __device__ static void q_stage(const lds_char *qb, const AttnArgs &a, const Seg &w, int lane) {
+        const char *base = (const char *)a.q + q_block_base(w, a) * (4 * D);
+#pragma unroll
+        for (int c = 0; c < kQBytes / 1024; ++c) {
+            const int r = RPL * c + lane / P4;
+            dma_b128(base, (uint32_t)(q_block_row(w, a, r) * 4 * D + 16 * (lane % P4)), qb + 1024 * c);
+        }
+    }
+    __device__ static QOp q_fetch(const lds_char *qb, const RowInfo &ri, int col, int grp) {
         QOp op;
-        const float *qp = (const float *)a.q + q_row_offset(w, a, ri) * D + grp * NS;
+        const lds_char *row = qb + col * 4 * D + grp * NS * 4;
 #pragma unroll
         for (int s4 = 0; s4 < NS; s4 += 4) {
-            const float4 v = ri.ok ? ld_global<float4>(qp + s4) : make_float4(0.f, 0.f, 0.f, 0.f);
-            op.q[s4] = v.x;
-            op.q[s4 + 1] = v.y;
-            op.q[s4 + 2] = v.z;
-            op.q[s4 + 3] = v.w;
+            const f32x4 v = *(const __attribute__((address_space(3))) f32x4 *)(row + 4 * s4);
+            op.q[s4] = ri.ok ? v[0] : 0.f;
+            op.q[s4 + 1] = ri.ok ? v[1] : 0.f;
+            op.q[s4 + 2] = ri.ok ? v[2] : 0.f;
+            op.q[s4 + 3] = ri.ok ? v[3] : 0.f;
         }
         return op;
     }
+
+    // ---- K/V ring: PF register slots per wave (the compiler tracks these loads) -----------
+    template <int PF>
+    static constexpr int ring_bytes() { return 0; }
+    template <int PF>
+    struct Ring {
+        Frag buf[PF];
+        int col, grp, hkv;
+    };
+    template <int PF>
+    __device__ static void ring_init(Ring<PF> &r, const lds_char *, int lane, int hkv) {
+        r.col = lane & 15;
+        r.grp = lane >> 4;
+        r.hkv = hkv;
+    }
+    template <int PF>
+    __device__ static void ring_issue(Ring<PF> &r, int slot, const void *k, const void *v, int row0) {
+        load(r.buf[slot], k, v, row0, r.hkv, r.col, r.grp);
+    }
+    template <int LATER, int PF>
+    __device__ static void ring_arrive(Ring<PF> &, int) {
+        wait_vm<LATER * kLoads>();
+    }
+    template <int PF>
+    __device__ static const Frag &ring_frag(const Ring<PF> &r, int slot) { return r.buf[slot]; }
+    __device__ static void ring_release() {}
 
     __device__ static void load(Frag &f, const void *k, const void *v, int row0, int hkv, int col,
                                 int grp) {
@@ -486,7 +647,7 @@ __device__ __forceinline__ void part_store1(__amdgpu_buffer_rsrc_t rs, int byte_
 }
 
 // ---------------------------------------------------------------------------------------
-// LDS for the per-segment fold: four wave states (8-wave groups fold pairwise first)
+// LDS for the per-segment fold: the four wave states
 // ---------------------------------------------------------------------------------------
 template <int D>
 struct Smem {
@@ -562,35 +723,10 @@ __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, con
     constexpr int EPT = D / TPR;
     l_run += shfl_xor(l_run, 16);
     l_run += shfl_xor(l_run, 32);
-    if constexpr (NW == 8) {
-        if (wave >= 4) {
-            T::to_smem(o, sm.o[wave - 4][col], grp);
-            if (grp == 0) {
-                sm.m[wave - 4][col] = m_run;
-                sm.l[wave - 4][col] = l_run;
-            }
-        }
-        __syncthreads();
-        if (wave < 4) {
-            f32x4 o2[NJ];
-            T::from_smem(o2, sm.o[wave][col], grp);
-            const float m2 = sm.m[wave][col], l2 = sm.l[wave][col];
-            const float M = fmaxf(m_run, m2);
-            const float a1 = M == kNegInf ? 0.f : fast_exp2(m_run - M);
-            const float a2 = M == kNegInf ? 0.f : fast_exp2(m2 - M);
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) o[j] = o[j] * a1 + o2[j] * a2;
-            l_run = l_run * a1 + l2 * a2;
-            m_run = M;
-        }
-        __syncthreads();
-    }
-    if (wave < 4) {
-        T::to_smem(o, sm.o[wave][col], grp);
-        if (grp == 0) {
-            sm.m[wave][col] = m_run;
-            sm.l[wave][col] = l_run;
-        }
+    T::to_smem(o, sm.o[wave][col], grp);
+    if (grp == 0) {
+        sm.m[wave][col] = m_run;
+        sm.l[wave][col] = l_run;
     }
     __syncthreads();
     const int r = threadIdx.x / TPR;
@@ -641,10 +777,11 @@ __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, con
     for (int j = 0; j < NJ; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Pool rows of this wave's steps win .. win+63 (lane i <- step win + i).
-__device__ __forceinline__ int load_step_rows(const int32_t *rows, int win, int lane, int nsteps) {
-    const int i = win + lane;
-    return i < nsteps ? rows[i] : 0;
+// Pool rows of 64 steps of this wave (win .. win+63; past the end: the last step's row)
+// into an LDS window of 256 bytes.
+__device__ __forceinline__ void stage_rows(const lds_char *dst, const int32_t *rows, int win, int nsteps,
+                                           int lane) {
+    dma_b32(rows, 4u * (uint32_t)min(win + lane, nsteps - 1), dst);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -652,7 +789,7 @@ __device__ __forceinline__ int load_step_rows(const int32_t *rows, int win, int 
 // ---------------------------------------------------------------------------------------
 template <class T, int DT, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
-    static_assert((NW == 4 || NW == 8) && NW <= kMaxWaves, "4 or 8 waves");
+    static_assert(NW == 4 && NW <= kMaxWaves, "four waves per workgroup");
     static_assert(REC_ROWS + kMaxWaves * kRingDepth <= REC_HEAD &&
                   REC_HEAD + FL_WORK_ITEM_INTS <= kRecInts, "record layout");
     constexpr int PF = kRingDepth;
@@ -660,39 +797,54 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     constexpr int TPR = NW * 64 / kBlockRows;  // fold: threads per row
     constexpr int EPT = D / TPR;               // fold: elements per thread
     static_assert(D % TPR == 0 && EPT % 2 == 0, "bad fold split");
+    constexpr int kLoads = T::kLoads;
+    static_assert(PF * kLoads < 64, "vmcnt range");
+    // Per-wave LDS: the K/V ring (16-bit types), the Q rows of the block being computed,
+    // a ring of four segment headers and two 64-step windows of pool rows.
+    constexpr int kRingB = T::template ring_bytes<PF>();
+    constexpr int kQB = T::kQBytes;
+    constexpr int kWaveB = kRingB + kQB + 4 * kHdrSlot + 2 * 256;
     __shared__ Smem<D> sm;
+    __shared__ __attribute__((aligned(16))) char wave_lds[NW * kWaveB];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int col = lane & 15;
     const int grp = lane >> 4;
-    // The workgroup record (scalar loads) gives the share, the first segment and every
-    // wave's first rows: the step rows, Q and the first K/V tiles all go out at once.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    // The workgroup record (scalar loads, all read before the first LDS load is issued)
+    // gives the share, the first segment and every wave's first pool rows.
     const int32_t *rec = a.wg_rec + (size_t)blockIdx.x * kRecInts;
     const int seg_b = rec[REC_SEG_BEGIN], seg_e = rec[REC_SEG_END];
     const int pos0 = rec[REC_POS];
-    const int nsteps = rec[REC_STEPS];  // steps per wave (multiple of PF)
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int32_t *rows = a.step_rows + pos0 + wv * nsteps;
-    int k = seg_b;
-    Seg cs = seg_fields_mem(rec + REC_HEAD);
+    const int nsteps = rec[REC_STEPS];  // steps per wave (a positive multiple of PF)
     int seg_end = rec[REC_FIRST_END];
-    int rows_cur = load_step_rows(rows, 0, lane, nsteps);
-    int rows_nxt = load_step_rows(rows, 64, lane, nsteps);
-    RowInfo ri = row_info(cs, a, col);
-    typename T::QOp qc = T::load_q(a, cs, ri, col, grp);
-    typename T::QOp qn = qc;
-    // the next two segment headers (clamped: always one load each, used only if they exist);
-    // issued ahead of the ring so that waiting for them never waits for a K/V tile
-    int hv1 = load_header(a.segs, min(seg_b + 1, seg_e - 1), lane);
-    int hv2 = load_header(a.segs, min(seg_b + 2, seg_e - 1), lane);
-    __builtin_amdgcn_sched_barrier(0);
-    typename T::Frag buf[PF];
+    int row_first[PF];
 #pragma unroll
-    for (int s = 0; s < PF; ++s) {
-        T::load(buf[s], a.k, a.v, rec[REC_ROWS + wv * PF + s], a.num_kv_heads, col, grp);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int s = 0; s < PF; ++s) row_first[s] = rec[REC_ROWS + wv * PF + s];
+    Seg cs = seg_fields_mem(rec + REC_HEAD);
+    int k = seg_b;
+    const int32_t *rows = a.step_rows + pos0 + wv * nsteps;
+    const lds_char *ring_b = (const lds_char *)wave_lds + wv * kWaveB;
+    const lds_char *q_b = ring_b + kRingB;
+    const lds_char *hdr_b = q_b + kQB;
+    const lds_char *rows_b = hdr_b + 4 * kHdrSlot;
+    auto hdr_slot = [&](int seg) { return hdr_b + kHdrSlot * ((seg - seg_b) & 3); };
+
+    // Q, the next two headers and the first row windows go out ahead of the ring, so
+    // that reading them never waits for a K/V tile.
+    T::q_stage(q_b, a, cs, lane);
+    stage_header(hdr_slot(seg_b + 1), a.segs, min(seg_b + 1, seg_e - 1), lane);
+    stage_header(hdr_slot(seg_b + 2), a.segs, min(seg_b + 2, seg_e - 1), lane);
+    stage_rows(rows_b, rows, 0, nsteps, lane);
+    stage_rows(rows_b + 256, rows, 64, nsteps, lane);
+    typename T::template Ring<PF> ring;
+    T::ring_init(ring, ring_b, lane, a.num_kv_heads);
+#pragma unroll
+    for (int s = 0; s < PF; ++s) T::ring_issue(ring, s, a.k, a.v, row_first[s]);
+    wait_vm<PF * kLoads>();  // everything but the ring
+    RowInfo ri = row_info(cs, a, col);
+    typename T::QOp qc = T::q_fetch(q_b, ri, col, grp);
     int ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
 
     float m_run = kNegInf, l_run = 0.f;
@@ -702,52 +854,65 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     int pend0 = -1, pend1 = -1;  // pieces whose merge ticket is still to be drawn
 
     // ---- the step stream: PF tiles of K and V in flight per wave -------------------------
-    // Every slot of the ring is always in flight (padding steps re-read a real tile and are
-    // never scored), so the outstanding-load count is the same on every path and each tile
-    // waits only for its own data.
-    int win_issue = 0;
-    auto issue = [&](typename T::Frag &f, int p) {  // p < nsteps
-        if ((p & ~63) != win_issue) {              // next 64-step window of pool rows
-            win_issue = p & ~63;
-            rows_cur = rows_nxt;
-            rows_nxt = load_step_rows(rows, win_issue + 64, lane, nsteps);
-        }
-        T::load(f, a.k, a.v, __builtin_amdgcn_readlane(rows_cur, p & 63), a.num_kv_heads, col, grp);
-    };
+    // Every slot of the ring is in flight until its step (padding steps re-read a real tile
+    // and are never scored). Loads complete in issue order, so at slot s at most PF - 1
+    // later tiles are outstanding behind it, and at a group's top everything issued before
+    // the previous group's refills has landed (headers, Q, row windows included).
+    int win = 0;  // window of the last refill
     // One group of PF steps. The last group issues no refills, so nothing is in flight when
     // the final fold starts.
     auto group = [&](int p0, auto refill) {
+        constexpr bool kRefill = decltype(refill)::value;
+        wait_vm<PF * kLoads>();
         if (p0 == seg_end) {  // the same step in every wave: segment k is done
             fold_segment<T, DT, D, NW>(sm, a, cs, k, m_run, l_run, o, pend0, pend1, wave, col, grp);
             ++k;
-            cs = seg_fields(hv1);
-            hv1 = hv2;
-            hv2 = load_header(a.segs, min(k + 2, seg_e - 1), lane);
+            cs = seg_fields_lds(hdr_slot(k));
+            seg_end = k + 1 < seg_e ? lds_int(hdr_slot(k + 1) + 4 * FL_WI_POS_BEGIN) : nsteps;
             ri = row_info(cs, a, col);
-            qc = qn;
-            seg_end = k + 1 < seg_e ? hfield(hv1, FL_WI_POS_BEGIN) : nsteps;
+            qc = T::q_fetch(q_b, ri, col, grp);
             ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
+            wait_lds();  // the slot of header k - 2 is free
+            stage_header(hdr_slot(k + 2), a.segs, min(k + 2, seg_e - 1), lane);
         }
         if (p0 + PF == seg_end && k + 1 < seg_e) {
-            // the last step group of segment k: Q of segment k + 1 goes out before the
-            // tiles of k + 1 this group issues, so it is complete before they are
-            const Seg ns = seg_fields(hv1);
-            qn = T::load_q(a, ns, row_info(ns, a, col), col, grp);
+            // the last group of segment k: the Q rows of segment k + 1 go out before this
+            // group's refills, so they have landed at the next group's top
+            const Seg ns = seg_fields_lds(hdr_slot(k + 1));
+            wait_lds();  // this wave's reads of the Q rows are done
+            T::q_stage(q_b, a, ns, lane);
         }
+        int nrow[PF];  // pool rows of this group's refills
+        if constexpr (kRefill) {
 #pragma unroll
-        for (int s = 0; s < PF; ++s) {
+            for (int s = 0; s < PF; ++s) {
+                const int q = p0 + PF + s;  // < nsteps
+                nrow[s] = lds_int(rows_b + 256 * ((q >> 6) & 1) + 4 * (q & 63));
+            }
+        }
+        static_for<0, PF>([&](auto si) {
+            constexpr int s = decltype(si)::value;
             const int p = p0 + s;
             const int j = (p - cs.pos_begin) * NW + wave;  // tile of the segment
+            T::template ring_arrive<kRefill ? PF - 1 : PF - 1 - s>(ring, s);
             if (j < ntile) {
                 const int t0 = cs.tok_begin + j * kTileTokens;
-                T::compute(buf[s], qc, t0, col, grp, cs.tok_end, ri.limit, a.scale_log2, m_run,
-                           l_run, o);
+                T::compute(T::ring_frag(ring, s), qc, t0, col, grp, cs.tok_end, ri.limit,
+                           a.scale_log2, m_run, l_run, o);
             }
-            if constexpr (decltype(refill)::value) issue(buf[s], min(p + PF, nsteps - 1));
+            if constexpr (kRefill) {
+                const int q = p + PF;
+                T::ring_release();
+                if ((q >> 6) != win) {  // first refill in window q/64: fetch the window after it
+                    win = q >> 6;
+                    stage_rows(rows_b + 256 * ((win + 1) & 1), rows, 64 * (win + 1), nsteps, lane);
+                }
+                T::ring_issue(ring, s, a.k, a.v, nrow[s]);
+            }
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     };
-    int p0 = 0;  // nsteps is a positive multiple of PF
+    int p0 = 0;
     for (; p0 + PF < nsteps; p0 += PF) group(p0, std::true_type{});
     group(p0, std::false_type{});
     fold_segment<T, DT, D, NW>(sm, a, cs, k, m_run, l_run, o, pend0, pend1, wave, col, grp);
@@ -782,7 +947,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             if (pend[i] < 0 || !sm.last[i]) continue;
-            const Seg ps = seg_fields(load_header(a.segs, pend[i], lane));
+            const Seg ps = seg_fields_mem(a.segs + (size_t)pend[i] * FL_WORK_ITEM_INTS);
             if (r < ps.num_rows) merge_pieces<DT, D, TPR>(ps, a, r, c0);
         }
     }
@@ -806,7 +971,7 @@ hipError_t launch_t(int n, const AttnArgs &a, hipStream_t s) {  // n: workgroups
 
 template <int DT, int D>
 hipError_t launch_w(int waves, int n, const AttnArgs &a, hipStream_t s) {
-    return waves == 8 ? launch_t<DT, D, 8>(n, a, s) : launch_t<DT, D, 4>(n, a, s);
+    return waves == 4 ? launch_t<DT, D, 4>(n, a, s) : hipErrorInvalidValue;
 }
 
 }  // namespace
