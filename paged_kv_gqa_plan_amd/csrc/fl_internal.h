@@ -26,7 +26,7 @@ constexpr int kRingDepth = FL_RING_DEPTH;
 // end step, and the pool rows of every wave's first kRingDepth steps, so every load a
 // workgroup issues first (Q, K/V, step rows) depends on this record alone.
 constexpr int kRecInts = 64;
-constexpr int kMaxWaves = 8;
+constexpr int kMaxWaves = 4;
 enum {
     REC_SEG_BEGIN = 0, REC_SEG_END = 1, REC_POS = 2, REC_STEPS = 3, REC_FIRST_END = 4,
     REC_ROWS = 8,    // kMaxWaves * kRingDepth entries
