@@ -189,7 +189,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="saturated_decode", choices=sorted(LAYERS))
     ap.add_argument("--layers", type=int, default=0, help="per-layer pools (0: 24 or 28 by workload)")
     ap.add_argument("--seed", type=int, default=0)

@@ -56,6 +56,7 @@ struct fl_paged_attn {
 
     // pinned staging, double-buffered
     char *h_stage[2] = {nullptr, nullptr};
+    char *d_stage[2] = {nullptr, nullptr};   // the same buffers as the device addresses them
     hipEvent_t ev[2] = {nullptr, nullptr};
     bool ev_live[2] = {false, false};
     int cur = 0;
@@ -195,8 +196,17 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
             release(h);
             return hip_err(e, "hipMalloc (handle buffers)");
         }
+        // merge tickets start at zero once; runs keep them there
+        if ((e = hipMemset(h->d_meta + h->off_tickets, 0, (size_t)(h->off_steps - h->off_tickets))) !=
+                hipSuccess ||
+            (e = hipStreamSynchronize(nullptr)) != hipSuccess) {
+            release(h);
+            return hip_err(e, "hipMemset (merge tickets)");
+        }
         for (int i = 0; i < 2; ++i) {
             if ((e = hipHostMalloc((void **)&h->h_stage[i], h->meta_bytes, hipHostMallocDefault)) !=
+                    hipSuccess ||
+                (e = hipHostGetDevicePointer((void **)&h->d_stage[i], h->h_stage[i], 0)) !=
                     hipSuccess ||
                 (e = hipEventCreateWithFlags(&h->ev[i], hipEventDisableTiming)) != hipSuccess) {
                 release(h);
@@ -244,17 +254,20 @@ fl_status fl_paged_attn_plan(fl_handle h, int32_t batch, const int32_t *qo_indpt
         }
         char *st_buf = h->h_stage[slot];
         const Plan &p = h->plan;
+        // The used part of each region goes over, read by one small kernel straight from
+        // the pinned staging buffer. The merge tickets are not copied: they are zeroed at
+        // create and every run leaves them at zero (the piece that merges a row block
+        // resets its ticket).
         std::memcpy(st_buf, p.segs.data(), p.segs.size() * 4);
         std::memcpy(st_buf + h->off_wg_rec, p.wg_rec.data(), p.wg_rec.size() * 4);
-        // merge tickets start at zero for every plan (the kernel keeps them at zero between
-        // runs: the piece that merges a row block resets its ticket)
-        std::memset(st_buf + h->off_tickets, 0, (size_t)p.num_merges * 4);
         std::memcpy(st_buf + h->off_steps, p.step_rows.data(), p.step_rows.size() * 4);
-        // one transfer covers [segments .. end of the step rows]
-        const int64_t bytes = h->off_steps + (int64_t)p.step_rows.size() * 4;
+        fl::StageCopy sc{h->d_stage[slot], h->d_meta,
+                         {0, h->off_wg_rec, h->off_steps},
+                         {(int64_t)p.segs.size() * 4, (int64_t)p.wg_rec.size() * 4,
+                          (int64_t)p.step_rows.size() * 4}};
         hipStream_t s = (hipStream_t)stream;
-        if ((e = hipMemcpyAsync(h->d_meta, st_buf, bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
-            return hip_err(e, "hipMemcpyAsync (plan)");
+        if ((e = (hipError_t)fl::launch_stage_copy(sc, s)) != hipSuccess)
+            return hip_err(e, "plan metadata copy");
         if ((e = hipEventRecord(h->ev[slot], s)) != hipSuccess)
             return hip_err(e, "hipEventRecord (plan)");
         h->ev_live[slot] = true;

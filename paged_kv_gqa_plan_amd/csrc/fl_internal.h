@@ -104,4 +104,14 @@ struct AttnArgs {
 int launch_attention(int dtype, int head_dim, int waves, int num_groups, const AttnArgs &a,
                      void *stream);
 
+// Copy byte ranges [off, off + bytes) from pinned host memory to the same offsets of a
+// device buffer with one kernel (offsets 16-byte aligned, sizes multiples of 4).
+constexpr int kStageParts = 3;
+struct StageCopy {
+    const char *src;   // pinned host memory, device-accessible
+    char *dst;         // device memory
+    int64_t off[kStageParts], bytes[kStageParts];
+};
+int launch_stage_copy(const StageCopy &c, void *stream);
+
 }  // namespace fl
