@@ -427,6 +427,10 @@ struct HalfTile {
     template <int PF>
     __device__ static const Frag &ring_frag(const Ring<PF> &r, int) { return r.f; }
     __device__ static void ring_release() { wait_lds(); }
+    // Refill a slot before its tile's arithmetic (the slot is free once the tile is in
+    // registers) where the arithmetic is long enough to hide the wait for the LDS reads:
+    // measured faster at head_dim 128, slower at 64.
+    static constexpr bool kEarlyRefill = D >= 128;
 
     __device__ static void compute(const Frag &f, const QOp &q, int t0, int col, int grp, int tok_end,
                                    int limit, float scale_log2, float &m_run, float &l_run, f32x4 *o) {
@@ -541,6 +545,7 @@ struct F32Tile {
     template <int PF>
     __device__ static const Frag &ring_frag(const Ring<PF> &r, int slot) { return r.buf[slot]; }
     __device__ static void ring_release() {}
+    static constexpr bool kEarlyRefill = false;
 
     __device__ static void load(Frag &f, const void *k, const void *v, int row0, int hkv, int col,
                                 int grp) {
@@ -898,20 +903,27 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
             const int p = p0 + s;
             const int j = (p - cs.pos_begin) * NW + wave;  // tile of the segment
             T::template ring_arrive<kRefill ? PF - 1 : PF - 1 - s>(ring, s);
+            auto refill = [&] {
+                if constexpr (kRefill) {
+                    const int q = p + PF;
+                    T::ring_release();
+                    if ((q >> 6) != win) {  // first refill in window q/64: fetch the next window
+                        win = q >> 6;
+                        stage_rows(rows_b + 256 * ((win + 1) & 1), rows, 64 * (win + 1), nsteps, lane);
+                    }
+                    T::ring_issue(ring, s, a.k, a.v, nrow[s]);
+                }
+            };
+            // An LDS slot is free once its tile is in registers: refill it before computing,
+            // so the load's latency runs under the arithmetic. A register slot is free only
+            // after the arithmetic.
+            if constexpr (T::kEarlyRefill) refill();
             if (j < ntile) {
                 const int t0 = cs.tok_begin + j * kTileTokens;
                 T::compute(T::ring_frag(ring, s), qc, t0, col, grp, cs.tok_end, ri.limit,
                            a.scale_log2, m_run, l_run, o);
             }
-            if constexpr (kRefill) {
-                const int q = p + PF;
-                T::ring_release();
-                if ((q >> 6) != win) {  // first refill in window q/64: fetch the window after it
-                    win = q >> 6;
-                    stage_rows(rows_b + 256 * ((win + 1) & 1), rows, 64 * (win + 1), nsteps, lane);
-                }
-                T::ring_issue(ring, s, a.k, a.v, nrow[s]);
-            }
+            if constexpr (!T::kEarlyRefill) refill();
             __builtin_amdgcn_sched_barrier(0);
         });
     };
