@@ -22,6 +22,9 @@ constexpr int kBlockRows = 16;
 #define FL_RING_DEPTH 2
 #endif
 constexpr int kRingDepth = FL_RING_DEPTH;
+// Planner's estimate of one segment fold (the cross-wave merge of the softmax states at a
+// segment's end) in units of tiles: measured at about 1.5 ring steps of a 4-wave group.
+constexpr int kFoldCostTiles = 6;
 // Per-workgroup record (int32): segment range, step range, the first segment's header and
 // end step, and the pool rows of every wave's first kRingDepth steps, so every load a
 // workgroup issues first (Q, K/V, step rows) depends on this record alone.

@@ -159,21 +159,51 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
                 pieces.push_back({b, j * per, std::min<int64_t>((j + 1) * per, tiles[b]), G_wg++});
         }
     } else {
-        // equal contiguous shares of the tile sequence
+        // Contiguous shares of the tile sequence with equal estimated time. A piece of n tiles
+        // costs the ring steps it occupies in all waves (n rounded up to whole step groups)
+        // plus a fixed charge for its fold; a block cut inside a share is cut at a multiple
+        // of a step group, so only a block's last piece carries padding. The smallest
+        // per-share budget that needs at most G shares is found by bisection.
         const int64_t want = (int64_t)lim.num_cus * lim.groups_per_cu;
-        G_wg = std::max<int64_t>(1, std::min(want, ceil_div(T, lim.min_group_tiles)));
-        G_wg = std::min(G_wg, T);
-        int64_t b = 0;
-        for (int64_t g = 0; g < G_wg; ++g) {
-            const int64_t a0 = T * g / G_wg, a1 = T * (g + 1) / G_wg;
-            int64_t pos = a0;
-            while (pos < a1) {
-                while (first_tile[b + 1] <= pos) ++b;
-                const int64_t hi = std::min(a1, first_tile[b + 1]);
-                pieces.push_back({b, pos - first_tile[b], hi - first_tile[b], g});
-                pos = hi;
+        const int64_t G_max = std::min(std::max<int64_t>(1, std::min(want, ceil_div(T, lim.min_group_tiles))), T);
+        const int64_t U = (int64_t)lim.waves * kRingDepth;
+        auto cost = [&](int64_t n) { return U * ceil_div(n, U) + kFoldCostTiles; };
+        // walk the blocks filling shares of budget C; emit pieces when `out` is set
+        auto fill = [&](int64_t C, bool out) {
+            int64_t shares = 0, b = 0, pos = 0;
+            while (b < nblocks) {
+                int64_t budget = C;
+                while (b < nblocks) {
+                    const int64_t r = tiles[b] - pos;
+                    if (cost(r) <= budget) {
+                        if (out) pieces.push_back({b, pos, tiles[b], shares});
+                        budget -= cost(r);
+                        ++b;
+                        pos = 0;
+                        continue;
+                    }
+                    const int64_t n = budget >= kFoldCostTiles + U ? U * ((budget - kFoldCostTiles) / U) : 0;
+                    if (n > 0) {
+                        if (out) pieces.push_back({b, pos, pos + n, shares});
+                        pos += n;
+                    }
+                    break;
+                }
+                ++shares;
             }
+            return shares;
+        };
+        int64_t total = 0;
+        for (int64_t b = 0; b < nblocks; ++b) total += cost(tiles[b]);
+        int64_t lo = std::max<int64_t>(kFoldCostTiles + U, ceil_div(total, G_max)), hi = total;
+        while (lo < hi) {  // every budget >= kFoldCostTiles + U makes progress
+            const int64_t mid = lo + (hi - lo) / 2;
+            if (fill(mid, false) <= G_max)
+                hi = mid;
+            else
+                lo = mid + 1;
         }
+        G_wg = fill(lo, true);
     }
     if ((int64_t)pieces.size() > lim.seg_cap || G_wg > lim.group_cap)
         return fail(err, FL_ERR_CAPACITY, "%lld work items / %lld workgroups exceed the handle's "

@@ -138,7 +138,21 @@ def tiles_per_group(items):
     return np.bincount(g, weights=t).astype(int)
 
 
-def test_long_histories_are_spread_and_shares_are_equal():
+STEP_GROUP = 8        # tiles of one ring step group of a 4-wave workgroup (4 waves x 2)
+FOLD_COST = 6         # the planner's charge for one segment fold, in tiles
+
+
+def cost_per_group(items):
+    """The planner's time estimate per workgroup: each piece's tiles rounded up to whole step
+    groups, plus one fold charge per piece."""
+    idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
+    g = items[:, idx["group"]]
+    t = -(-(items[:, idx["tok_end"]] - items[:, idx["tok_begin"]]) // 16)
+    c = STEP_GROUP * -(-t // STEP_GROUP) + FOLD_COST
+    return np.bincount(g, weights=c).astype(int)
+
+
+def test_long_histories_are_spread_and_shares_are_balanced():
     lens = W.long_context_lengths(0)
     b = W.make_batch(lens, num_qo_heads=12, num_kv_heads=2, head_dim=64, page_size=256,
                      dtype="f16", num_pages=1200, poison=False)
@@ -151,7 +165,16 @@ def test_long_histories_are_spread_and_shares_are_equal():
     assert ns[kvl == 512].max() <= 2            # short ones stay (nearly) whole
     tpg = tiles_per_group(items)
     assert len(tpg) == 256                      # one share per compute unit
-    assert tpg.max() - tpg.min() <= 1           # equal shares
+    assert tpg.sum() == -(-b.kv_lens // 16).sum() * 2
+    # equal estimated time: no share above the ideal average of whole blocks by more than
+    # one step group and one fold
+    whole = (STEP_GROUP * -(-(-(-b.kv_lens // 16)) // STEP_GROUP) + FOLD_COST).sum() * 2
+    cpg = cost_per_group(items)
+    assert cpg.max() <= -(-whole // 256) + STEP_GROUP + FOLD_COST
+    # a block is cut only at multiples of a step group (its last piece takes the rest)
+    t = -(-(items[:, idx["tok_end"]] - items[:, idx["tok_begin"]]) // 16)
+    not_last = items[:, idx["tok_end"]] < items[:, idx["kv_len"]]
+    assert (t[not_last] % STEP_GROUP == 0).all()
     # a share cuts at most its first and last segment out of a longer row block
     g = items[:, idx["group"]]
     for gg in range(256):
