@@ -62,7 +62,26 @@ constexpr float kLn2 = 0.69314718055994530942f;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+// Reductions across the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48) with the
+// gfx950 lane-swap instructions: a swap of x with itself leaves, in the two results, x of
+// lane l and of lane l^16 (or l^32) in some order, so max and + of the pair are the same in
+// both lanes of it (bit-identical: both operations are commutative).
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // ---------------------------------------------------------------------------------------
 // 16-bit element types
@@ -263,8 +282,7 @@ __device__ __forceinline__ void softmax_tile(const f32x4 &s, int t0, int grp, in
         sv[e] = ok ? s[e] * scale_log2 : kNegInf;
         mt = fmaxf(mt, sv[e]);
     }
-    mt = fmaxf(mt, shfl_xor(mt, 16));
-    mt = fmaxf(mt, shfl_xor(mt, 32));
+    mt = max_xor32(max_xor16(mt));
     const bool move = mt > m_run + kSlack;  // false while both are -inf
     const float m_new = move ? mt : m_run;
     rescaled = __builtin_amdgcn_ballot_w64(move) != 0;
@@ -321,11 +339,11 @@ struct HalfTile {
     static constexpr int NC = D / 32;
     static constexpr int NJ = D / 16;
     struct Frag {
-        u32x4 k[NC], v[NC];
+        u32x4 k[NC];   // K piece c of this lane's key
+        u32x2 vt[NJ];  // V of keys 4grp .. 4grp+3 at this lane's output column of block j
     };
     struct QOp {
         u32x4 q[NC];
-        u32x2 ident;
     };
 
     // ---- 16-byte pieces in LDS -------------------------------------------------------------
@@ -354,6 +372,16 @@ struct HalfTile {
     __device__ static __forceinline__ uint32_t op_off(int c, int t, int g) {
         return (uint32_t)(t * 2 * D + 16 * ((4 * c + g) ^ swz(t)));
     }
+    // V for PV block j through the 16-bit transpose read: lane (i, g) of a 16-lane group
+    // receives element i % 4 of the 8 bytes read by lane 16g + 4e + i/4, for e = 0..3. So
+    // lane 16g + 4e + q reads key 4g + e at columns 32(j/2) + 8q + 4(j%2) .. +3, and lane
+    // (i, g) ends up with V[4g + e][32(j/2) + 8(i/4) + 4(j%2) + i%4], e = 0..3: the A operand
+    // of PV (output column of block j for element i, keys of the lane's B-operand group).
+    __device__ static __forceinline__ uint32_t vt_off(int j, int lane) {
+        const int t = 4 * (lane >> 4) + ((lane >> 2) & 3);
+        const int piece = 4 * (j >> 1) + (lane & 3);
+        return (uint32_t)(t * 2 * D + 16 * (piece ^ swz(t)) + 8 * (j & 1));
+    }
 
     // Q rows of block segment w into LDS (rows past num_rows repeat row 0)
     __device__ static void q_stage(const lds_char *qb, const AttnArgs &a, const Seg &w, int lane) {
@@ -372,12 +400,6 @@ struct HalfTile {
             const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)(qb + op_off(c, col, grp));
             op.q[c] = ri.ok ? v : u32x4{0, 0, 0, 0};
         }
-        // identity operand: element e of lane l is 1 where 4*grp + e == col
-        const uint32_t e0 = (4 * grp + 0 == col) ? H::kOne : 0u;
-        const uint32_t e1 = (4 * grp + 1 == col) ? H::kOne : 0u;
-        const uint32_t e2 = (4 * grp + 2 == col) ? H::kOne : 0u;
-        const uint32_t e3 = (4 * grp + 3 == col) ? H::kOne : 0u;
-        op.ident = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
         return op;
     }
 
@@ -387,6 +409,7 @@ struct HalfTile {
         const lds_char *base;  // this wave's PF slots
         uint32_t goff[NC];     // lane's byte offset in load c from the tile's first key row
         uint32_t roff[NC];     // lane's LDS byte offset of operand piece c
+        uint32_t toff[NJ];     // lane's LDS byte offset of its transpose read for PV block j
         Frag f;                // the tile being computed
     };
     template <int PF>
@@ -399,6 +422,8 @@ struct HalfTile {
             r.goff[c] = (uint32_t)(key * hkv * 2 * D + 16 * piece);
             r.roff[c] = op_off(c, lane & 15, lane >> 4);
         }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) r.toff[j] = kOpBytes + vt_off(j, lane);
     }
     // row0: pool row of the tile's first key; consecutive keys are hkv rows apart.
     template <int PF>
@@ -419,10 +444,13 @@ struct HalfTile {
         wait_vm<LATER * kLoads>();
         const lds_char *src = r.base + slot * kSlotBytes;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
+        for (int c = 0; c < NC; ++c)
             r.f.k[c] = *(const __attribute__((address_space(3))) u32x4 *)(src + r.roff[c]);
-            r.f.v[c] = *(const __attribute__((address_space(3))) u32x4 *)(src + kOpBytes + r.roff[c]);
-        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            r.f.vt[j] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (__attribute__((address_space(3))) s16x4 *)(src + r.toff[j])));
     }
     template <int PF>
     __device__ static const Frag &ring_frag(const Ring<PF> &r, int) { return r.f; }
@@ -451,14 +479,17 @@ struct HalfTile {
         const uint32_t l01 = H::pack(p[0] - H::lo_f(h01), p[1] - H::hi_f(h01));
         const uint32_t l23 = H::pack(p[2] - H::lo_f(h23), p[3] - H::hi_f(h23));
         const u32x4 pk = {h01, h23, l01, l23};
-        const bool kv_ok = t0 + col < tok_end;  // this lane's V row is a real key
+        // keys at or past tok_end may hold anything (NaN included): their V becomes 0
+        u32x2 vmask = {~0u, ~0u};
+        if (t0 + kTileTokens > tok_end) {
+            const int k0 = t0 + 4 * grp;
+            vmask = u32x2{(k0 < tok_end ? 0xFFFFu : 0u) | (k0 + 1 < tok_end ? 0xFFFF0000u : 0u),
+                          (k0 + 2 < tok_end ? 0xFFFFu : 0u) | (k0 + 3 < tok_end ? 0xFFFF0000u : 0u)};
+        }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const u32x4 ch = kv_ok ? f.v[j >> 1] : u32x4{0, 0, 0, 0};
-            const u32x2 va = (j & 1) ? u32x2{ch[2], ch[3]} : u32x2{ch[0], ch[1]};
-            const f32x4 vt = H::mma_k16(va, q.ident, f32x4{0.f, 0.f, 0.f, 0.f});
-            const uint32_t v01 = H::pack(vt[0], vt[1]), v23 = H::pack(vt[2], vt[3]);
-            o[j] = H::mma_k32(u32x4{v01, v23, v01, v23}, pk, o[j]);
+            const u32x2 va = f.vt[j] & vmask;
+            o[j] = H::mma_k32(u32x4{va[0], va[1], va[0], va[1]}, pk, o[j]);
         }
     }
 
@@ -729,8 +760,7 @@ __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, con
     constexpr int NJ = D / 16;
     constexpr int TPR = NW * 64 / kBlockRows;
     constexpr int EPT = D / TPR;
-    l_run += shfl_xor(l_run, 16);
-    l_run += shfl_xor(l_run, 32);
+    l_run = sum_xor32(sum_xor16(l_run));
     T::to_smem(o, sm.o[wave][col], grp);
     if (grp == 0) {
         sm.m[wave][col] = m_run;
