@@ -269,18 +269,28 @@ __device__ __forceinline__ void store_out(void *out, int64_t idx, const float *r
 // value gives the same result once the final sum divides it out.
 constexpr float kSlack = 8.f;
 
+// full: every key of the tile is below tok_end and visible to every real row of the block
+// (rows past the block's end see garbage-free zeros and are never stored), so no mask.
 __device__ __forceinline__ void softmax_tile(const f32x4 &s, int t0, int grp, int tok_end,
-                                             int limit, float scale_log2, float &m_run,
+                                             int limit, bool full, float scale_log2, float &m_run,
                                              float &l_run, float p[4], float &alpha,
                                              bool &rescaled) {
     float sv[4];
     float mt = kNegInf;
+    if (full) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int t = t0 + 4 * grp + e;
-        const bool ok = (t < tok_end) && (t <= limit);
-        sv[e] = ok ? s[e] * scale_log2 : kNegInf;
-        mt = fmaxf(mt, sv[e]);
+        for (int e = 0; e < 4; ++e) {
+            sv[e] = s[e] * scale_log2;
+            mt = fmaxf(mt, sv[e]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = t0 + 4 * grp + e;
+            const bool ok = (t < tok_end) && (t <= limit);
+            sv[e] = ok ? s[e] * scale_log2 : kNegInf;
+            mt = fmaxf(mt, sv[e]);
+        }
     }
     mt = max_xor32(max_xor16(mt));
     const bool move = mt > m_run + kSlack;  // false while both are -inf
@@ -303,6 +313,13 @@ struct RowInfo {
     int qi, qh, limit;
     bool ok;
 };
+
+// End of the keys every real row of the segment's block may see (the first row has the
+// tightest causal limit): tiles wholly below it need no mask.
+__device__ __forceinline__ int seg_full_end(const Seg &w, const AttnArgs &a) {
+    const int first_limit = a.causal ? w.kv_len - w.qo_len + w.row_begin / a.group : w.kv_len - 1;
+    return min(w.tok_end, first_limit + 1);
+}
 
 __device__ __forceinline__ RowInfo row_info(const Seg &w, const AttnArgs &a, int col) {
     RowInfo ri;
@@ -461,13 +478,14 @@ struct HalfTile {
     static constexpr bool kEarlyRefill = D >= 128;
 
     __device__ static void compute(const Frag &f, const QOp &q, int t0, int col, int grp, int tok_end,
-                                   int limit, float scale_log2, float &m_run, float &l_run, f32x4 *o) {
+                                   int limit, bool full, float scale_log2, float &m_run, float &l_run,
+                                   f32x4 *o) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NC; ++c) s = H::mma_k32(f.k[c], q.q[c], s);
         float p[4], alpha;
         bool rescaled;
-        softmax_tile(s, t0, grp, tok_end, limit, scale_log2, m_run, l_run, p, alpha, rescaled);
+        softmax_tile(s, t0, grp, tok_end, limit, full, scale_log2, m_run, l_run, p, alpha, rescaled);
         if (rescaled) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) o[j] = o[j] * alpha;
@@ -592,7 +610,8 @@ struct F32Tile {
     }
 
     __device__ static void compute(const Frag &f, const QOp &q, int t0, int, int grp, int tok_end,
-                                   int limit, float scale_log2, float &m_run, float &l_run, f32x4 *o) {
+                                   int limit, bool full, float scale_log2, float &m_run, float &l_run,
+                                   f32x4 *o) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NS / 4; ++c) {
@@ -603,7 +622,7 @@ struct F32Tile {
         }
         float p[4], alpha;
         bool rescaled;
-        softmax_tile(s, t0, grp, tok_end, limit, scale_log2, m_run, l_run, p, alpha, rescaled);
+        softmax_tile(s, t0, grp, tok_end, limit, full, scale_log2, m_run, l_run, p, alpha, rescaled);
         if (rescaled) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) o[j] = o[j] * alpha;
@@ -884,6 +903,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     RowInfo ri = row_info(cs, a, col);
     typename T::QOp qc = T::q_fetch(q_b, ri, col, grp);
     int ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
+    int full_end = seg_full_end(cs, a);
 
     float m_run = kNegInf, l_run = 0.f;
     f32x4 o[NJ];
@@ -910,6 +930,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
             ri = row_info(cs, a, col);
             qc = T::q_fetch(q_b, ri, col, grp);
             ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
+            full_end = seg_full_end(cs, a);
             wait_lds();  // the slot of header k - 2 is free
             stage_header(hdr_slot(k + 2), a.segs, min(k + 2, seg_e - 1), lane);
         }
@@ -951,7 +972,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
             if (j < ntile) {
                 const int t0 = cs.tok_begin + j * kTileTokens;
                 T::compute(T::ring_frag(ring, s), qc, t0, col, grp, cs.tok_end, ri.limit,
-                           a.scale_log2, m_run, l_run, o);
+                           t0 + kTileTokens <= full_end, a.scale_log2, m_run, l_run, o);
             }
             if constexpr (!T::kEarlyRefill) refill();
             __builtin_amdgcn_sched_barrier(0);
