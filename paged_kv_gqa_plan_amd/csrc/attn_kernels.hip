@@ -66,13 +66,20 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // gfx950 lane-swap instructions: a swap of x with itself leaves, in the two results, x of
 // lane l and of lane l^16 (or l^32) in some order, so max and + of the pair are the same in
 // both lanes of it (bit-identical: both operations are commutative).
+// max of two values that are never NaN (scores are finite or -inf): one instruction, with
+// none of the quieting that fmaxf adds for operands of unknown origin
+__device__ __forceinline__ float max_nonan(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 __device__ __forceinline__ float max_xor16(float x) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max_nonan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_xor32(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max_nonan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_xor16(float x) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -498,17 +505,18 @@ struct HalfTile {
         const uint32_t l23 = H::pack(p[2] - H::lo_f(h23), p[3] - H::hi_f(h23));
         const u32x4 pk = {h01, h23, l01, l23};
         // keys at or past tok_end may hold anything (NaN included): their V becomes 0
-        u32x2 vmask = {~0u, ~0u};
+        u32x2 vt[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) vt[j] = f.vt[j];
         if (t0 + kTileTokens > tok_end) {
             const int k0 = t0 + 4 * grp;
-            vmask = u32x2{(k0 < tok_end ? 0xFFFFu : 0u) | (k0 + 1 < tok_end ? 0xFFFF0000u : 0u),
-                          (k0 + 2 < tok_end ? 0xFFFFu : 0u) | (k0 + 3 < tok_end ? 0xFFFF0000u : 0u)};
+            const u32x2 vmask = {(k0 < tok_end ? 0xFFFFu : 0u) | (k0 + 1 < tok_end ? 0xFFFF0000u : 0u),
+                                 (k0 + 2 < tok_end ? 0xFFFFu : 0u) | (k0 + 3 < tok_end ? 0xFFFF0000u : 0u)};
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) vt[j] &= vmask;
         }
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const u32x2 va = f.vt[j] & vmask;
-            o[j] = H::mma_k32(u32x4{va[0], va[1], va[0], va[1]}, pk, o[j]);
-        }
+        for (int j = 0; j < NJ; ++j) o[j] = H::mma_k32(u32x4{vt[j][0], vt[j][1], vt[j][0], vt[j][1]}, pk, o[j]);
     }
 
     // accumulator element (block j, element e) of lane (col, grp) -> output column d
@@ -952,7 +960,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
         static_for<0, PF>([&](auto si) {
             constexpr int s = decltype(si)::value;
             const int p = p0 + s;
-            const int j = (p - cs.pos_begin) * NW + wave;  // tile of the segment
+            const int j = (p - cs.pos_begin) * NW + wv;  // tile of the segment (wave-uniform)
             T::template ring_arrive<kRefill ? PF - 1 : PF - 1 - s>(ring, s);
             auto refill = [&] {
                 if constexpr (kRefill) {
