@@ -81,7 +81,8 @@ typedef struct {
     int32_t num_cus;           /* compute units to plan for; 0 = ask the device
                                   (a host-only handle then plans for 256)                */
     int32_t groups_per_cu;     /* workgroups per compute unit the plan spreads work over;
-                                  0 = library default (1)                                */
+                                  0 = chosen per step (2 when the step has prefill rows
+                                  at head_dim 64 in a 16-bit type, else 1)               */
     int32_t min_group_tokens;  /* fewest keys (per row block piece) a workgroup's share
                                   may hold before fewer workgroups are used; 0 = default */
     int32_t waves_per_group;   /* wavefronts per workgroup: 4 (0 = the same)              */

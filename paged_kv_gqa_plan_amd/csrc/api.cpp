@@ -158,16 +158,17 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
     L.num_kv_heads = cfg->num_kv_heads;
     L.head_dim = cfg->head_dim;
     L.page_size = cfg->page_size;
+    L.dtype = cfg->dtype;
     L.max_batch = cfg->max_batch;
     L.max_qo_rows = cfg->max_qo_rows;
     L.max_kv_pages = cfg->max_kv_pages;
     L.num_cus = num_cus;
-    L.groups_per_cu = cfg->groups_per_cu > 0 ? cfg->groups_per_cu : 1;
+    L.groups_per_cu = cfg->groups_per_cu;  // 0: the plan picks per step
     L.waves = h->waves;
     L.min_group_tiles =
         cfg->min_group_tokens > 0 ? (int32_t)((cfg->min_group_tokens + 15) / 16) : 8;
     const int64_t blocks = fl::row_block_bound(L);
-    L.group_cap = std::max<int64_t>((int64_t)num_cus * L.groups_per_cu, 16384);
+    L.group_cap = std::max<int64_t>((int64_t)num_cus * std::max(L.groups_per_cu, 2), 16384);
     L.seg_cap = blocks + L.group_cap;
     // steps: every row block may read at most all of the plan's pages; each work item adds
     // at most one ring group of padding per wave

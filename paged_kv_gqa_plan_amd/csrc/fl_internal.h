@@ -38,10 +38,11 @@ enum {
 
 struct PlanLimits {
     int32_t num_qo_heads, num_kv_heads, head_dim, page_size;
+    int32_t dtype;
     int32_t max_batch, max_qo_rows;
     int64_t max_kv_pages;
     int32_t num_cus;
-    int32_t groups_per_cu;        // resolved (> 0)
+    int32_t groups_per_cu;        // > 0, or 0: per step (see build_plan)
     int32_t waves;                // wavefronts per workgroup
     int32_t min_group_tiles;      // resolved (> 0)
     int64_t max_tiles;            // per-wave steps (x waves) one plan may hold

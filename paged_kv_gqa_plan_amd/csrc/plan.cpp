@@ -164,7 +164,19 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         // plus a fixed charge for its fold; a block cut inside a share is cut at a multiple
         // of a step group, so only a block's last piece carries padding. The smallest
         // per-share budget that needs at most G shares is found by bisection.
-        const int64_t want = (int64_t)lim.num_cus * lim.groups_per_cu;
+        // Workgroups per compute unit: a step with prefill rows is bound by the per-tile
+        // arithmetic, which two workgroups per unit overlap better, where their LDS fits
+        // (head_dim 64, 16-bit: measured 23 vs 33 us on the ragged mixed step); decode-only
+        // steps are bound by memory latency and do best with one (saturated decode 7.1 vs
+        // 10.5 us, the extra split's merge dominates).
+        int gpc = lim.groups_per_cu;
+        if (gpc <= 0) {
+            bool prefill = false;
+            for (int32_t r = 0; r < B && !prefill; ++r)
+                prefill = in.qo_indptr && in.qo_indptr[r + 1] - in.qo_indptr[r] > 1;
+            gpc = prefill && lim.head_dim <= 64 && lim.dtype != FL_F32 ? 2 : 1;
+        }
+        const int64_t want = (int64_t)lim.num_cus * gpc;
         const int64_t G_max = std::min(std::max<int64_t>(1, std::min(want, ceil_div(T, lim.min_group_tiles))), T);
         const int64_t U = (int64_t)lim.waves * kRingDepth;
         auto cost = [&](int64_t n) { return U * ceil_div(n, U) + kFoldCostTiles; };
