@@ -725,14 +725,13 @@ struct Smem {
 
 // Merge of a row block's pieces by the piece that finished last:
 //   M = max_s lse_s,  w_s = 2^(lse_s - M),  out = sum_s w_s o_s / sum_s w_s.
-// The partial rows were written with device-scope stores and are read the same way, eight
-// pieces at a time with every load of a batch issued before any is used (the running max
+// The partial rows were written with device-scope stores and are read the same way, a batch
+// of pieces at a time with every load of a batch issued before any is used (the running max
 // carries across batches by rescaling, as in the online softmax). Partial-row byte
 // offsets fit in 32 bits: the workspace is sized from the handle's capacities.
-template <int DT, int D, int TPR>
+template <int DT, int D, int TPR, int MB>
 __device__ __forceinline__ void merge_pieces(const Seg &w, const AttnArgs &a, int r, int c0) {
     constexpr int EPT = D / TPR;
-    constexpr int MB = 8;
     const int nr = w.num_rows;
     const int base = w.part_row - w.split * nr;
     const int ns = w.num_splits;
@@ -1022,7 +1021,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
         for (int i = 0; i < 2; ++i) {
             if (pend[i] < 0 || !sm.last[i]) continue;
             const Seg ps = seg_fields_mem(a.segs + (size_t)pend[i] * FL_WORK_ITEM_INTS);
-            if (r < ps.num_rows) merge_pieces<DT, D, TPR>(ps, a, r, c0);
+            if (ps.num_rows > kBlockRows / 2) {
+                if (r < ps.num_rows) merge_pieces<DT, D, TPR, 8>(ps, a, r, c0);
+            } else {  // up to 8 rows: twice the threads per row, up to 16 pieces per batch
+                constexpr int TPR2 = 2 * TPR;
+                const int r2 = threadIdx.x / TPR2;
+                if (r2 < ps.num_rows) merge_pieces<DT, D, TPR2, 16>(ps, a, r2, (threadIdx.x % TPR2) * (D / TPR2));
+            }
         }
     }
 }
