@@ -1,9 +1,8 @@
 // Plan metadata copy: pinned host staging -> the handle's device regions, one small kernel
 // that reads the staging buffer over the bus (instead of one DMA transfer per region).
+// Offsets are 16-byte aligned; sizes are multiples of 4 bytes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-
-#include <algorithm>
 
 #include "fl_internal.h"
 
@@ -12,29 +11,42 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
-__global__ __launch_bounds__(256) void stage_copy_kernel(const StageCopy c) {
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
-#pragma unroll
-    for (int p = 0; p < kStageParts; ++p) {
-        const char *src = c.src + c.off[p];
-        char *dst = c.dst + c.off[p];
-        const int64_t n16 = c.bytes[p] / 16;
-        for (int64_t i = tid; i < n16; i += nthreads)
-            *reinterpret_cast<u32x4 *>(dst + 16 * i) = *reinterpret_cast<const u32x4 *>(src + 16 * i);
-        for (int64_t i = 16 * n16 + 4 * tid; i < c.bytes[p]; i += 4 * nthreads)
-            *reinterpret_cast<uint32_t *>(dst + i) = *reinterpret_cast<const uint32_t *>(src + i);
+// Every thread copies one 16-byte chunk (or one 4-byte word of a part's tail) of one part:
+// all reads of the bus go out at once, so the copy costs one round trip.
+__global__ __launch_bounds__(256) void stage_copy_kernel(const StageCopy c, int64_t chunks0, int64_t chunks1) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // chunk index over all parts
+    int p = 0;
+    if (i >= chunks0) {
+        i -= chunks0;
+        p = 1;
+        if (i >= chunks1) {
+            i -= chunks1;
+            p = 2;
+        }
+    }
+    const char *src = c.src + c.off[p];
+    char *dst = c.dst + c.off[p];
+    const int64_t n16 = c.bytes[p] / 16;
+    if (i < n16) {
+        *reinterpret_cast<u32x4 *>(dst + 16 * i) = *reinterpret_cast<const u32x4 *>(src + 16 * i);
+    } else {  // the part's last 4, 8 or 12 bytes, one word per thread
+        const int64_t b = 16 * n16 + 4 * (i - n16);
+        if (b < c.bytes[p]) *reinterpret_cast<uint32_t *>(dst + b) = *reinterpret_cast<const uint32_t *>(src + b);
     }
 }
 
 }  // namespace
 
 int launch_stage_copy(const StageCopy &c, void *stream) {
-    int64_t chunks = 0;
-    for (int p = 0; p < kStageParts; ++p) chunks = std::max<int64_t>(chunks, (c.bytes[p] + 15) / 16);
-    if (chunks == 0) return (int)hipSuccess;
-    const int grid = (int)std::min<int64_t>((chunks + 255) / 256, 1024);
-    hipLaunchKernelGGL(stage_copy_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, c);
+    static_assert(kStageParts == 3, "three parts");
+    int64_t ch[kStageParts];  // 16-byte chunks of each part plus up to 3 tail words
+    for (int p = 0; p < kStageParts; ++p) ch[p] = c.bytes[p] / 16 + (c.bytes[p] % 16) / 4;
+    const int64_t total = ch[0] + ch[1] + ch[2];
+    if (total == 0) return (int)hipSuccess;
+    const int64_t grid = (total + 255) / 256;
+    if (grid > INT32_MAX) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(stage_copy_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, c, ch[0],
+                       ch[1]);
     return (int)hipGetLastError();
 }
 
