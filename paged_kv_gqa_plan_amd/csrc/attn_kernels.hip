@@ -6,28 +6,27 @@
 // several compute units and the partial results merged ("A library kernel for decode",
 // What changed: per-slice partial results merged into one).
 //
-// Work layout. The plan gives each workgroup an equal contiguous share of all row blocks'
-// tiles: a list of segments (pieces of row blocks) whose tiles the waves take round-robin
-// across the whole share. Each tile's pool row was resolved by the plan, so the loads need
-// no page table and no segment state: each wave keeps PF tiles of K and V in flight in a
-// register ring across segment boundaries, refilling a slot as soon as its tile is
-// consumed. Segment headers arrive two segments ahead and Q one segment ahead; at each
-// segment's end the waves fold their softmax states in LDS and write the output rows, or,
-// for a row block cut by a share boundary, fp32 partial rows. The piece of a cut block that
-// finishes last merges the partials by log-sum-exp.
+// Work layout. The plan gives each workgroup a contiguous share of all row blocks' tiles
+// (shares of equal estimated time): a list of segments (pieces of row blocks) whose tiles
+// the waves take round-robin across the whole share. Each tile's pool row was resolved by
+// the plan, so the loads need no page table and no segment state. Each wave keeps PF tiles
+// of K and V in flight in its own LDS ring, loaded straight into LDS with full-cache-line
+// loads and refilled as soon as a tile is consumed, across segment boundaries. Segment
+// headers, Q rows and windows of pool rows are staged into LDS the same way, ahead of
+// use. At each segment's end the waves fold their softmax states in LDS and write the
+// output rows, or, for a row block cut by a share boundary, fp32 partial rows. The piece
+// of a cut block that finishes last merges the partials by log-sum-exp.
 //
 // Per 16-key tile, a wave computes
 //   S^T[16 keys x 16 rows]  = K_tile . Q^T      (MFMA 16x16x32, 16-bit; 16x16x4, fp32)
 //   online softmax per row in the exp2 domain (scale * log2(e) folded into one factor)
-//   O^T[d x 16 rows]       += V_tile^T . P^T     (MFMA 16x16x32, 16-bit; 16x16x4, fp32)
+//   O^T[d x 16 rows]       += V_tile^T . P^T     (MFMA 16x16x16 twice, 16-bit; 16x16x4, fp32)
 // The S^T accumulator layout (lane = row + 16 * (key / 4), 4 keys per lane) is exactly the
 // B-operand layout the PV instruction wants for P^T, so P never leaves registers. V is
-// stored token-major, so its tokens must move into each lane's registers: for 16-bit
-// types one extra MFMA against the identity matrix turns the natural row load
-// (4 consecutive d of one token per lane) into 4 tokens of one d per lane, exactly.
-// Since the contraction over d can run in any order, each lane loads a contiguous
-// 16-byte piece of a K row and the matching piece of the q row, and the output columns
-// are permuted the same way, so every global load and store is a 16-byte vector access.
+// stored token-major; for 16-bit types the transpose LDS read gives each lane 4 keys of
+// one output column, which is the A operand of PV. Since the contraction over d can run
+// in any order, each lane holds a contiguous 16-byte piece of a K row and the matching
+// piece of the q row, and the output columns are permuted the same way.
 //
 // Memory is read straight from the pool: token t of a request lives in page
 // kv_indices[page_base + t / P], slot t % P, at pool row (page * P + slot) * Hkv + kv_head.
@@ -499,11 +498,10 @@ struct HalfTile {
         }
         // P = P_hi + P_lo, both in the 16-bit type: the pair carries p to ~16 bits more
         // than one rounding would, so the product with the exact 16-bit V loses nothing
-        // measurable. One K=32 instruction contracts [V^T V^T] with [P_hi; P_lo].
+        // measurable. Two K=16 instructions contract V^T with P_hi and with P_lo.
         const uint32_t h01 = H::pack(p[0], p[1]), h23 = H::pack(p[2], p[3]);
         const uint32_t l01 = H::pack(p[0] - H::lo_f(h01), p[1] - H::hi_f(h01));
         const uint32_t l23 = H::pack(p[2] - H::lo_f(h23), p[3] - H::hi_f(h23));
-        const u32x4 pk = {h01, h23, l01, l23};
         // keys at or past tok_end may hold anything (NaN included): their V becomes 0
         u32x2 vt[NJ];
 #pragma unroll
@@ -516,7 +514,10 @@ struct HalfTile {
             for (int j = 0; j < NJ; ++j) vt[j] &= vmask;
         }
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) o[j] = H::mma_k32(u32x4{vt[j][0], vt[j][1], vt[j][0], vt[j][1]}, pk, o[j]);
+        for (int j = 0; j < NJ; ++j) {
+            o[j] = H::mma_k16(vt[j], u32x2{h01, h23}, o[j]);
+            o[j] = H::mma_k16(vt[j], u32x2{l01, l23}, o[j]);
+        }
     }
 
     // accumulator element (block j, element e) of lane (col, grp) -> output column d

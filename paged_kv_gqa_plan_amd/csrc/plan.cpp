@@ -10,11 +10,11 @@
 //     key its final row may see plus one (kv_len - qo_len + i_last + 1); they form
 //     ceil(kv_end / 16) tiles.
 //   * Every block's tiles are laid in one sequence (request, kv head, row block order) and
-//     the sequence is cut into equal contiguous shares, one per workgroup, about one
-//     workgroup per compute unit. Long histories thereby spread over many compute units
-//     and short ones pack together, so every unit streams the same number of tiles
-//     ("A library kernel for decode", What changed: one history's slices run on many
-//     processor groups; What I expected: the longest histories set the step's cost).
+//     the sequence is cut into contiguous shares of equal estimated time (ring steps plus
+//     a charge per segment fold), one per workgroup, one or two workgroups per compute
+//     unit. Long histories thereby spread over many compute units and short ones pack
+//     together ("A library kernel for decode", What changed: one history's slices run on
+//     many processor groups; What I expected: the longest histories set the step's cost).
 //     A block cut by a share boundary becomes several pieces whose partial results are
 //     merged by log-sum-exp; only the first and last piece of a share can be partial.
 //   * Within a share's segment, tile j runs on wave j % NW as that wave's step j / NW, and
