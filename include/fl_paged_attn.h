@@ -76,7 +76,8 @@ typedef struct {
     int32_t page_size;         /* power of two in [16, 256]                              */
     int32_t dtype;             /* fl_dtype of q, pools and out                           */
     int32_t max_batch;         /* most requests one plan may hold                        */
-    int32_t max_qo_rows;       /* most query rows one plan may hold (qo_indptr[batch])   */
+    int32_t max_qo_rows;       /* most query rows one plan may hold (qo_indptr[batch]);
+                                  (max_qo_rows * G + 16) * G must be below 2^32          */
     int64_t max_kv_pages;      /* most page-table entries one plan may hold              */
     int32_t num_cus;           /* compute units to plan for; 0 = ask the device
                                   (a host-only handle then plans for 256)                */

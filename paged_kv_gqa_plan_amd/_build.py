@@ -13,9 +13,11 @@ LIB = os.path.join(PKG, "libfl_paged_attn.so")
 SOURCES = ["plan.cpp", "api.cpp", "attn_kernels.hip", "stage_copy.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of every kernel; MFMA accumulators live in ordinary
-# VGPRs (the accumulator-register form costs a copy each time the VALU touches them).
+# VGPRs (the accumulator-register form costs a copy each time the VALU touches them); the
+# attention kernel's first seven argument dwords (record, pools, kv heads) are preloaded
+# into SGPRs at dispatch.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-kernarg-preload-count=7"]
 
 
 def hipcc() -> str:

@@ -89,6 +89,12 @@ fl_status check_config(const fl_config *c) {
                                            "max_tiles must be >= 0");
     if (c->waves_per_group != 0 && c->waves_per_group != 4)
         return set_err(FL_ERR_UNSUPPORTED, "waves_per_group must be 0 or 4");
+    // the kernels divide flattened rows of a request (below max_qo_rows * G + 16) by G
+    // with a 32-bit reciprocal multiply, exact while the dividend stays below 2^32 / G
+    const uint64_t g = (uint64_t)(c->num_qo_heads / c->num_kv_heads);
+    if (((uint64_t)c->max_qo_rows * g + 16) * g >= (1ull << 32))
+        return set_err(FL_ERR_UNSUPPORTED, "(max_qo_rows * G + 16) * G must be below 2^32 "
+                                           "(G = num_qo_heads / num_kv_heads)");
     return FL_OK;
 }
 
@@ -305,6 +311,7 @@ fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, cons
     a.num_qo_heads = h->cfg.num_qo_heads;
     a.num_kv_heads = h->cfg.num_kv_heads;
     a.group = h->group;
+    a.group_magic = h->group > 1 ? (uint32_t)(((1ull << 32) + h->group - 1) / h->group) : 0u;
     a.causal = h->causal;
     a.scale_log2 = h->scale_log2;
     const int e = fl::launch_attention(h->cfg.dtype, h->cfg.head_dim, h->waves, p.num_groups, a,

@@ -320,10 +320,18 @@ struct RowInfo {
     bool ok;
 };
 
+// f / G for 0 <= f < 2^32 / G. With m = ceil(2^32 / G) = 2^32 / G + e, 0 <= e < 1, the
+// product f * m / 2^32 exceeds f / G by f * e / 2^32 < 1 / G, while f / G sits at least
+// 1 / G below the next integer, so the high word of f * m is exactly floor(f / G). The
+// create call bounds every flattened row so that this holds. G = 1 has m = 0 and adds f.
+__device__ __forceinline__ int div_group(int f, const AttnArgs &a) {
+    return (int)__umulhi((uint32_t)f, a.group_magic) + (a.group_magic ? 0 : f);
+}
+
 // End of the keys every real row of the segment's block may see (the first row has the
 // tightest causal limit): tiles wholly below it need no mask.
 __device__ __forceinline__ int seg_full_end(const Seg &w, const AttnArgs &a) {
-    const int first_limit = a.causal ? w.kv_len - w.qo_len + w.row_begin / a.group : w.kv_len - 1;
+    const int first_limit = a.causal ? w.kv_len - w.qo_len + div_group(w.row_begin, a) : w.kv_len - 1;
     return min(w.tok_end, first_limit + 1);
 }
 
@@ -331,7 +339,7 @@ __device__ __forceinline__ RowInfo row_info(const Seg &w, const AttnArgs &a, int
     RowInfo ri;
     const int f = w.row_begin + col;
     ri.ok = col < w.num_rows;
-    ri.qi = f / a.group;
+    ri.qi = div_group(f, a);
     ri.qh = f - ri.qi * a.group;
     ri.limit = !ri.ok ? -1 : (a.causal ? w.kv_len - w.qo_len + ri.qi : w.kv_len - 1);
     return ri;
@@ -342,12 +350,12 @@ __device__ __forceinline__ RowInfo row_info(const Seg &w, const AttnArgs &a, int
 // the returned offset (in rows) of block row r from it is small (rows past num_rows use
 // row 0, whose data is never used).
 __device__ __forceinline__ int64_t q_block_base(const Seg &w, const AttnArgs &a) {
-    return ((int64_t)(w.q_start + w.row_begin / a.group) * a.num_qo_heads + w.kv_head * a.group);
+    return ((int64_t)(w.q_start + div_group(w.row_begin, a)) * a.num_qo_heads + w.kv_head * a.group);
 }
 __device__ __forceinline__ int q_block_row(const Seg &w, const AttnArgs &a, int r) {
     const int f = w.row_begin + (r < w.num_rows ? r : 0);
-    const int qi = f / a.group;
-    return (qi - w.row_begin / a.group) * a.num_qo_heads + (f - qi * a.group);
+    const int qi = div_group(f, a);
+    return (qi - div_group(w.row_begin, a)) * a.num_qo_heads + (f - qi * a.group);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -482,6 +490,9 @@ struct HalfTile {
     // registers) where the arithmetic is long enough to hide the wait for the LDS reads:
     // measured faster at head_dim 128, slower at 64.
     static constexpr bool kEarlyRefill = D >= 128;
+    // Issue the first tile ahead of the Q rows at the start: measured faster at head_dim
+    // 128 (2-6%), slower at 64 (where the second tile then leaves later).
+    static constexpr bool kTileFirst = D >= 128;
 
     __device__ static void compute(const Frag &f, const QOp &q, int t0, int col, int grp, int tok_end,
                                    int limit, bool full, float scale_log2, float &m_run, float &l_run,
@@ -604,6 +615,7 @@ struct F32Tile {
     __device__ static const Frag &ring_frag(const Ring<PF> &r, int slot) { return r.buf[slot]; }
     __device__ static void ring_release() {}
     static constexpr bool kEarlyRefill = false;
+    static constexpr bool kTileFirst = false;
 
     __device__ static void load(Frag &f, const void *k, const void *v, int row0, int hkv, int col,
                                 int grp) {
@@ -716,12 +728,28 @@ __device__ __forceinline__ void part_store1(__amdgpu_buffer_rsrc_t rs, int byte_
 // ---------------------------------------------------------------------------------------
 // LDS for the per-segment fold: the four wave states
 // ---------------------------------------------------------------------------------------
+// Fields of a piece whose merge ticket is still to be drawn, kept in LDS from its fold to
+// the end of the kernel (no global reload of its header on the way to the merge).
+enum { PD_MERGE, PD_NUM_SPLITS, PD_NUM_ROWS, PD_PART_ROW, PD_SPLIT, PD_ROW_BEGIN, PD_Q_START,
+       PD_KV_HEAD, PD_INTS };
 template <int D>
 struct Smem {
     float o[4][kBlockRows][D + 4];
     float m[4][kBlockRows];
     float l[4][kBlockRows];
+    int pend[2][PD_INTS];
     int last[2];
+};
+
+// Columns of a row handled by thread t of the TPR threads on it: EPT = D / TPR values in
+// chunks of up to four floats, chunk q at column CW * (q * TPR + t), so each load or store
+// instruction covers whole contiguous stretches of the row across the threads.
+template <int D, int TPR>
+struct RowSplit {
+    static constexpr int EPT = D / TPR;
+    static constexpr int CW = EPT < 4 ? EPT : 4;
+    static constexpr int NCH = EPT / CW;
+    __device__ static __forceinline__ int col(int t, int q) { return CW * (q * TPR + t); }
 };
 
 // Merge of a row block's pieces by the piece that finished last:
@@ -731,8 +759,9 @@ struct Smem {
 // carries across batches by rescaling, as in the online softmax). Partial-row byte
 // offsets fit in 32 bits: the workspace is sized from the handle's capacities.
 template <int DT, int D, int TPR, int MB>
-__device__ __forceinline__ void merge_pieces(const Seg &w, const AttnArgs &a, int r, int c0) {
-    constexpr int EPT = D / TPR;
+__device__ __forceinline__ void merge_pieces(const Seg &w, const AttnArgs &a, int r, int t) {
+    using RS = RowSplit<D, TPR>;
+    constexpr int EPT = RS::EPT, CW = RS::CW;
     const int nr = w.num_rows;
     const int base = w.part_row - w.split * nr;
     const int ns = w.num_splits;
@@ -746,9 +775,17 @@ __device__ __forceinline__ void merge_pieces(const Seg &w, const AttnArgs &a, in
         float ov[MB][EPT];
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
-            const int pr = base + min(s0 + i, ns - 1) * nr + r;  // a repeat past the end is unused
-            ls[i] = part_load1(rl, pr * 4);
-            part_load<EPT>(ro, (pr * D + c0) * 4, ov[i]);
+            if (s0 + i < ns) {  // the vector-memory path of one compute unit bounds the merge:
+                                // no loads past the last piece
+                const int pr = base + (s0 + i) * nr + r;
+                ls[i] = part_load1(rl, pr * 4);
+#pragma unroll
+                for (int q = 0; q < RS::NCH; ++q) part_load<CW>(ro, (pr * D + RS::col(t, q)) * 4, ov[i] + q * CW);
+            } else {
+                ls[i] = kNegInf;
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) ov[i][e] = 0.f;
+            }
         }
         float bm = M;
 #pragma unroll
@@ -771,19 +808,20 @@ __device__ __forceinline__ void merge_pieces(const Seg &w, const AttnArgs &a, in
 #pragma unroll
     for (int e = 0; e < EPT; ++e) acc[e] *= inv;
     const int f = w.row_begin + r;
-    const int qi = f / a.group;
+    const int qi = div_group(f, a);
     const int qh = f - qi * a.group;
     const int64_t row = (int64_t)(w.q_start + qi) * a.num_qo_heads + w.kv_head * a.group + qh;
-    store_out<DT, EPT>(a.out, row * D + c0, acc);
-    if (a.lse && c0 == 0) a.lse[row] = (M + fast_log2(L)) * kLn2;
+#pragma unroll
+    for (int q = 0; q < RS::NCH; ++q) store_out<DT, CW>(a.out, row * D + RS::col(t, q), acc + q * CW);
+    if (a.lse && t == 0) a.lse[row] = (M + fast_log2(L)) * kLn2;
 }
 
 // Fold of one segment across the waves (all waves call it at the same step), then the
 // output rows: final rows for a whole row block, device-scope fp32 partial rows for a piece.
 template <class T, int DT, int D, int NW>
 __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, const Seg &cs, int k,
-                                             float &m_run, float &l_run, f32x4 *o, int &pend0,
-                                             int &pend1, int wave, int col, int grp) {
+                                             float &m_run, float &l_run, f32x4 *o, int &npend,
+                                             int wave, int col, int grp) {
     constexpr int NJ = D / 16;
     constexpr int TPR = NW * 64 / kBlockRows;
     constexpr int EPT = D / TPR;
@@ -795,7 +833,9 @@ __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, con
     }
     __syncthreads();
     const int r = threadIdx.x / TPR;
-    const int c0 = (threadIdx.x % TPR) * EPT;
+    const int t = threadIdx.x % TPR;
+    using RS = RowSplit<D, TPR>;
+    constexpr int CW = RS::CW;
     if (r < cs.num_rows) {
         float M = kNegInf;
 #pragma unroll
@@ -813,27 +853,38 @@ __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, con
         for (int e = 0; e < EPT; ++e) {
             float acc = 0.f;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc += sm.o[v][r][c0 + e] * wt[v];
+            for (int v = 0; v < 4; ++v) acc += sm.o[v][r][RS::col(t, e / CW) + e % CW] * wt[v];
             res[e] = acc * inv;
         }
         const float lse2 = L > 0.f ? M + fast_log2(L) : kNegInf;  // log2 domain
         if (cs.part_row < 0) {
             const int f = cs.row_begin + r;
-            const int qi = f / a.group;
+            const int qi = div_group(f, a);
             const int qh = f - qi * a.group;
             const int64_t row = (int64_t)(cs.q_start + qi) * a.num_qo_heads + cs.kv_head * a.group + qh;
-            store_out<DT, EPT>(a.out, row * D + c0, res);
-            if (a.lse && c0 == 0) a.lse[row] = lse2 * kLn2;
+#pragma unroll
+            for (int q = 0; q < RS::NCH; ++q) store_out<DT, CW>(a.out, row * D + RS::col(t, q), res + q * CW);
+            if (a.lse && t == 0) a.lse[row] = lse2 * kLn2;
         } else {
-            part_store<EPT>(part_rsrc(a.part_o), ((cs.part_row + r) * D + c0) * 4, res);
-            if (c0 == 0) part_store1(part_rsrc(a.part_lse), (cs.part_row + r) * 4, lse2);
+#pragma unroll
+            for (int q = 0; q < RS::NCH; ++q)
+                part_store<CW>(part_rsrc(a.part_o), ((cs.part_row + r) * D + RS::col(t, q)) * 4, res + q * CW);
+            if (t == 0) part_store1(part_rsrc(a.part_lse), (cs.part_row + r) * 4, lse2);
         }
     }
-    if (cs.part_row >= 0) {
-        if (pend0 < 0)
-            pend0 = k;
-        else
-            pend1 = k;
+    if (cs.part_row >= 0 && npend < 2) {  // the plan cuts only a share's first and last piece
+        if (threadIdx.x == 0) {
+            int *pd = sm.pend[npend];
+            pd[PD_MERGE] = cs.merge;
+            pd[PD_NUM_SPLITS] = cs.num_splits;
+            pd[PD_NUM_ROWS] = cs.num_rows;
+            pd[PD_PART_ROW] = cs.part_row;
+            pd[PD_SPLIT] = cs.split;
+            pd[PD_ROW_BEGIN] = cs.row_begin;
+            pd[PD_Q_START] = cs.q_start;
+            pd[PD_KV_HEAD] = cs.kv_head;
+        }
+        ++npend;
     }
     __syncthreads();  // the LDS slots are free again
     m_run = kNegInf;
@@ -852,11 +903,15 @@ __device__ __forceinline__ void stage_rows(const lds_char *dst, const int32_t *r
 // ---------------------------------------------------------------------------------------
 // the kernel: one workgroup per equal share of the plan's tiles
 // ---------------------------------------------------------------------------------------
+// The record and the pools come as separate leading arguments as well: those arrive in
+// SGPRs with the dispatch (kernel-argument preloading), so the record's loads go out at
+// once, beside the loads of the other arguments instead of after them.
 template <class T, int DT, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, const void *k_pool,
+                                                      const void *v_pool, int hkv, const AttnArgs a) {
     static_assert(NW == 4 && NW <= kMaxWaves, "four waves per workgroup");
-    static_assert(REC_ROWS + kMaxWaves * kRingDepth <= REC_HEAD &&
-                  REC_HEAD + FL_WORK_ITEM_INTS <= kRecInts, "record layout");
+    static_assert(REC_HEAD + FL_WORK_ITEM_INTS <= REC_SEG_BEGIN &&
+                  REC_ROWS + kMaxWaves * kRingDepth <= kRecInts, "record layout");
     constexpr int PF = kRingDepth;
     constexpr int NJ = D / 16;
     constexpr int TPR = NW * 64 / kBlockRows;  // fold: threads per row
@@ -877,17 +932,26 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     const int col = lane & 15;
     const int grp = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    // The workgroup record (scalar loads, all read before the first LDS load is issued)
-    // gives the share, the first segment and every wave's first pool rows.
-    const int32_t *rec = a.wg_rec + (size_t)blockIdx.x * kRecInts;
-    const int seg_b = rec[REC_SEG_BEGIN], seg_e = rec[REC_SEG_END];
-    const int pos0 = rec[REC_POS];
-    const int nsteps = rec[REC_STEPS];  // steps per wave (a positive multiple of PF)
-    int seg_end = rec[REC_FIRST_END];
-    int row_first[PF];
+    // The workgroup record gives the share, the first segment and every wave's first pool
+    // rows: one batch of scalar loads, issued before anything else.
+    const int32_t *rec = wg_rec + (size_t)blockIdx.x * kRecInts;
+    int rv[REC_ROWS + kMaxWaves * PF];
 #pragma unroll
-    for (int s = 0; s < PF; ++s) row_first[s] = rec[REC_ROWS + wv * PF + s];
-    Seg cs = seg_fields_mem(rec + REC_HEAD);
+    for (int i = 0; i < REC_ROWS + kMaxWaves * PF; ++i) rv[i] = rec[i];
+    __builtin_amdgcn_sched_barrier(0);
+    const int seg_b = rv[REC_SEG_BEGIN], seg_e = rv[REC_SEG_END];
+    const int pos0 = rv[REC_POS];
+    const int nsteps = rv[REC_STEPS];  // steps per wave (a positive multiple of PF)
+    int seg_end = rv[REC_FIRST_END];
+    int row_first[PF];  // this wave's (a select over the waves' entries, all in SGPRs)
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+        int r = rv[REC_ROWS + s];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) r = wv == w ? rv[REC_ROWS + w * PF + s] : r;
+        row_first[s] = r;
+    }
+    Seg cs = seg_fields_mem(rv + REC_HEAD);
     int k = seg_b;
     const int32_t *rows = a.step_rows + pos0 + wv * nsteps;
     const lds_char *ring_b = (const lds_char *)wave_lds + wv * kWaveB;
@@ -896,18 +960,20 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     const lds_char *rows_b = hdr_b + 4 * kHdrSlot;
     auto hdr_slot = [&](int seg) { return hdr_b + kHdrSlot * ((seg - seg_b) & 3); };
 
-    // Q, the next two headers and the first row windows go out ahead of the ring, so
-    // that reading them never waits for a K/V tile.
+    // Q, the next two headers and the first row windows go out ahead of the ring, or just
+    // behind its first tile (whose addresses need the least arithmetic); the first
+    // arrival waits for all but the ring slots behind them.
+    typename T::template Ring<PF> ring;
+    T::ring_init(ring, ring_b, lane, hkv);
+    constexpr int kAhead = T::kTileFirst ? 1 : 0;  // ring slots issued before Q
+    static_for<0, kAhead>([&](auto si) { T::ring_issue(ring, si, k_pool, v_pool, row_first[si]); });
     T::q_stage(q_b, a, cs, lane);
     stage_header(hdr_slot(seg_b + 1), a.segs, min(seg_b + 1, seg_e - 1), lane);
     stage_header(hdr_slot(seg_b + 2), a.segs, min(seg_b + 2, seg_e - 1), lane);
     stage_rows(rows_b, rows, 0, nsteps, lane);
     stage_rows(rows_b + 256, rows, 64, nsteps, lane);
-    typename T::template Ring<PF> ring;
-    T::ring_init(ring, ring_b, lane, a.num_kv_heads);
-#pragma unroll
-    for (int s = 0; s < PF; ++s) T::ring_issue(ring, s, a.k, a.v, row_first[s]);
-    wait_vm<PF * kLoads>();  // everything but the ring
+    static_for<kAhead, PF>([&](auto si) { T::ring_issue(ring, si, k_pool, v_pool, row_first[si]); });
+    wait_vm<(PF - kAhead) * kLoads>();
     RowInfo ri = row_info(cs, a, col);
     typename T::QOp qc = T::q_fetch(q_b, ri, col, grp);
     int ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
@@ -917,7 +983,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     f32x4 o[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    int pend0 = -1, pend1 = -1;  // pieces whose merge ticket is still to be drawn
+    int npend = 0;  // pieces whose merge ticket is still to be drawn (fields in sm.pend)
 
     // ---- the step stream: PF tiles of K and V in flight per wave -------------------------
     // Every slot of the ring is in flight until its step (padding steps re-read a real tile
@@ -931,7 +997,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
         constexpr bool kRefill = decltype(refill)::value;
         wait_vm<PF * kLoads>();
         if (p0 == seg_end) {  // the same step in every wave: segment k is done
-            fold_segment<T, DT, D, NW>(sm, a, cs, k, m_run, l_run, o, pend0, pend1, wave, col, grp);
+            fold_segment<T, DT, D, NW>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);
             ++k;
             cs = seg_fields_lds(hdr_slot(k));
             seg_end = k + 1 < seg_e ? lds_int(hdr_slot(k + 1) + 4 * FL_WI_POS_BEGIN) : nsteps;
@@ -970,7 +1036,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
                         win = q >> 6;
                         stage_rows(rows_b + 256 * ((win + 1) & 1), rows, 64 * (win + 1), nsteps, lane);
                     }
-                    T::ring_issue(ring, s, a.k, a.v, nrow[s]);
+                    T::ring_issue(ring, s, k_pool, v_pool, nrow[s]);
                 }
             };
             // An LDS slot is free once its tile is in registers: refill it before computing,
@@ -989,45 +1055,67 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     int p0 = 0;
     for (; p0 + PF < nsteps; p0 += PF) group(p0, std::true_type{});
     group(p0, std::false_type{});
-    fold_segment<T, DT, D, NW>(sm, a, cs, k, m_run, l_run, o, pend0, pend1, wave, col, grp);
+    fold_segment<T, DT, D, NW>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);
 
     // ---- merge tickets of the partial pieces (at most the first and the last) -----------
     // The partial rows went out as device-scope stores; each wave waits for their
-    // acknowledgement before the workgroup draws its tickets with device-scope atomics, so
-    // the piece that draws a row block's last ticket finds every other piece complete.
-    if (pend0 >= 0) {
+    // acknowledgement before the workgroup draws its tickets with device-scope atomics (one
+    // lane per piece, both in one instruction), so the piece that draws a row block's last
+    // ticket finds every other piece complete.
+    if (npend > 0) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (threadIdx.x == 0) {
-            const int pend[2] = {pend0, pend1};
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                sm.last[i] = 0;
-                if (pend[i] < 0) continue;
-                const int32_t *hp = a.segs + (size_t)pend[i] * FL_WORK_ITEM_INTS;
-                const int tk = hp[FL_WI_MERGE], ns = hp[FL_WI_NUM_SPLITS];
+        if (threadIdx.x < 2) {
+            int last = 0;
+            if ((int)threadIdx.x < npend) {
+                const int *pd = sm.pend[threadIdx.x];
+                const int tk = pd[PD_MERGE];
                 const int done = __hip_atomic_fetch_add(a.tickets + tk, 1, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT);
-                if (done == ns - 1) {
+                if (done == pd[PD_NUM_SPLITS] - 1) {
                     __hip_atomic_store(a.tickets + tk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    sm.last[i] = 1;
+                    last = 1;
                 }
             }
+            sm.last[threadIdx.x] = last;
         }
         __syncthreads();
-        const int r = threadIdx.x / TPR;
-        const int c0 = (threadIdx.x % TPR) * EPT;
-        const int pend[2] = {pend0, pend1};
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            if (pend[i] < 0 || !sm.last[i]) continue;
-            const Seg ps = seg_fields_mem(a.segs + (size_t)pend[i] * FL_WORK_ITEM_INTS);
+        auto pend_seg = [&](int i) {
+            const lds_char *pd = (const lds_char *)sm.pend[i];
+            Seg ps{};
+            ps.merge = lds_int(pd + 4 * PD_MERGE);
+            ps.num_splits = lds_int(pd + 4 * PD_NUM_SPLITS);
+            ps.num_rows = lds_int(pd + 4 * PD_NUM_ROWS);
+            ps.part_row = lds_int(pd + 4 * PD_PART_ROW);
+            ps.split = lds_int(pd + 4 * PD_SPLIT);
+            ps.row_begin = lds_int(pd + 4 * PD_ROW_BEGIN);
+            ps.q_start = lds_int(pd + 4 * PD_Q_START);
+            ps.kv_head = lds_int(pd + 4 * PD_KV_HEAD);
+            return ps;
+        };
+        const bool m0 = lds_int((const lds_char *)&sm.last[0]) != 0;
+        const bool m1 = npend > 1 && lds_int((const lds_char *)&sm.last[1]) != 0;
+        if (m0 && m1) {
+            // Both: waves 0-1 merge the first piece's block and waves 2-3 the second's, side
+            // by side (the compute unit's vector-memory path is shared either way).
+            static_assert(NW == 4, "two halves of two waves");
+            const int t = threadIdx.x & 127;
+            const Seg ps = pend_seg(__builtin_amdgcn_readfirstlane(threadIdx.x >> 7));
             if (ps.num_rows > kBlockRows / 2) {
-                if (r < ps.num_rows) merge_pieces<DT, D, TPR, 8>(ps, a, r, c0);
+                constexpr int TPH = TPR / 2;
+                if (t / TPH < ps.num_rows) merge_pieces<DT, D, TPH, 8>(ps, a, t / TPH, t % TPH);
+            } else {
+                if (t / TPR < ps.num_rows) merge_pieces<DT, D, TPR, 16>(ps, a, t / TPR, t % TPR);
+            }
+        } else if (m0 || m1) {
+            const Seg ps = pend_seg(m0 ? 0 : 1);
+            if (ps.num_rows > kBlockRows / 2) {
+                const int r = threadIdx.x / TPR;
+                if (r < ps.num_rows) merge_pieces<DT, D, TPR, 8>(ps, a, r, threadIdx.x % TPR);
             } else {  // up to 8 rows: twice the threads per row, up to 16 pieces per batch
                 constexpr int TPR2 = 2 * TPR;
                 const int r2 = threadIdx.x / TPR2;
-                if (r2 < ps.num_rows) merge_pieces<DT, D, TPR2, 16>(ps, a, r2, (threadIdx.x % TPR2) * (D / TPR2));
+                if (r2 < ps.num_rows) merge_pieces<DT, D, TPR2, 16>(ps, a, r2, threadIdx.x % TPR2);
             }
         }
     }
@@ -1045,7 +1133,8 @@ struct TileFor<FL_F32, D> {
 template <int DT, int D, int NW>
 hipError_t launch_t(int n, const AttnArgs &a, hipStream_t s) {  // n: workgroups
     using T = typename TileFor<DT, D>::type;
-    hipLaunchKernelGGL((attn_kernel<T, DT, D, NW>), dim3(n), dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<T, DT, D, NW>), dim3(n), dim3(NW * 64), 0, s, a.wg_rec, a.k, a.v,
+                       a.num_kv_heads, a);
     return hipGetLastError();
 }
 

@@ -25,16 +25,17 @@ constexpr int kRingDepth = FL_RING_DEPTH;
 // Planner's estimate of one segment fold (the cross-wave merge of the softmax states at a
 // segment's end) in units of tiles: measured at about 1.5 ring steps of a 4-wave group.
 constexpr int kFoldCostTiles = 6;
-// Per-workgroup record (int32): segment range, step range, the first segment's header and
-// end step, and the pool rows of every wave's first kRingDepth steps, so every load a
-// workgroup issues first (Q, K/V, step rows) depends on this record alone.
-constexpr int kRecInts = 64;
+// Per-workgroup record (int32): the first segment's header, the segment range, the step
+// range, the first segment's end step and the pool rows of every wave's first kRingDepth
+// steps, so every load a workgroup issues first (Q, K/V, step rows) depends on this record
+// alone. With two ring slots it is one 128-byte line, read by one batch of scalar loads.
 constexpr int kMaxWaves = 4;
 enum {
-    REC_SEG_BEGIN = 0, REC_SEG_END = 1, REC_POS = 2, REC_STEPS = 3, REC_FIRST_END = 4,
-    REC_ROWS = 8,    // kMaxWaves * kRingDepth entries
-    REC_HEAD = 48,   // FL_WORK_ITEM_INTS entries
+    REC_HEAD = 0,    // FL_WORK_ITEM_INTS entries
+    REC_SEG_BEGIN = 16, REC_SEG_END = 17, REC_POS = 18, REC_STEPS = 19, REC_FIRST_END = 20,
+    REC_ROWS = 24,   // kMaxWaves * kRingDepth entries
 };
+constexpr int kRecInts = (REC_ROWS + kMaxWaves * kRingDepth + 31) / 32 * 32;
 
 struct PlanLimits {
     int32_t num_qo_heads, num_kv_heads, head_dim, page_size;
@@ -100,6 +101,7 @@ struct AttnArgs {
     int32_t num_qo_heads;
     int32_t num_kv_heads;
     int32_t group;
+    uint32_t group_magic;      // ceil(2^32 / group) (unused when group == 1)
     int32_t causal;
     float scale_log2;          // sm_scale * log2(e)
 };

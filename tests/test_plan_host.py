@@ -76,6 +76,13 @@ def check_coverage(items, b, causal=True):
         for h in range(b.num_kv_heads):
             for f in range(int(b.qo_lens[r]) * G):
                 assert seen_rows.get((r, h, f)) == 1, (r, h, f)
+    # a workgroup holds at most two cut pieces, its first and its last segment (the kernel
+    # keeps the fields of two pending pieces for the merge tickets)
+    groups = col("group")
+    for g in np.unique(groups):
+        mine = np.nonzero(groups == g)[0]
+        cut = [j for j, i in enumerate(mine) if items[i, idx["part_row"]] >= 0]
+        assert len(cut) <= 2 and all(j in (0, len(mine) - 1) for j in cut), (g, cut)
     # the items carry the right request facts
     for it in items:
         r = it[idx["request"]]
@@ -266,6 +273,9 @@ def test_create_rejects_unsupported_configs():
     cfg = fl.make_config(14, 2, 64, 16, "bf16", 8, 8, 64)
     cfg.dtype = 7
     _expect(fl.FL_ERR_UNSUPPORTED, fl.fl_paged_attn_create, cfg, -1)
+    # flattened rows must stay below 2^32 / G for the kernels' division by G
+    _expect(fl.FL_ERR_UNSUPPORTED, host_handle, Hq=128, Hkv=1, max_rows=(1 << 18))
+    host_handle(Hq=128, Hkv=1, max_rows=(1 << 18) - 1)
 
 
 def test_run_needs_a_device_handle_and_a_plan():
