@@ -22,9 +22,33 @@ constexpr int kBlockRows = 16;
 #define FL_RING_DEPTH 2
 #endif
 constexpr int kRingDepth = FL_RING_DEPTH;
-// Planner's estimate of one segment fold (the cross-wave merge of the softmax states at a
-// segment's end) in units of tiles: measured at about 1.5 ring steps of a 4-wave group.
-constexpr int kFoldCostTiles = 6;
+// Planner's time estimate, in fifths of a streamed tile. A tile whose keys only its own
+// row block reads is streamed from memory (5); the tiles of a request with several row
+// blocks per kv head (a prefill chunk) are shared through the L2 cache (4: measured 0.098
+// vs 0.121 us per tile on a ragged mixed step). Each segment adds a fold (the cross-wave
+// merge of the softmax states at its end, with the padding of its last step group), and a
+// piece of a block cut by a share boundary adds its end-of-kernel merge ticket (and the
+// merge itself when it finishes last). Measured best: decode-only steps 6 and 4 tiles
+// (mixed-length decode 13.6 vs 14.5 us with 6 and 0), steps with a prefill chunk, whose
+// short decode blocks pack many segments into a share, 12 and 0 (ragged step 19.1 vs 19.7).
+constexpr int kStreamTileCost = 5;
+constexpr int kSharedTileCost = 4;
+#ifndef FL_FOLD_TILES_DECODE
+#define FL_FOLD_TILES_DECODE 6
+#endif
+#ifndef FL_CUT_TILES_DECODE
+#define FL_CUT_TILES_DECODE 4
+#endif
+#ifndef FL_FOLD_TILES_MIXED
+#define FL_FOLD_TILES_MIXED 12
+#endif
+#ifndef FL_CUT_TILES_MIXED
+#define FL_CUT_TILES_MIXED 0
+#endif
+constexpr int kFoldCostDecode = kStreamTileCost * FL_FOLD_TILES_DECODE;
+constexpr int kCutCostDecode = kStreamTileCost * FL_CUT_TILES_DECODE;
+constexpr int kFoldCostMixed = kStreamTileCost * FL_FOLD_TILES_MIXED;
+constexpr int kCutCostMixed = kStreamTileCost * FL_CUT_TILES_MIXED;
 // Per-workgroup record (int32): the first segment's header, the segment range, the step
 // range, the first segment's end step and the pool rows of every wave's first kRingDepth
 // steps, so every load a workgroup issues first (Q, K/V, step rows) depends on this record

@@ -35,6 +35,7 @@ namespace {
 
 struct Block {
     int32_t req, kvh, row_begin, nrows, kv_end;
+    int32_t tile_cost;  // kStreamTileCost, or kSharedTileCost when the request has several
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -127,12 +128,13 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         const int32_t kv_len = (np - 1) * P + in.last_page_len[r];
         const int32_t ql = in.qo_indptr ? in.qo_indptr[r + 1] - in.qo_indptr[r] : 1;
         const int32_t nflat = ql * G;
+        const int32_t tile_cost = nflat > kBlockRows ? kSharedTileCost : kStreamTileCost;
         for (int32_t h = 0; h < Hkv; ++h)
             for (int32_t f0 = 0; f0 < nflat; f0 += kBlockRows) {
                 const int32_t nr = std::min(kBlockRows, nflat - f0);
                 const int32_t i_last = (f0 + nr - 1) / G;
                 const int32_t kv_end = in.causal ? kv_len - ql + i_last + 1 : kv_len;
-                blocks.push_back({r, h, f0, nr, kv_end});
+                blocks.push_back({r, h, f0, nr, kv_end, tile_cost});
             }
     }
     const int64_t nblocks = (int64_t)blocks.size();
@@ -160,26 +162,29 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         }
     } else {
         // Contiguous shares of the tile sequence with equal estimated time. A piece of n tiles
-        // costs the ring steps it occupies in all waves (n rounded up to whole step groups)
-        // plus a fixed charge for its fold; a block cut inside a share is cut at a multiple
-        // of a step group, so only a block's last piece carries padding. The smallest
-        // per-share budget that needs at most G shares is found by bisection.
+        // costs the ring steps it occupies in all waves (n rounded up to whole step groups,
+        // at its block's tile cost) plus a fixed charge for its fold; a block cut inside a
+        // share is cut at a multiple of a step group, so only a block's last piece carries
+        // padding. The smallest per-share budget that needs at most G shares is found by
+        // bisection.
         // Workgroups per compute unit: a step with prefill rows is bound by the per-tile
         // arithmetic, which two workgroups per unit overlap better, where their LDS fits
         // (head_dim 64, 16-bit: measured 23 vs 33 us on the ragged mixed step); decode-only
         // steps are bound by memory latency and do best with one (saturated decode 7.1 vs
         // 10.5 us, the extra split's merge dominates).
+        bool prefill = false;
+        for (int32_t r = 0; r < B && !prefill; ++r)
+            prefill = in.qo_indptr && in.qo_indptr[r + 1] - in.qo_indptr[r] > 1;
         int gpc = lim.groups_per_cu;
-        if (gpc <= 0) {
-            bool prefill = false;
-            for (int32_t r = 0; r < B && !prefill; ++r)
-                prefill = in.qo_indptr && in.qo_indptr[r + 1] - in.qo_indptr[r] > 1;
-            gpc = prefill && lim.head_dim <= 64 && lim.dtype != FL_F32 ? 2 : 1;
-        }
+        if (gpc <= 0) gpc = prefill && lim.head_dim <= 64 && lim.dtype != FL_F32 ? 2 : 1;
+        const int64_t kFoldCost = prefill ? kFoldCostMixed : kFoldCostDecode;
+        const int64_t kCutCost = prefill ? kCutCostMixed : kCutCostDecode;
         const int64_t want = (int64_t)lim.num_cus * gpc;
         const int64_t G_max = std::min(std::max<int64_t>(1, std::min(want, ceil_div(T, lim.min_group_tiles))), T);
         const int64_t U = (int64_t)lim.waves * kRingDepth;
-        auto cost = [&](int64_t n) { return U * ceil_div(n, U) + kFoldCostTiles; };
+        auto cost = [&](int64_t b, int64_t n, bool cut) {
+            return blocks[b].tile_cost * U * ceil_div(n, U) + kFoldCost + (cut ? kCutCost : 0);
+        };
         // walk the blocks filling shares of budget C; emit pieces when `out` is set
         auto fill = [&](int64_t C, bool out) {
             int64_t shares = 0, b = 0, pos = 0;
@@ -187,14 +192,16 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
                 int64_t budget = C;
                 while (b < nblocks) {
                     const int64_t r = tiles[b] - pos;
-                    if (cost(r) <= budget) {
+                    if (cost(b, r, pos > 0) <= budget) {
                         if (out) pieces.push_back({b, pos, tiles[b], shares});
-                        budget -= cost(r);
+                        budget -= cost(b, r, pos > 0);
                         ++b;
                         pos = 0;
                         continue;
                     }
-                    const int64_t n = budget >= kFoldCostTiles + U ? U * ((budget - kFoldCostTiles) / U) : 0;
+                    const int64_t step_cost = blocks[b].tile_cost * U;
+                    const int64_t fixed = kFoldCost + kCutCost;
+                    const int64_t n = budget >= fixed + step_cost ? U * ((budget - fixed) / step_cost) : 0;
                     if (n > 0) {
                         if (out) pieces.push_back({b, pos, pos + n, shares});
                         pos += n;
@@ -206,9 +213,10 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
             return shares;
         };
         int64_t total = 0;
-        for (int64_t b = 0; b < nblocks; ++b) total += cost(tiles[b]);
-        int64_t lo = std::max<int64_t>(kFoldCostTiles + U, ceil_div(total, G_max)), hi = total;
-        while (lo < hi) {  // every budget >= kFoldCostTiles + U makes progress
+        for (int64_t b = 0; b < nblocks; ++b) total += cost(b, tiles[b], false);
+        const int64_t least = kFoldCost + kCutCost + kStreamTileCost * U;
+        int64_t lo = std::max<int64_t>(least, ceil_div(total, G_max)), hi = std::max(total, least);
+        while (lo < hi) {  // every budget >= least makes progress
             const int64_t mid = lo + (hi - lo) / 2;
             if (fill(mid, false) <= G_max)
                 hi = mid;

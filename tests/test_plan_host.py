@@ -146,16 +146,18 @@ def tiles_per_group(items):
 
 
 STEP_GROUP = 8        # tiles of one ring step group of a 4-wave workgroup (4 waves x 2)
-FOLD_COST = 6         # the planner's charge for one segment fold, in tiles
+FOLD_COST = 6         # the planner's charge for one segment fold, in tiles (decode-only step)
+CUT_COST = 4          # and for a piece of a block cut by a share boundary
 
 
 def cost_per_group(items):
-    """The planner's time estimate per workgroup: each piece's tiles rounded up to whole step
-    groups, plus one fold charge per piece."""
+    """The planner's time estimate per workgroup of a decode-only step: each piece's tiles
+    rounded up to whole step groups, plus one fold charge per piece and a cut charge per
+    piece of a block that was cut."""
     idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
     g = items[:, idx["group"]]
     t = -(-(items[:, idx["tok_end"]] - items[:, idx["tok_begin"]]) // 16)
-    c = STEP_GROUP * -(-t // STEP_GROUP) + FOLD_COST
+    c = STEP_GROUP * -(-t // STEP_GROUP) + FOLD_COST + CUT_COST * (items[:, idx["num_splits"]] > 1)
     return np.bincount(g, weights=c).astype(int)
 
 
@@ -174,10 +176,10 @@ def test_long_histories_are_spread_and_shares_are_balanced():
     assert len(tpg) == 256                      # one share per compute unit
     assert tpg.sum() == -(-b.kv_lens // 16).sum() * 2
     # equal estimated time: no share above the ideal average of whole blocks by more than
-    # one step group and one fold
+    # one step group, one fold and its two cut charges
     whole = (STEP_GROUP * -(-(-(-b.kv_lens // 16)) // STEP_GROUP) + FOLD_COST).sum() * 2
     cpg = cost_per_group(items)
-    assert cpg.max() <= -(-whole // 256) + STEP_GROUP + FOLD_COST
+    assert cpg.max() <= -(-whole // 256) + STEP_GROUP + FOLD_COST + 2 * CUT_COST
     # a block is cut only at multiples of a step group (its last piece takes the rest)
     t = -(-(items[:, idx["tok_end"]] - items[:, idx["tok_begin"]]) // 16)
     not_last = items[:, idx["tok_end"]] < items[:, idx["kv_len"]]
