@@ -1093,22 +1093,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
             ps.kv_head = lds_int(pd + 4 * PD_KV_HEAD);
             return ps;
         };
-        const bool m0 = lds_int((const lds_char *)&sm.last[0]) != 0;
-        const bool m1 = npend > 1 && lds_int((const lds_char *)&sm.last[1]) != 0;
-        if (m0 && m1) {
-            // Both: waves 0-1 merge the first piece's block and waves 2-3 the second's, side
-            // by side (the compute unit's vector-memory path is shared either way).
-            static_assert(NW == 4, "two halves of two waves");
-            const int t = threadIdx.x & 127;
-            const Seg ps = pend_seg(__builtin_amdgcn_readfirstlane(threadIdx.x >> 7));
-            if (ps.num_rows > kBlockRows / 2) {
-                constexpr int TPH = TPR / 2;
-                if (t / TPH < ps.num_rows) merge_pieces<DT, D, TPH, 8>(ps, a, t / TPH, t % TPH);
-            } else {
-                if (t / TPR < ps.num_rows) merge_pieces<DT, D, TPR, 16>(ps, a, t / TPR, t % TPR);
-            }
-        } else if (m0 || m1) {
-            const Seg ps = pend_seg(m0 ? 0 : 1);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (i >= npend || !lds_int((const lds_char *)&sm.last[i])) continue;
+            const Seg ps = pend_seg(i);
             if (ps.num_rows > kBlockRows / 2) {
                 const int r = threadIdx.x / TPR;
                 if (r < ps.num_rows) merge_pieces<DT, D, TPR, 8>(ps, a, r, threadIdx.x % TPR);
