@@ -314,8 +314,9 @@ fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, cons
     a.group_magic = h->group > 1 ? (uint32_t)(((1ull << 32) + h->group - 1) / h->group) : 0u;
     a.causal = h->causal;
     a.scale_log2 = h->scale_log2;
-    const int e = fl::launch_attention(h->cfg.dtype, h->cfg.head_dim, h->waves, p.num_groups, a,
-                                       stream);
+    // two workgroups per compute unit are chosen for steps bound by the per-tile arithmetic
+    const int e = fl::launch_attention(h->cfg.dtype, h->cfg.head_dim, h->waves,
+                                       p.groups_per_cu == 1, p.num_groups, a, stream);
     if (e != (int)hipSuccess) return hip_err((hipError_t)e, "attention launch");
     return FL_OK;
 }

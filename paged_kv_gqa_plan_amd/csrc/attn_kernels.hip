@@ -486,10 +486,11 @@ struct HalfTile {
     template <int PF>
     __device__ static const Frag &ring_frag(const Ring<PF> &r, int) { return r.f; }
     __device__ static void ring_release() { wait_lds(); }
-    // Refill a slot before its tile's arithmetic (the slot is free once the tile is in
-    // registers) where the arithmetic is long enough to hide the wait for the LDS reads:
-    // measured faster at head_dim 128, slower at 64.
-    static constexpr bool kEarlyRefill = D >= 128;
+    // A slot can be refilled before its tile's arithmetic (it is free once the tile is in
+    // registers); the launch chooses: at head_dim 128 always (the arithmetic hides the wait
+    // for the LDS reads), at 64 on memory-bound steps (saturated decode 6.92 -> 6.72 us) but
+    // not where the arithmetic bounds the step (ragged step 20.1 vs 20.8 us).
+    static constexpr bool kCanRefillEarly = true;
     // Issue the first tile ahead of the Q rows at the start: measured faster at head_dim
     // 128 (2-6%), slower at 64 (where the second tile then leaves later).
     static constexpr bool kTileFirst = D >= 128;
@@ -614,7 +615,7 @@ struct F32Tile {
     template <int PF>
     __device__ static const Frag &ring_frag(const Ring<PF> &r, int slot) { return r.buf[slot]; }
     __device__ static void ring_release() {}
-    static constexpr bool kEarlyRefill = false;
+    static constexpr bool kCanRefillEarly = false;  // a register slot is busy until the end
     static constexpr bool kTileFirst = false;
 
     __device__ static void load(Frag &f, const void *k, const void *v, int row0, int hkv, int col,
@@ -906,7 +907,7 @@ __device__ __forceinline__ void stage_rows(const lds_char *dst, const int32_t *r
 // The record and the pools come as separate leading arguments as well: those arrive in
 // SGPRs with the dispatch (kernel-argument preloading), so the record's loads go out at
 // once, beside the loads of the other arguments instead of after them.
-template <class T, int DT, int D, int NW>
+template <class T, int DT, int D, int NW, bool EARLY>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, const void *k_pool,
                                                       const void *v_pool, int hkv, const AttnArgs a) {
     static_assert(NW == 4 && NW <= kMaxWaves, "four waves per workgroup");
@@ -1042,13 +1043,14 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
             // An LDS slot is free once its tile is in registers: refill it before computing,
             // so the load's latency runs under the arithmetic. A register slot is free only
             // after the arithmetic.
-            if constexpr (T::kEarlyRefill) refill();
+            constexpr bool kEarly = T::kCanRefillEarly && EARLY;
+            if constexpr (kEarly) refill();
             if (j < ntile) {
                 const int t0 = cs.tok_begin + j * kTileTokens;
                 T::compute(T::ring_frag(ring, s), qc, t0, col, grp, cs.tok_end, ri.limit,
                            t0 + kTileTokens <= full_end, a.scale_log2, m_run, l_run, o);
             }
-            if constexpr (!T::kEarlyRefill) refill();
+            if constexpr (!kEarly) refill();
             __builtin_amdgcn_sched_barrier(0);
         });
     };
@@ -1118,30 +1120,36 @@ struct TileFor<FL_F32, D> {
     using type = F32Tile<D>;
 };
 
-template <int DT, int D, int NW>
+template <int DT, int D, int NW, bool EARLY>
 hipError_t launch_t(int n, const AttnArgs &a, hipStream_t s) {  // n: workgroups
     using T = typename TileFor<DT, D>::type;
-    hipLaunchKernelGGL((attn_kernel<T, DT, D, NW>), dim3(n), dim3(NW * 64), 0, s, a.wg_rec, a.k, a.v,
-                       a.num_kv_heads, a);
+    hipLaunchKernelGGL((attn_kernel<T, DT, D, NW, EARLY>), dim3(n), dim3(NW * 64), 0, s, a.wg_rec,
+                       a.k, a.v, a.num_kv_heads, a);
     return hipGetLastError();
 }
 
+// One instantiation where the refill point cannot vary: always early at head_dim 128,
+// never for fp32 (register ring).
 template <int DT, int D>
-hipError_t launch_w(int waves, int n, const AttnArgs &a, hipStream_t s) {
-    return waves == 4 ? launch_t<DT, D, 4>(n, a, s) : hipErrorInvalidValue;
+hipError_t launch_w(int waves, bool early, int n, const AttnArgs &a, hipStream_t s) {
+    if (waves != 4) return hipErrorInvalidValue;
+    if constexpr (DT == FL_F32) return launch_t<DT, D, 4, false>(n, a, s);
+    else if constexpr (D >= 128) return launch_t<DT, D, 4, true>(n, a, s);
+    else return early ? launch_t<DT, D, 4, true>(n, a, s) : launch_t<DT, D, 4, false>(n, a, s);
 }
 
 }  // namespace
 
-int launch_attention(int dtype, int head_dim, int waves, int n, const AttnArgs &a, void *stream) {
+int launch_attention(int dtype, int head_dim, int waves, bool early, int n, const AttnArgs &a,
+                     void *stream) {
     hipStream_t s = (hipStream_t)stream;
     switch (dtype * 1000 + head_dim) {
-    case FL_BF16 * 1000 + 64: return (int)launch_w<FL_BF16, 64>(waves, n, a, s);
-    case FL_BF16 * 1000 + 128: return (int)launch_w<FL_BF16, 128>(waves, n, a, s);
-    case FL_F16 * 1000 + 64: return (int)launch_w<FL_F16, 64>(waves, n, a, s);
-    case FL_F16 * 1000 + 128: return (int)launch_w<FL_F16, 128>(waves, n, a, s);
-    case FL_F32 * 1000 + 64: return (int)launch_w<FL_F32, 64>(waves, n, a, s);
-    case FL_F32 * 1000 + 128: return (int)launch_w<FL_F32, 128>(waves, n, a, s);
+    case FL_BF16 * 1000 + 64: return (int)launch_w<FL_BF16, 64>(waves, early, n, a, s);
+    case FL_BF16 * 1000 + 128: return (int)launch_w<FL_BF16, 128>(waves, early, n, a, s);
+    case FL_F16 * 1000 + 64: return (int)launch_w<FL_F16, 64>(waves, early, n, a, s);
+    case FL_F16 * 1000 + 128: return (int)launch_w<FL_F16, 128>(waves, early, n, a, s);
+    case FL_F32 * 1000 + 64: return (int)launch_w<FL_F32, 64>(waves, early, n, a, s);
+    case FL_F32 * 1000 + 128: return (int)launch_w<FL_F32, 128>(waves, early, n, a, s);
     default: return (int)hipErrorInvalidValue;
     }
 }

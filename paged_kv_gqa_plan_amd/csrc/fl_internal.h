@@ -94,6 +94,7 @@ struct Plan {
                                     // (page * P + slot) * Hkv + kv_head of the step's tile's
                                     // first key (padding steps repeat a real tile's row)
     int32_t num_groups = 0;
+    int32_t groups_per_cu = 1;      // workgroups per compute unit the shares were cut for
     int32_t num_segs = 0;
     int32_t num_merges = 0;
     int32_t max_splits = 0;
@@ -131,8 +132,10 @@ struct AttnArgs {
 };
 
 // Return hipSuccess or the launch error (as int to keep HIP headers out of this file).
-int launch_attention(int dtype, int head_dim, int waves, int num_groups, const AttnArgs &a,
-                     void *stream);
+// early_refill: refill a K/V slot as soon as its tile is in registers (memory-bound steps)
+// rather than after the tile's arithmetic (steps bound by the arithmetic).
+int launch_attention(int dtype, int head_dim, int waves, bool early_refill, int num_groups,
+                     const AttnArgs &a, void *stream);
 
 // Copy byte ranges [off, off + bytes) from pinned host memory to the same offsets of a
 // device buffer with one kernel (offsets 16-byte aligned, sizes multiples of 4).

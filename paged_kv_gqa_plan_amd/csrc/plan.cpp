@@ -179,6 +179,7 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         if (gpc <= 0) gpc = prefill && lim.head_dim <= 64 && lim.dtype != FL_F32 ? 2 : 1;
         const int64_t kFoldCost = prefill ? kFoldCostMixed : kFoldCostDecode;
         const int64_t kCutCost = prefill ? kCutCostMixed : kCutCostDecode;
+        out.groups_per_cu = gpc;
         const int64_t want = (int64_t)lim.num_cus * gpc;
         const int64_t G_max = std::min(std::max<int64_t>(1, std::min(want, ceil_div(T, lim.min_group_tiles))), T);
         const int64_t U = (int64_t)lim.waves * kRingDepth;
