@@ -173,6 +173,53 @@ def summarize_profiles(workload: str, kt: str, pf: str, pw: str, cf: str, cw: st
     print(json.dumps(d))
 
 
+SQ_PASS_A = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+             "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_INSTS_VALU")
+SQ_PASS_B = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
+             "SQ_ACTIVE_INST_VMEM", "SQ_INSTS_SALU", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_VMEM")
+# flops per MFMA instruction of the 16-bit path: per tile NC = D/32 instructions of 16x16x32
+# (16384 flops) and 2 * D/16 of 16x16x16 (8192 flops), the same 1:4 mix at d 64 and 128
+FLOPS_PER_MFMA_16BIT = (16384 + 4 * 8192) / 5
+
+
+def summarize_sq(workload: str, da: str, db: str, commands: str):
+    """Write profiles/sq_<workload>.md from two rocprofv3 --pmc passes of SQ counters."""
+    import workloads as W
+    b = W.WORKLOADS[workload]()
+    c = {}
+    for d, names in ((da, SQ_PASS_A), (db, SQ_PASS_B)):
+        for n in names:
+            c[n], nd = _counter_per_dispatch(d, "attn_kernel", n)
+    tp = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    tr = json.loads(open(tp).read()) if os.path.exists(tp) else None
+    wc = c["SQ_WAVE_CYCLES"]
+    frac = lambda n: c[n] / wc
+    lines = [f"# attention kernel, {workload}: SQ counters (rocprofv3 --pmc, two passes)", "",
+             "Commands (from the repository root on the GPU host):", "", "```", commands.strip(), "```", "",
+             "| counter | per dispatch |", "|---|---|"]
+    lines += [f"| {n} | {c[n]:.4g} |" for n in SQ_PASS_A + SQ_PASS_B]
+    lines += ["", "Fractions of wave time (SQ_WAVE_CYCLES, same units):", "",
+              f"* any instruction issuing: {frac('SQ_ACTIVE_INST_ANY'):.1%}",
+              f"* VALU issuing: {frac('SQ_ACTIVE_INST_VALU'):.1%}; LDS: {frac('SQ_ACTIVE_INST_LDS'):.1%}; "
+              f"scalar: {frac('SQ_ACTIVE_INST_SCA'):.1%}; vector memory: {frac('SQ_ACTIVE_INST_VMEM'):.1%}",
+              f"* waiting at s_waitcnt (SQ_WAIT_ANY): {frac('SQ_WAIT_ANY'):.1%}; "
+              f"waiting to issue (SQ_WAIT_INST_ANY): {frac('SQ_WAIT_INST_ANY'):.1%}",
+              f"* LDS bank-conflict cycles per LDS instruction: "
+              f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_INSTS_LDS'], 1):.2f}"]
+    if b.dtype != "f32":
+        mf = c["SQ_INSTS_MFMA"] * FLOPS_PER_MFMA_16BIT
+        lines += [f"* MFMA instructions: {c['SQ_INSTS_MFMA']:.4g} per dispatch, {mf / 1e9:.2f} GFLOP issued"]
+        if tr is not None:
+            us = tr["kernel_avg_us"]
+            lines += [f"* at the kernel-trace average of {us:.2f} us (profiles/traffic_{workload}.txt): "
+                      f"{mf / us / 1e6:.0f} TFLOP/s issued on MFMA, {mf / us / 1e6 / 2500:.1%} of the "
+                      f"2.5 PFLOP/s dense 16-bit peak"]
+    lines.append("")
+    with open(os.path.join(ROOT, "profiles", f"sq_{workload}.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines[-8:]))
+
+
 def copy_calibration(mib: int):
     """A plain device copy of known size (for scaling the HBM byte counters)."""
     import torch
@@ -205,10 +252,16 @@ def main(argv=None):
     ap.add_argument("--summarize-profiles", nargs=5, metavar=("KT", "PF", "PW", "CF", "CW"),
                     help="write profiles/ summaries from rocprofv3 CSV directories (kernel "
                          "trace; FETCH_SIZE and WRITE_SIZE of the bench; the same of a copy)")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("A", "B"),
+                    help="write profiles/sq_<workload>.md from two rocprofv3 --pmc CSV directories "
+                         "holding the SQ counter passes")
     ap.add_argument("--calib-mib", type=int, default=1024)
     ap.add_argument("--commands", default="", help="commands recorded in the summary")
     args = ap.parse_args(argv)
 
+    if args.summarize_sq:
+        summarize_sq(args.workload, *args.summarize_sq, args.commands)
+        return 0
     if args.summarize_profiles:
         summarize_profiles(args.workload, *args.summarize_profiles, args.calib_mib, args.commands)
         return 0
