@@ -9,11 +9,14 @@
 // Work layout. The plan gives each workgroup a contiguous share of all row blocks' tiles
 // (shares of equal estimated time): a list of segments (pieces of row blocks) whose tiles
 // the waves take round-robin across the whole share. Each tile's pool row was resolved by
-// the plan, so the loads need no page table and no segment state. Each wave keeps PF tiles
-// of K and V in flight in its own LDS ring, loaded straight into LDS with full-cache-line
-// loads and refilled as soon as a tile is consumed, across segment boundaries. Segment
-// headers, Q rows and windows of pool rows are staged into LDS the same way, ahead of
-// use. At each segment's end the waves fold their softmax states in LDS and write the
+// the plan, so the loads need no page table and no segment state. A workgroup starts from
+// its record (one line: the first segment, the share's bounds, each wave's first pool
+// rows). Each wave keeps PF tiles of K and V in flight in its own LDS ring, loaded
+// straight into LDS with full-cache-line loads and refilled, across segment boundaries,
+// as soon as a tile is in registers (memory-bound steps) or after its arithmetic (steps
+// the arithmetic bounds). Segment headers, Q rows and windows of pool rows are staged into
+// LDS the same way, ahead of use. At each segment's end the waves fold their softmax
+// states in LDS and write the
 // output rows, or, for a row block cut by a share boundary, fp32 partial rows. The piece
 // of a cut block that finishes last merges the partials by log-sum-exp.
 //
