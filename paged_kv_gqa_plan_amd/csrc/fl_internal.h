@@ -22,17 +22,23 @@ constexpr int kBlockRows = 16;
 #define FL_RING_DEPTH 2
 #endif
 constexpr int kRingDepth = FL_RING_DEPTH;
-// Planner's time estimate, in fifths of a streamed tile. A tile whose keys only its own
-// row block reads is streamed from memory (5); the tiles of a request with several row
-// blocks per kv head (a prefill chunk) are shared through the L2 cache (4: measured 0.098
-// vs 0.121 us per tile on a ragged mixed step). Each segment adds a fold (the cross-wave
+// Planner's time estimate, in hundredths of a streamed tile. A tile whose keys only its
+// own row block reads is streamed from memory (100); the tiles of a request with several
+// row blocks per kv head (a prefill chunk) are shared through the L2 cache (80: measured
+// 0.098 vs 0.121 us per tile on a ragged mixed step). Where every token row of the pool
+// spans whole 512-byte units, a kv head whose slice of the row lies in the odd 256-byte
+// half of a unit streams slower than one in the even half (long-context skew at head_dim
+// 128: 49.5 vs 43.4 us per workgroup for equal tiles; shifting the pools by 256 bytes
+// swaps which head is slow), so its tiles cost kOddHalfPercent more (chosen by A/B:
+// long-context skew 56.5 -> 55.4 us, mixed-length decode 13.6 -> 13.5 us). Each segment adds a fold (the cross-wave
 // merge of the softmax states at its end, with the padding of its last step group), and a
 // piece of a block cut by a share boundary adds its end-of-kernel merge ticket (and the
 // merge itself when it finishes last). Measured best: decode-only steps 6 and 4 tiles
 // (mixed-length decode 13.6 vs 14.5 us with 6 and 0), steps with a prefill chunk, whose
 // short decode blocks pack many segments into a share, 12 and 0 (ragged step 19.1 vs 19.7).
-constexpr int kStreamTileCost = 5;
-constexpr int kSharedTileCost = 4;
+constexpr int kStreamTileCost = 100;
+constexpr int kSharedTileCost = 80;
+constexpr int kOddHalfPercent = 20;
 #ifndef FL_FOLD_TILES_DECODE
 #define FL_FOLD_TILES_DECODE 6
 #endif

@@ -36,6 +36,7 @@ namespace {
 struct Block {
     int32_t req, kvh, row_begin, nrows, kv_end;
     int32_t tile_cost;  // kStreamTileCost, or kSharedTileCost when the request has several
+                        // blocks per kv head; tilted by the head's odd-half share
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -122,15 +123,28 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
 
 
     // ---- row blocks -------------------------------------------------------------------
+    // per kv head: the share of its row slice in odd 256-byte halves, in percent; 50 (no
+    // tilt) unless token rows span whole 512-byte units
+    const int64_t elem = lim.dtype == FL_F32 ? 4 : 2;
+    const int64_t slice = (int64_t)lim.head_dim * elem, row_bytes = slice * Hkv;
+    std::vector<int64_t> odd_pct(Hkv, 50);
+    if (row_bytes % 512 == 0)
+        for (int32_t h = 0; h < Hkv; ++h) {
+            int64_t odd = 0;
+            for (int64_t x = h * slice; x < (h + 1) * slice; x += 16) odd += (x / 256) & 1;
+            odd_pct[h] = 100 * odd / (slice / 16);
+        }
     std::vector<Block> blocks;
     for (int32_t r = 0; r < B; ++r) {
         const int32_t np = in.kv_indptr[r + 1] - in.kv_indptr[r];
         const int32_t kv_len = (np - 1) * P + in.last_page_len[r];
         const int32_t ql = in.qo_indptr ? in.qo_indptr[r + 1] - in.qo_indptr[r] : 1;
         const int32_t nflat = ql * G;
-        const int32_t tile_cost = nflat > kBlockRows ? kSharedTileCost : kStreamTileCost;
+        const int32_t base_cost = nflat > kBlockRows ? kSharedTileCost : kStreamTileCost;
         for (int32_t h = 0; h < Hkv; ++h)
             for (int32_t f0 = 0; f0 < nflat; f0 += kBlockRows) {
+                const int32_t tile_cost =
+                    (int32_t)(base_cost * (10000 + kOddHalfPercent * (odd_pct[h] - 50)) / 10000);
                 const int32_t nr = std::min(kBlockRows, nflat - f0);
                 const int32_t i_last = (f0 + nr - 1) / G;
                 const int32_t kv_end = in.causal ? kv_len - ql + i_last + 1 : kv_len;
@@ -215,7 +229,9 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         };
         int64_t total = 0;
         for (int64_t b = 0; b < nblocks; ++b) total += cost(b, tiles[b], false);
-        const int64_t least = kFoldCost + kCutCost + kStreamTileCost * U;
+        int64_t max_tile_cost = 0;
+        for (const Block &bl : blocks) max_tile_cost = std::max<int64_t>(max_tile_cost, bl.tile_cost);
+        const int64_t least = kFoldCost + kCutCost + max_tile_cost * U;
         int64_t lo = std::max<int64_t>(least, ceil_div(total, G_max)), hi = std::max(total, least);
         while (lo < hi) {  // every budget >= least makes progress
             const int64_t mid = lo + (hi - lo) / 2;

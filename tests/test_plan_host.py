@@ -192,6 +192,31 @@ def test_long_histories_are_spread_and_shares_are_balanced():
         assert (items[inner, idx["num_splits"]] == 1).all()
 
 
+def test_odd_half_kv_heads_get_smaller_shares():
+    # d 128 fp16 with 2 kv heads: a token row is 512 bytes and kv head 1 reads its odd
+    # 256-byte half, which streams slower; the plan gives its shares fewer tiles
+    lens = np.full(8, 32768, np.int32)
+    b = W.make_batch(lens, num_qo_heads=12, num_kv_heads=2, head_dim=128, page_size=256,
+                     dtype="f16", num_pages=1100, poison=False)
+    h = host_handle(Hq=12, Hkv=2, D=128, P=256, dtype="f16", max_pages=4096, num_cus=256)
+    items = plan_batch(h, b)
+    idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
+    t = -(-(items[:, idx["tok_end"]] - items[:, idx["tok_begin"]]) // 16)
+    whole = items[:, idx["num_splits"]] > 2  # interior pieces of the long blocks
+    head = items[:, idx["kv_head"]]
+    m0, m1 = np.median(t[whole & (head == 0)]), np.median(t[whole & (head == 1)])
+    assert 1.15 < m0 / m1 < 1.30, (m0, m1)
+    # with d 64 the rows are 256 bytes, each head's slice spans both halves: no tilt
+    b2 = W.make_batch(lens, num_qo_heads=12, num_kv_heads=2, head_dim=64, page_size=256,
+                      dtype="f16", num_pages=1100, poison=False)
+    h2 = host_handle(Hq=12, Hkv=2, D=64, P=256, dtype="f16", max_pages=4096, num_cus=256)
+    it2 = plan_batch(h2, b2)
+    t2 = -(-(it2[:, idx["tok_end"]] - it2[:, idx["tok_begin"]]) // 16)
+    w2 = it2[:, idx["num_splits"]] > 2
+    hd2 = it2[:, idx["kv_head"]]
+    assert np.median(t2[w2 & (hd2 == 0)]) == np.median(t2[w2 & (hd2 == 1)])
+
+
 def test_decode_batch_of_equal_histories_is_not_split():
     b = W.saturated_decode()
     h = host_handle(num_cus=256)
