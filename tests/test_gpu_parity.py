@@ -83,6 +83,35 @@ def test_variants(v, ragged):
     _check(b, what=f"variant-{v}-ragged{ragged}")
 
 
+def _random_case(seed):
+    """A seeded random configuration: dtype, head_dim, page size, heads, a batch of lengths
+    mixing short, tile- and page-aligned and long histories, some prefill chunks, the mask
+    and a forced slice count."""
+    r = np.random.default_rng(1000 + seed)
+    dtype = ["bf16", "f16", "f32"][r.integers(3)]
+    D = [64, 128][r.integers(2)]
+    P = [16, 32, 64, 128, 256][r.integers(5)]
+    Hq, Hkv = [(14, 2), (12, 2), (8, 1), (4, 4), (32, 4), (6, 3)][r.integers(6)]
+    B = int(r.integers(1, 25))
+    kinds = r.integers(4, size=B)
+    kv = np.where(kinds == 0, r.integers(1, 40, size=B),
+         np.where(kinds == 1, 16 * r.integers(1, 40, size=B),
+         np.where(kinds == 2, P * r.integers(1, 6, size=B), r.integers(40, 3000, size=B))))
+    qo = np.where(r.random(B) < 0.25, np.minimum(kv, r.integers(2, 80, size=B)), 1)
+    causal = bool(r.random() < 0.8)
+    splits = int([0, 0, 0, 1, 2, 5][r.integers(6)])
+    b = W.make_batch(kv.tolist(), qo.tolist(), num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                     page_size=P, dtype=dtype, seed=seed, causal=causal,
+                     num_pages=int(sum(-(-k // P) for k in kv)) + 3)
+    return b, splits
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configurations(seed):
+    b, splits = _random_case(seed)
+    _check(b, num_splits=splits, what=f"random-{seed}")
+
+
 def test_fp32_long_context_skew_reduced():
     b = W.make_batch(W.long_context_lengths(0, long_len=8192), num_qo_heads=12, num_kv_heads=2,
                      head_dim=128, page_size=256, dtype="f32", seed=0)
