@@ -8,6 +8,8 @@ arrays from ``workloads``.
 The arithmetic lives in ``paged_attn_oracle.c`` (plain C, double precision): a gather of
 each request's pages into dense K/V followed by plain softmax attention, plus an optional
 split-and-merge mode. ``attention(batch)`` returns unrounded fp64 results.
+``kv_append(...)`` writes a step's new K/V rows into copies of the pools (a byte copy to
+each new token's page slot).
 """
 from __future__ import annotations
 
@@ -54,6 +56,11 @@ def load(path: Optional[str] = None):
         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     lib.oracle_decode.restype = ctypes.c_int
     lib.oracle_decode.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.oracle_paged_kv_append.restype = ctypes.c_int
+    lib.oracle_paged_kv_append.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     if path is None or path == _LIB_OVERRIDE:
@@ -107,6 +114,41 @@ def attention(batch, num_splits: int = 1, num_threads: int = 0, lib=None):
                            batch.num_kv_heads, batch.head_dim, batch.page_size, batch.q,
                            batch.k_pool, batch.v_pool, batch.causal, batch.sm_scale, num_splits,
                            num_threads, lib=lib)
+
+
+def paged_kv_append(elem_bytes: int, qo_indptr, kv_indptr, kv_indices, last_page_len,
+                    num_pages: int, num_kv_heads: int, head_dim: int, page_size: int,
+                    k_new, v_new, k_pool, v_pool, lib=None):
+    """Raw entry: returns new (k_pool, v_pool) arrays with the rows of k_new / v_new
+    ``[rows, Hkv, D]`` written to their tokens' page slots; the inputs are not modified."""
+    lib = lib or load()
+    kv_indptr = np.ascontiguousarray(kv_indptr, dtype=np.int32)
+    kv_indices = np.ascontiguousarray(kv_indices, dtype=np.int32)
+    last_page_len = np.ascontiguousarray(last_page_len, dtype=np.int32)
+    B = int(kv_indptr.shape[0]) - 1
+    if qo_indptr is not None:
+        qo_indptr = np.ascontiguousarray(qo_indptr, dtype=np.int32)
+    k_out = np.array(k_pool, copy=True, order="C")
+    v_out = np.array(v_pool, copy=True, order="C")
+    k_new = np.ascontiguousarray(k_new)
+    v_new = np.ascontiguousarray(v_new)
+    rc = lib.oracle_paged_kv_append(
+        int(elem_bytes), B, _ptr(qo_indptr), _ptr(kv_indptr), _ptr(kv_indices),
+        _ptr(last_page_len), int(num_pages), int(num_kv_heads), int(head_dim), int(page_size),
+        _ptr(k_new), _ptr(v_new), _ptr(k_out), _ptr(v_out))
+    if rc != 0:
+        raise OracleError(f"oracle_paged_kv_append returned {rc}")
+    return k_out, v_out
+
+
+def kv_append(batch, k_new, v_new, k_pool=None, v_pool=None, lib=None):
+    """Oracle append for a ``workloads.Batch``'s page table and query rows: the new rows go
+    into copies of ``k_pool`` / ``v_pool`` (default: the batch's own pools)."""
+    return paged_kv_append(batch.elem_bytes, batch.qo_indptr, batch.kv_indptr, batch.kv_indices,
+                           batch.last_page_len, batch.num_pages, batch.num_kv_heads,
+                           batch.head_dim, batch.page_size, k_new, v_new,
+                           batch.k_pool if k_pool is None else k_pool,
+                           batch.v_pool if v_pool is None else v_pool, lib=lib)
 
 
 def decode(dtype_code: int, values: np.ndarray, lib=None) -> np.ndarray:

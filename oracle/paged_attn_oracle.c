@@ -268,3 +268,67 @@ int oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Appending the new tokens' K/V to the paged cache (flashlet README, design bullets:
+ * set_kv writes the step's new K and V rows into the NHD pool in place, before
+ * attention reads it).
+ *
+ * Request r's query rows qo_indptr[r] .. qo_indptr[r+1] are its newest qo_len tokens,
+ * so query row i of the request is logical token kv_len - qo_len + i (the same position
+ * the bottom-right causal mask gives it). Its K row k_new[qo_indptr[r] + i, :, :]
+ * (all kv heads, head_dim values each) is copied byte for byte into page
+ * kv_indices[kv_indptr[r] + pos / P], slot pos % P of k_pool; likewise V. Nothing else
+ * in the pools changes. Rows are copied as raw bytes (elem_bytes per value), so the
+ * result is exact for every storage type.
+ *
+ * Returns 0, or a negative code (pools untouched) when the metadata is inconsistent:
+ * a request with more new rows than cached tokens, or a page id outside the pool.
+ */
+int oracle_paged_kv_append(int elem_bytes, int batch, const int32_t *qo_indptr,
+                           const int32_t *kv_indptr, const int32_t *kv_indices,
+                           const int32_t *last_page_len, int64_t num_pages,
+                           int num_kv_heads, int head_dim, int page_size,
+                           const void *k_new, const void *v_new, void *k_pool, void *v_pool)
+{
+    if ((elem_bytes != 2 && elem_bytes != 4) || batch < 0 || num_kv_heads <= 0 ||
+        head_dim <= 0 || page_size <= 0)
+        return ORACLE_BAD_ARG;
+    if (batch == 0)
+        return ORACLE_OK;
+    if (!kv_indptr || !kv_indices || !last_page_len || !k_pool || !v_pool)
+        return ORACLE_BAD_ARG;
+    if (kv_indptr[0] != 0 || (qo_indptr && qo_indptr[0] != 0))
+        return ORACLE_BAD_ARG;
+    const int P = page_size;
+    const size_t token_bytes = (size_t)num_kv_heads * head_dim * elem_bytes;
+    for (int r = 0; r < batch; ++r) {
+        int np_ = kv_indptr[r + 1] - kv_indptr[r];
+        int qlen = qo_indptr ? qo_indptr[r + 1] - qo_indptr[r] : 1;
+        if (np_ < 1 || qlen < 0 || last_page_len[r] < 1 || last_page_len[r] > P)
+            return ORACLE_BAD_ARG;
+        int64_t kv_len = (int64_t)(np_ - 1) * P + last_page_len[r];
+        if (qlen > kv_len)
+            return ORACLE_BAD_ARG;
+        if (qlen > 0 && (!k_new || !v_new))
+            return ORACLE_BAD_ARG;
+        for (int j = kv_indptr[r]; j < kv_indptr[r + 1]; ++j)
+            if (kv_indices[j] < 0 || kv_indices[j] >= num_pages)
+                return ORACLE_BAD_ARG;
+    }
+    for (int r = 0; r < batch; ++r) {
+        const int np_ = kv_indptr[r + 1] - kv_indptr[r];
+        const int kv_len = (np_ - 1) * P + last_page_len[r];
+        const int row0 = qo_indptr ? qo_indptr[r] : r;
+        const int qlen = qo_indptr ? qo_indptr[r + 1] - qo_indptr[r] : 1;
+        for (int i = 0; i < qlen; ++i) {
+            const int pos = kv_len - qlen + i;
+            const int64_t page = kv_indices[kv_indptr[r] + pos / P];
+            const size_t dst = ((size_t)page * P + (size_t)(pos % P)) * token_bytes;
+            const size_t src = (size_t)(row0 + i) * token_bytes;
+            memcpy((char *)k_pool + dst, (const char *)k_new + src, token_bytes);
+            memcpy((char *)v_pool + dst, (const char *)v_new + src, token_bytes);
+        }
+    }
+    return ORACLE_OK;
+}

@@ -32,6 +32,16 @@ MUTANTS = {
     "last_key_dropped": ("for (int t = t0; t < t1; ++t) {\n        double p",
                          "for (int t = t0; t < t1 - 1; ++t) {\n        double p"),
     "f16_exponent_bias": ("v = ldexp((double)(f | 0x400), e - 25);", "v = ldexp((double)(f | 0x400), e - 24);"),
+    # appending new K/V rows
+    "append_top_left_positions": ("const int pos = kv_len - qlen + i;", "const int pos = i;"),
+    "append_slot_off_by_one": ("((size_t)page * P + (size_t)(pos % P)) * token_bytes",
+                               "((size_t)page * P + (size_t)((pos + 1) % P)) * token_bytes"),
+    "append_page_ignores_request": ("const int64_t page = kv_indices[kv_indptr[r] + pos / P];",
+                                    "const int64_t page = kv_indices[pos / P];"),
+    "append_rows_ignore_request": ("const size_t src = (size_t)(row0 + i) * token_bytes;",
+                                   "const size_t src = (size_t)i * token_bytes;"),
+    "append_k_v_swapped": ("memcpy((char *)v_pool + dst, (const char *)v_new + src, token_bytes);",
+                           "memcpy((char *)v_pool + dst, (const char *)k_new + src, token_bytes);"),
 }
 
 

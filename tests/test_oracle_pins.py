@@ -360,3 +360,85 @@ def test_generator_is_deterministic_and_poisons_unused_slots():
             used[pages[t // 16], t % 16] = True
     vals = W.storage_to_f32(a.k_pool, "bf16")
     assert np.isnan(vals[~used]).all() and np.isfinite(vals[used]).all()
+
+
+# ---------------------------------------------------------------------------------------
+# appending a step's new K/V rows to the paged cache
+# ---------------------------------------------------------------------------------------
+def as_bytes(a):
+    return np.ascontiguousarray(a).view(np.uint8)
+
+
+APPEND_CASES = [
+    dict(kv=[1, 17, 100, 300], Hkv=2, D=64, P=16, dtype="bf16"),
+    dict(kv=[16, 17, 64, 65, 300], Hkv=2, D=128, P=64, dtype="f16"),
+    dict(kv=[3, 256, 257, 600], Hkv=1, D=64, P=256, dtype="f32"),
+    dict(kv=[80, 17, 33, 5], qo=[37, 1, 0, 5], Hkv=2, D=64, P=16, dtype="bf16"),  # ragged, empty
+    dict(kv=[50, 20], qo=[50, 1], Hkv=8, D=64, P=16, dtype="f16"),                # whole history
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES,
+                         ids=lambda c: f"{c['dtype']}-Hkv{c['Hkv']}-D{c['D']}-P{c['P']}-{'ragged' if 'qo' in c else 'decode'}")
+def test_append_restores_the_generator_pools(case):
+    """The generator scatters every request's whole history; with the newest qo_len tokens
+    taken out (poisoned) and given as new rows, the append must rebuild the same pools, byte
+    for byte, NaN slots included."""
+    b = W.make_batch(case["kv"], case.get("qo"), num_qo_heads=case["Hkv"] * 2,
+                     num_kv_heads=case["Hkv"], head_dim=case["D"], page_size=case["P"],
+                     dtype=case["dtype"], num_pages=sum(-(-k // case["P"]) for k in case["kv"]) + 4,
+                     seed=21, keep_dense=True)
+    st = W.append_step(b)
+    assert not np.array_equal(as_bytes(st.k_before), as_bytes(b.k_pool))
+    k, v = oracle.kv_append(b, st.k_new, st.v_new, st.k_before, st.v_before)
+    assert np.array_equal(as_bytes(k), as_bytes(b.k_pool))
+    assert np.array_equal(as_bytes(v), as_bytes(b.v_pool))
+
+
+def test_append_writes_the_slots_worked_out_by_hand():
+    """Three requests on a pool of 4 pages of 16 slots, one kv head, head_dim 64, fp32.
+      r0: pages [2, 0], last_page_len 1  -> kv_len 17, its one new token is token 16:
+          page 0, slot 0 (the first slot of its second page)
+      r1: pages [3],    last_page_len 16 -> kv_len 16, new token 15: page 3, slot 15
+      r2: pages [1],    last_page_len 5, 3 new rows -> tokens 2, 3, 4: page 1, slots 2-4
+    Every other slot keeps its old value."""
+    qo_indptr = np.array([0, 1, 2, 5], np.int32)
+    kv_indptr = np.array([0, 2, 3, 4], np.int32)
+    kv_indices = np.array([2, 0, 3, 1], np.int32)
+    last = np.array([1, 16, 5], np.int32)
+    rng = np.random.default_rng(3)
+    k_pool = rng.standard_normal((4, 16, 1, 64)).astype(np.float32)
+    v_pool = rng.standard_normal((4, 16, 1, 64)).astype(np.float32)
+    k_new = (1000 + np.arange(5, dtype=np.float32))[:, None, None] * np.ones((5, 1, 64), np.float32)
+    v_new = -k_new
+    k, v = oracle.paged_kv_append(4, qo_indptr, kv_indptr, kv_indices, last, 4, 1, 64, 16,
+                                  k_new, v_new, k_pool, v_pool)
+    expect_k, expect_v = k_pool.copy(), v_pool.copy()
+    for row, (page, slot) in enumerate([(0, 0), (3, 15), (1, 2), (1, 3), (1, 4)]):
+        expect_k[page, slot] = 1000 + row
+        expect_v[page, slot] = -(1000 + row)
+    assert np.array_equal(k, expect_k) and np.array_equal(v, expect_v)
+
+
+def test_append_then_attention_matches_the_full_history():
+    b = W.make_batch([80, 17, 33], [37, 1, 1], num_qo_heads=14, num_kv_heads=2, head_dim=64,
+                     page_size=16, dtype="bf16", seed=22, keep_dense=True)
+    st = W.append_step(b)
+    k, v = oracle.kv_append(b, st.k_new, st.v_new, st.k_before, st.v_before)
+    out_full, lse_full = oracle.attention(b)
+    out, lse = oracle.attention(dataclasses.replace(b, k_pool=k, v_pool=v))
+    assert np.array_equal(out, out_full) and np.array_equal(lse, lse_full)
+
+
+def test_append_rejects_bad_metadata():
+    b = W.tiny_decode(keep_dense=True)
+    st = W.append_step(b)
+
+    def run(qo=b.qo_indptr, kvi=b.kv_indices):
+        return oracle.paged_kv_append(2, qo, b.kv_indptr, kvi, b.last_page_len, b.num_pages, 2, 64,
+                                      16, st.k_new, st.v_new, st.k_before, st.v_before)
+    with pytest.raises(oracle.OracleError):
+        run(qo=np.array([0, 2, 3, 4, 5], np.int32))      # 2 new rows on a 1-token history
+    bad = b.kv_indices.copy(); bad[0] = -1
+    with pytest.raises(oracle.OracleError):
+        run(kvi=bad)

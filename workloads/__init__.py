@@ -220,6 +220,45 @@ def make_batch(kv_lens: Sequence[int], qo_lens: Optional[Sequence[int]] = None, 
                  qo_lens=qo_lens, seed=seed, cfg_id=cfg_id, dense_k=dk, dense_v=dv)
 
 
+@dataclass
+class AppendStep:
+    """A step's new K/V rows and the pools as they were before the step.
+
+    The batch's pools hold every request's whole history; here the newest qo_len tokens
+    of each request (the tokens its query rows stand for) are taken out of them:
+    ``k_new`` / ``v_new`` ``[rows, Hkv, D]`` hold those tokens in query-row order and
+    ``k_before`` / ``v_before`` are the pools with their slots poisoned. Writing the new
+    rows back gives the batch's pools again."""
+    k_new: np.ndarray
+    v_new: np.ndarray
+    k_before: np.ndarray
+    v_before: np.ndarray
+
+
+def append_step(b: Batch) -> AppendStep:
+    """Split a batch made with ``keep_dense=True`` into pools before the step and new rows."""
+    if b.dense_k is None:
+        raise ValueError("append_step needs a batch made with keep_dense=True")
+    if np.any(b.qo_lens > b.kv_lens):
+        raise ValueError("every request needs qo_len <= kv_len")
+    pre = (b.kv_lens - b.qo_lens).astype(np.int64)
+    sd = storage_np_dtype(b.dtype)
+    fill = poison_value(b.dtype)
+    shape = b.k_pool.shape
+    k_before = np.full(shape, fill, dtype=sd)
+    v_before = np.full(shape, fill, dtype=sd)
+    k_old = np.concatenate([k[:n] for k, n in zip(b.dense_k, pre)])
+    v_old = np.concatenate([v[:n] for v, n in zip(b.dense_v, pre)])
+    scatter_tokens(k_before, k_old, b.kv_indptr, b.kv_indices, pre, b.page_size)
+    scatter_tokens(v_before, v_old, b.kv_indptr, b.kv_indices, pre, b.page_size)
+    tail = [(k[n:], v[n:]) for k, v, n in zip(b.dense_k, b.dense_v, pre)]
+    empty = np.zeros((0, b.num_kv_heads, b.head_dim), dtype=sd)
+    k_new = np.concatenate([t[0] for t in tail] + [empty])
+    v_new = np.concatenate([t[1] for t in tail] + [empty])
+    return AppendStep(k_new=np.ascontiguousarray(k_new), v_new=np.ascontiguousarray(v_new),
+                      k_before=k_before, v_before=v_before)
+
+
 def relabel_pages(b: Batch, perm: np.ndarray) -> Batch:
     """The same logical batch with physical page p moved to ``perm[p]``."""
     perm = np.asarray(perm, dtype=np.int64)
