@@ -98,6 +98,41 @@ def cpu_baseline(b, gpu_out0, budget_s: float):
             "gpu_vs_oracle_max_abs": err}
 
 
+def time_kv_append(h, b, ks, vs, L: int, stream, replays: int = 20):
+    """The KV append of the same step: each layer's new K/V rows ([rows, Hkv, D], seeded
+    device data) written into that layer's pools by one launch, the L launches captured in
+    one HIP graph. Timed after the attention measurement (it overwrites the new tokens'
+    slots). Bytes: the new rows read plus the same bytes written, for K and V."""
+    import torch
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(7)
+    shape = (b.rows, b.num_kv_heads, b.head_dim)
+    kn = [torch.randn(shape, dtype=ks[0].dtype, device="cuda:0", generator=gen) for _ in range(L)]
+    vn = [torch.randn(shape, dtype=ks[0].dtype, device="cuda:0", generator=gen) for _ in range(L)]
+    for l in range(L):
+        h.append(kn[l], vn[l], ks[l], vs[l])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for l in range(L):
+            h.append(kn[l], vn[l], ks[l], vs[l])
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(replays)]
+    for a, e in ev:
+        a.record(stream)
+        g.replay()
+        e.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(e) / L * 1e3 for a, e in ev)
+    us_med = us[len(us) // 2]
+    nbytes = b.rows * b.num_kv_heads * b.head_dim * b.elem_bytes * 2 * 2
+    return {"us_per_call_median": round(us_med, 3), "bytes_per_call": nbytes,
+            "GB_per_s": round(nbytes / (us_med * 1e-6) / 1e9, 2), "rows": b.rows,
+            "launch": "hip_graph", "layers": L}
+
+
 def _csv_rows(path):
     import csv
     with open(path, newline="") as f:
@@ -395,6 +430,7 @@ def main(argv=None):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
     }
+    res["kv_append"] = time_kv_append(h, b, ks, vs, L, stream)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(b, outs[0], args.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -144,6 +144,42 @@ fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, cons
                             void *out, float *lse, void *stream);
 
 /*
+ * Append one layer's new K and V rows to the paged pools with the current plan, before
+ * that layer's run() reads them (flashlet README, design bullets: set_kv writes the new
+ * tokens into the NHD pool in place with one indexed copy; the pool keeps every layer's
+ * pages in the same layout). One kernel launch.
+ *
+ * Query row i of request r (global row qo_indptr[r] + i) stands for the request's token
+ * kv_len[r] - qo_len[r] + i, the position the causal mask gives it: the kv_len passed to
+ * plan() already counts the step's new tokens. That token lives in page
+ * kv_indices[kv_indptr[r] + t / page_size], slot t % page_size. Its K row
+ *     k_pool[page, slot, :, :] = k_new[qo_indptr[r] + i, :, :]
+ * and likewise for V; every other slot of the pools is left as it was. The copy moves
+ * bytes, so it is exact for every element type.
+ * Device pointers:
+ *   k_new, v_new    [rows, num_kv_heads, head_dim], rows = qo_indptr[batch] of the plan
+ *   k_pool, v_pool  [num_pages, page_size, num_kv_heads, head_dim], one layer
+ * All pointers 16-byte aligned; the element type is the handle's fl_dtype. Enqueues on
+ * `stream` and returns; never synchronises or allocates (graph-capturable).
+ * Errors: FL_ERR_NOT_PLANNED before a successful plan; FL_ERR_INVALID_ARG when a request
+ * of the plan has more query rows than cached tokens (possible without the causal mask),
+ * when two rows would write the same slot (a new token in a page two requests share), or
+ * for NULL or misaligned pointers; FL_ERR_UNSUPPORTED on a host-only handle, or when
+ * rows x (token row bytes / 16) reaches 2^31. A plan of zero rows makes this a no-op.
+ */
+fl_status fl_paged_kv_append(fl_handle h, const void *k_new, const void *v_new, void *k_pool,
+                             void *v_pool, void *stream);
+
+/*
+ * Copy the current plan's append destinations to host memory: for each query row, the
+ * token row page * page_size + slot that fl_paged_kv_append writes it to. *num_rows
+ * receives the row count; at most `capacity` entries are written. Works on host-only
+ * handles. FL_ERR_INVALID_ARG (with the reason) when the plan has no valid slots.
+ */
+fl_status fl_paged_kv_append_slots(fl_handle h, int32_t *slots, int32_t capacity,
+                                   int32_t *num_rows);
+
+/*
  * Facts about the current plan: the number of work items (segments, see below), the
  * number of workgroups of the attention launch, the largest number of pieces any row block
  * was cut into, and the fp32 partial-result bytes the plan uses. Outputs may be NULL.

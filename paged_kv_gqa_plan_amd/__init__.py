@@ -48,8 +48,9 @@ class FlError(RuntimeError):
 
 
 EXPORTED = ("fl_paged_attn_create", "fl_paged_attn_destroy", "fl_paged_attn_plan",
-            "fl_paged_attn_run", "fl_paged_attn_plan_info", "fl_paged_attn_get_work_items",
-            "fl_last_error")
+            "fl_paged_attn_run", "fl_paged_kv_append", "fl_paged_kv_append_slots",
+            "fl_paged_attn_plan_info",
+            "fl_paged_attn_get_work_items", "fl_last_error")
 
 _lib = None
 
@@ -69,6 +70,8 @@ def load_library(path: Optional[str] = None):
     lib.fl_paged_attn_destroy.argtypes = [vp]
     lib.fl_paged_attn_plan.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, ctypes.c_float, i32, vp]
     lib.fl_paged_attn_run.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.fl_paged_kv_append.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.fl_paged_kv_append_slots.argtypes = [vp, vp, i32, ctypes.POINTER(i32)]
     lib.fl_paged_attn_plan_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                             ctypes.POINTER(i32), ctypes.POINTER(i64)]
     lib.fl_paged_attn_get_work_items.argtypes = [vp, vp, i32, ctypes.POINTER(i32)]
@@ -128,6 +131,27 @@ def fl_paged_attn_run(h, q: int, k_pool: int, v_pool: int, out: int, lse: Option
                                             ctypes.c_void_p(v_pool), ctypes.c_void_p(out),
                                             ctypes.c_void_p(lse or 0), ctypes.c_void_p(int(stream))),
            "fl_paged_attn_run")
+
+
+def fl_paged_kv_append(h, k_new: int, v_new: int, k_pool: int, v_pool: int,
+                       stream: int = 0) -> None:
+    """Device pointers as integers: the plan's query rows' new K/V rows go to their tokens'
+    page slots of one layer's pools."""
+    _check(load_library().fl_paged_kv_append(h, ctypes.c_void_p(k_new), ctypes.c_void_p(v_new),
+                                             ctypes.c_void_p(k_pool), ctypes.c_void_p(v_pool),
+                                             ctypes.c_void_p(int(stream))),
+           "fl_paged_kv_append")
+
+
+def fl_paged_kv_append_slots(h) -> np.ndarray:
+    """The current plan's append destinations: int32 token row (page * P + slot) per query row."""
+    lib = load_library()
+    n = ctypes.c_int32()
+    _check(lib.fl_paged_kv_append_slots(h, None, 0, ctypes.byref(n)), "fl_paged_kv_append_slots")
+    buf = np.zeros(max(n.value, 1), dtype=np.int32)
+    _check(lib.fl_paged_kv_append_slots(h, _p(buf), n.value, ctypes.byref(n)),
+           "fl_paged_kv_append_slots")
+    return buf[:n.value]
 
 
 def fl_paged_attn_plan_info(h) -> Tuple[int, int, int, int]:
@@ -197,6 +221,13 @@ class PagedAttention:
         fl_paged_attn_run(self.handle, q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                           out.data_ptr(), None if lse is None else lse.data_ptr(),
                           self._stream(stream))
+
+    def append(self, k_new, v_new, k_pool, v_pool, stream=None):
+        fl_paged_kv_append(self.handle, k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
+                           v_pool.data_ptr(), self._stream(stream))
+
+    def append_slots(self) -> np.ndarray:
+        return fl_paged_kv_append_slots(self.handle)
 
     def info(self):
         return fl_paged_attn_plan_info(self.handle)

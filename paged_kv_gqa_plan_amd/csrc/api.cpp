@@ -48,10 +48,11 @@ struct fl_paged_attn {
     int32_t log2_page = 0;
 
     // device buffers
-    char *d_meta = nullptr;      // [segments | workgroup records | merge tickets | step rows]
+    char *d_meta = nullptr;      // [segments | workgroup records | merge tickets | step rows |
+                                 //  append slots]
     float *d_part_o = nullptr;   // [part_rows_cap, head_dim]
     float *d_part_lse = nullptr; // [part_rows_cap]
-    int64_t off_wg_rec = 0, off_tickets = 0, off_steps = 0, meta_bytes = 0;
+    int64_t off_wg_rec = 0, off_tickets = 0, off_steps = 0, off_append = 0, meta_bytes = 0;
     int32_t waves = 4;
 
     // pinned staging, double-buffered
@@ -192,7 +193,8 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
     h->off_wg_rec = align_up(L.seg_cap * FL_WORK_ITEM_INTS * 4, 256);
     h->off_tickets = align_up(h->off_wg_rec + L.group_cap * fl::kRecInts * 4, 256);
     h->off_steps = align_up(h->off_tickets + blocks * 4, 256);
-    h->meta_bytes = align_up(h->off_steps + std::max<int64_t>(1, L.max_tiles) * 4, 256);
+    h->off_append = align_up(h->off_steps + std::max<int64_t>(1, L.max_tiles) * 4, 256);
+    h->meta_bytes = align_up(h->off_append + std::max<int64_t>(1, cfg->max_qo_rows) * 4, 256);
 
     if (!h->host_only) {
         hipError_t e;
@@ -268,10 +270,12 @@ fl_status fl_paged_attn_plan(fl_handle h, int32_t batch, const int32_t *qo_indpt
         std::memcpy(st_buf, p.segs.data(), p.segs.size() * 4);
         std::memcpy(st_buf + h->off_wg_rec, p.wg_rec.data(), p.wg_rec.size() * 4);
         std::memcpy(st_buf + h->off_steps, p.step_rows.data(), p.step_rows.size() * 4);
+        const int64_t append_bytes = p.append_ok ? (int64_t)p.append_rows.size() * 4 : 0;
+        if (append_bytes) std::memcpy(st_buf + h->off_append, p.append_rows.data(), append_bytes);
         fl::StageCopy sc{h->d_stage[slot], h->d_meta,
-                         {0, h->off_wg_rec, h->off_steps},
+                         {0, h->off_wg_rec, h->off_steps, h->off_append},
                          {(int64_t)p.segs.size() * 4, (int64_t)p.wg_rec.size() * 4,
-                          (int64_t)p.step_rows.size() * 4}};
+                          (int64_t)p.step_rows.size() * 4, append_bytes}};
         hipStream_t s = (hipStream_t)stream;
         if ((e = (hipError_t)fl::launch_stage_copy(sc, s)) != hipSuccess)
             return hip_err(e, "plan metadata copy");
@@ -318,6 +322,46 @@ fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, cons
     const int e = fl::launch_attention(h->cfg.dtype, h->cfg.head_dim, h->waves,
                                        p.groups_per_cu == 1, p.num_groups, a, stream);
     if (e != (int)hipSuccess) return hip_err((hipError_t)e, "attention launch");
+    return FL_OK;
+}
+
+fl_status fl_paged_kv_append(fl_handle h, const void *k_new, const void *v_new, void *k_pool,
+                             void *v_pool, void *stream) {
+    g_last_error.clear();
+    if (!h) return set_err(FL_ERR_INVALID_ARG, "handle is NULL");
+    if (h->host_only) return set_err(FL_ERR_UNSUPPORTED, "append on a host-only handle");
+    if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "append before a successful plan()");
+    const Plan &p = h->plan;
+    if (!p.append_ok) return set_err(FL_ERR_INVALID_ARG, "the plan has no append slots: " + p.append_err);
+    const int64_t rows = (int64_t)p.append_rows.size();
+    if (rows == 0) return FL_OK;
+    if (!k_new || !v_new || !k_pool || !v_pool)
+        return set_err(FL_ERR_INVALID_ARG, "k_new, v_new, k_pool and v_pool must not be NULL");
+    if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_pool | (uintptr_t)v_pool) & 15)
+        return set_err(FL_ERR_INVALID_ARG, "k_new, v_new, k_pool and v_pool must be 16-byte aligned");
+    const int64_t elem = h->cfg.dtype == FL_F32 ? 4 : 2;
+    const int64_t row_bytes = (int64_t)h->cfg.num_kv_heads * h->cfg.head_dim * elem;
+    if (rows * (row_bytes / 16) >= INT32_MAX)
+        return set_err(FL_ERR_UNSUPPORTED, "rows x 16-byte chunks per token row must stay below 2^31");
+    fl::AppendArgs a{(const int32_t *)(h->d_meta + h->off_append), k_new, v_new, k_pool, v_pool,
+                     (int32_t)rows, (int32_t)row_bytes};
+    const int le = fl::launch_kv_append(a, stream);
+    if (le != (int)hipSuccess) return hip_err((hipError_t)le, "kv append launch");
+    return FL_OK;
+}
+
+fl_status fl_paged_kv_append_slots(fl_handle h, int32_t *slots, int32_t capacity, int32_t *num_rows) {
+    g_last_error.clear();
+    if (!h) return set_err(FL_ERR_INVALID_ARG, "handle is NULL");
+    if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "no plan");
+    if (capacity < 0 || (capacity > 0 && !slots))
+        return set_err(FL_ERR_INVALID_ARG, "slots is NULL or capacity < 0");
+    const Plan &p = h->plan;
+    if (!p.append_ok) return set_err(FL_ERR_INVALID_ARG, "the plan has no append slots: " + p.append_err);
+    const int32_t rows = (int32_t)p.append_rows.size();
+    const int32_t n = std::min(capacity, rows);
+    if (n > 0) std::memcpy(slots, p.append_rows.data(), (size_t)n * 4);
+    if (num_rows) *num_rows = rows;
     return FL_OK;
 }
 

@@ -105,6 +105,10 @@ struct Plan {
     int32_t num_merges = 0;
     int32_t max_splits = 0;
     int64_t part_rows = 0;
+    std::vector<int32_t> append_rows;  // per query row: token row page * P + slot of the
+                                       // token it stands for (the KV append's destination)
+    bool append_ok = false;            // every row has a slot, no two rows share one
+    std::string append_err;            // why not, when !append_ok
 };
 
 // Validate the step's metadata and build the work list. Host only, integer only.
@@ -143,9 +147,22 @@ struct AttnArgs {
 int launch_attention(int dtype, int head_dim, int waves, bool early_refill, int num_groups,
                      const AttnArgs &a, void *stream);
 
+// KV append: copy row r of k_new / v_new (row_bytes each, a multiple of 16) to token row
+// dst_rows[r] of k_pool / v_pool (kv_append.hip).
+struct AppendArgs {
+    const int32_t *dst_rows;
+    const void *k_new;
+    const void *v_new;
+    void *k_pool;
+    void *v_pool;
+    int32_t rows;
+    int32_t row_bytes;
+};
+int launch_kv_append(const AppendArgs &a, void *stream);
+
 // Copy byte ranges [off, off + bytes) from pinned host memory to the same offsets of a
 // device buffer with one kernel (offsets 16-byte aligned, sizes multiples of 4).
-constexpr int kStageParts = 3;
+constexpr int kStageParts = 4;
 struct StageCopy {
     const char *src;   // pinned host memory, device-accessible
     char *dst;         // device memory

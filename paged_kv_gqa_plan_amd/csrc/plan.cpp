@@ -69,7 +69,10 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         return fail(err, FL_ERR_CAPACITY, "batch %lld exceeds max_batch %lld", B, lim.max_batch);
     if (in.num_splits < 0)
         return fail(err, FL_ERR_INVALID_ARG, "num_splits %lld < 0", in.num_splits);
-    if (B == 0) return FL_OK;
+    if (B == 0) {
+        out.append_ok = true;  // nothing to append
+        return FL_OK;
+    }
     if (!in.kv_indptr || !in.last_page_len)
         return fail(err, FL_ERR_INVALID_ARG, "kv_indptr and last_page_len must not be NULL");
     if (in.kv_indptr[0] != 0)
@@ -121,6 +124,44 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
                         pg, in.num_pages);
     }
 
+    // ---- append slots: query row i of request r stands for token kv_len - qo_len + i -----
+    // (the position the bottom-right causal mask gives it); its K/V row goes to that
+    // token's page slot. Recorded as the token row page * P + slot (below 2^31 / Hkv).
+    out.append_rows.assign((size_t)rows, 0);
+    out.append_ok = true;
+    for (int32_t r = 0; r < B && out.append_ok; ++r) {
+        const int32_t np = in.kv_indptr[r + 1] - in.kv_indptr[r];
+        const int32_t kv_len = (np - 1) * P + in.last_page_len[r];
+        const int32_t q0 = in.qo_indptr ? in.qo_indptr[r] : r;
+        const int32_t ql = in.qo_indptr ? in.qo_indptr[r + 1] - q0 : 1;
+        if (ql > kv_len) {
+            char buf[160];
+            std::snprintf(buf, sizeof buf, "request %d has %d query rows but %d cached tokens: "
+                          "no slot to append them to", r, ql, kv_len);
+            out.append_ok = false;
+            out.append_err = buf;
+            break;
+        }
+        const int32_t *pages = in.kv_indices + in.kv_indptr[r];
+        for (int32_t i = 0; i < ql; ++i) {
+            const int32_t t = kv_len - ql + i;
+            out.append_rows[q0 + i] = pages[t / P] * P + t % P;
+        }
+    }
+    if (out.append_ok && rows > 1) {
+        // two rows appending to one slot (a new token placed in a page shared by two
+        // requests) would race; such a plan still serves attention
+        std::vector<int32_t> sorted(out.append_rows);
+        std::sort(sorted.begin(), sorted.end());
+        const auto dup = std::adjacent_find(sorted.begin(), sorted.end());
+        if (dup != sorted.end()) {
+            char buf[160];
+            std::snprintf(buf, sizeof buf, "two query rows append to page %d slot %d (a page "
+                          "shared by two requests)", *dup / P, *dup % P);
+            out.append_ok = false;
+            out.append_err = buf;
+        }
+    }
 
     // ---- row blocks -------------------------------------------------------------------
     // per kv head: the share of its row slice in odd 256-byte halves, in percent; 50 (no

@@ -11,19 +11,18 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
+struct PartChunks {
+    int64_t first[kStageParts + 1];  // first chunk index of each part; [kStageParts] = total
+};
+
 // Every thread copies one 16-byte chunk (or one 4-byte word of a part's tail) of one part:
 // all reads of the bus go out at once, so the copy costs one round trip.
-__global__ __launch_bounds__(256) void stage_copy_kernel(const StageCopy c, int64_t chunks0, int64_t chunks1) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // chunk index over all parts
+__global__ __launch_bounds__(256) void stage_copy_kernel(const StageCopy c, const PartChunks pc) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // chunk index over all parts
+    if (g >= pc.first[kStageParts]) return;
     int p = 0;
-    if (i >= chunks0) {
-        i -= chunks0;
-        p = 1;
-        if (i >= chunks1) {
-            i -= chunks1;
-            p = 2;
-        }
-    }
+    while (g >= pc.first[p + 1]) ++p;
+    const int64_t i = g - pc.first[p];
     const char *src = c.src + c.off[p];
     char *dst = c.dst + c.off[p];
     const int64_t n16 = c.bytes[p] / 16;
@@ -38,15 +37,15 @@ __global__ __launch_bounds__(256) void stage_copy_kernel(const StageCopy c, int6
 }  // namespace
 
 int launch_stage_copy(const StageCopy &c, void *stream) {
-    static_assert(kStageParts == 3, "three parts");
-    int64_t ch[kStageParts];  // 16-byte chunks of each part plus up to 3 tail words
-    for (int p = 0; p < kStageParts; ++p) ch[p] = c.bytes[p] / 16 + (c.bytes[p] % 16) / 4;
-    const int64_t total = ch[0] + ch[1] + ch[2];
+    PartChunks pc;  // 16-byte chunks of each part plus up to 3 tail words
+    pc.first[0] = 0;
+    for (int p = 0; p < kStageParts; ++p)
+        pc.first[p + 1] = pc.first[p] + c.bytes[p] / 16 + (c.bytes[p] % 16) / 4;
+    const int64_t total = pc.first[kStageParts];
     if (total == 0) return (int)hipSuccess;
     const int64_t grid = (total + 255) / 256;
     if (grid > INT32_MAX) return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(stage_copy_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, c, ch[0],
-                       ch[1]);
+    hipLaunchKernelGGL(stage_copy_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, c, pc);
     return (int)hipGetLastError();
 }
 

@@ -1,0 +1,174 @@
+"""GPU parity of the KV append: the HIP kernel against the CPU oracle, through the C interface.
+
+The append is a byte copy, so the bar is bit-exact: after the GPU append, both pools must
+equal the oracle's appended pools byte for byte (the NaN poison of unused slots included).
+Inputs: a seeded batch's pools with each request's newest qo_len tokens taken out and
+poisoned, plus those tokens as the new rows (workloads.append_step).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_gqa_plan_amd as fl
+import workloads as W
+from gpu_helpers import announce, compare, config_for, to_device, to_host_bits, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def _bytes(a):
+    return np.ascontiguousarray(a).view(np.uint8)
+
+
+def _device_append(b, st, h=None):
+    """Plan b on a device handle, append st's rows into device copies of the before-pools;
+    returns (handle, k_pool, v_pool, k_new, v_new) on the device."""
+    import torch
+    h = h or fl.PagedAttention(config_for(b), device=0)
+    h.plan(b.qo_indptr, b.kv_indptr, b.kv_indices, b.last_page_len, b.num_pages,
+           causal=b.causal, sm_scale=b.sm_scale)
+    k = to_device(st.k_before, b.dtype)
+    v = to_device(st.v_before, b.dtype)
+    kn = to_device(st.k_new, b.dtype)
+    vn = to_device(st.v_new, b.dtype)
+    h.append(kn, vn, k, v)
+    torch.cuda.synchronize()
+    return h, k, v, kn, vn
+
+
+def _check_append(b, what=""):
+    announce(f"append {what or b.name}: dtype={b.dtype} B={b.batch_size} rows={b.rows} "
+             f"Hkv={b.num_kv_heads} D={b.head_dim} P={b.page_size}")
+    st = W.append_step(b)
+    ref_k, ref_v = oracle.kv_append(b, st.k_new, st.v_new, st.k_before, st.v_before)
+    h, k, v, _, _ = _device_append(b, st)
+    assert np.array_equal(_bytes(to_host_bits(k, b.dtype)), _bytes(ref_k)), f"{what}: K pool"
+    assert np.array_equal(_bytes(to_host_bits(v, b.dtype)), _bytes(ref_v)), f"{what}: V pool"
+    return h, k, v
+
+
+@pytest.mark.parametrize("name", sorted(W.WORKLOADS))
+def test_append_workloads_full_size(name):
+    _check_append(W.WORKLOADS[name](keep_dense=True))
+
+
+APPEND_VARIANTS = [
+    dict(kv=[16, 17, 64, 65, 300], Hq=12, Hkv=2, D=128, P=64, dtype="f16"),
+    dict(kv=[3, 256, 257, 600], Hq=4, Hkv=1, D=64, P=256, dtype="f32"),
+    dict(kv=[33, 1, 900], Hq=32, Hkv=8, D=128, P=16, dtype="bf16"),
+    dict(kv=[80, 17, 33, 5, 1], qo=[37, 1, 0, 5, 1], Hq=14, Hkv=2, D=64, P=16, dtype="bf16"),
+    dict(kv=[50, 20, 256], qo=[50, 1, 256], Hq=8, Hkv=1, D=128, P=256, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_VARIANTS,
+                         ids=lambda c: f"{c['dtype']}-Hkv{c['Hkv']}-D{c['D']}-P{c['P']}-{'ragged' if 'qo' in c else 'decode'}")
+def test_append_variants(case):
+    b = W.make_batch(case["kv"], case.get("qo"), num_qo_heads=case["Hq"], num_kv_heads=case["Hkv"],
+                     head_dim=case["D"], page_size=case["P"], dtype=case["dtype"],
+                     num_pages=sum(-(-k // case["P"]) for k in case["kv"]) + 6, seed=31,
+                     keep_dense=True)
+    _check_append(b, what=str(case))
+
+
+def test_append_then_attention_matches_oracle_on_two_layers():
+    """One plan per step serves every layer: append layer l's new rows into layer l's pools,
+    then run attention on them; each layer matches the oracle on its full history."""
+    import torch
+
+    def layer(l):
+        return W.make_batch([300, 17, 1536, 100], [1, 1, 512, 1], num_qo_heads=14, num_kv_heads=2,
+                            head_dim=64, page_size=16, dtype="bf16", seed=50 + l, num_pages=200,
+                            keep_dense=True)
+    b0 = layer(0)
+    # layer 1 has its own values; its pages are relabelled onto layer 0's page table
+    b1 = layer(1)
+    perm = np.full(b1.num_pages, -1, np.int64)
+    perm[b1.kv_indices] = b0.kv_indices
+    perm[np.setdiff1d(np.arange(b1.num_pages), b1.kv_indices)] = np.setdiff1d(
+        np.arange(b0.num_pages), b0.kv_indices)
+    layers = [b0, W.relabel_pages(b1, perm)]
+    h = fl.PagedAttention(config_for(b0), device=0)
+    h.plan(b0.qo_indptr, b0.kv_indptr, b0.kv_indices, b0.last_page_len, b0.num_pages,
+           causal=True, sm_scale=b0.sm_scale)
+    for l, b in enumerate(layers):
+        announce(f"append + attention, layer {l}")
+        assert np.array_equal(b.kv_indices, b0.kv_indices)
+        st = W.append_step(b)
+        k, v = to_device(st.k_before, b.dtype), to_device(st.v_before, b.dtype)
+        kn, vn = to_device(st.k_new, b.dtype), to_device(st.v_new, b.dtype)
+        q = to_device(b.q, b.dtype)
+        out = torch.full(q.shape, float("nan"), dtype=torch_dtype(b.dtype), device="cuda:0")
+        lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device="cuda:0")
+        h.append(kn, vn, k, v)
+        h.run(q, k, v, out, lse)
+        torch.cuda.synchronize()
+        ref_out, ref_lse = oracle.attention(b)
+        compare(b, out, lse, ref_out, ref_lse, f"layer {l}")
+
+
+def test_append_graph_replay_across_replans():
+    """append + run captured once in a HIP graph; each replay after a new plan (other page
+    ids, same lengths) writes the new rows to the new slots."""
+    import torch
+    b1 = W.make_batch([40, 300, 17, 1], [1, 1, 9, 1], num_qo_heads=14, num_kv_heads=2, head_dim=64,
+                      page_size=16, dtype="bf16", seed=61, num_pages=64, keep_dense=True)
+    b2 = W.relabel_pages(b1, W.rng_for(62, 0, 0).permutation(b1.num_pages))
+    st1 = W.append_step(b1)
+    st2 = W.append_step(b2)
+    announce("append graph replay across re-plans")
+    h, k, v, kn, vn = _device_append(b1, st1)
+    q = to_device(b1.q, b1.dtype)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda:0")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h.append(kn, vn, k, v)
+        h.run(q, k, v, out)
+    ref = oracle.attention(b1)
+    for rep in range(4):
+        bb, st = (b2, st2) if rep % 2 else (b1, st1)
+        h.plan(bb.qo_indptr, bb.kv_indptr, bb.kv_indices, bb.last_page_len, bb.num_pages,
+               causal=True, sm_scale=bb.sm_scale)
+        k.copy_(to_device(st.k_before, bb.dtype))
+        v.copy_(to_device(st.v_before, bb.dtype))
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        ref_k, ref_v = oracle.kv_append(bb, st.k_new, st.v_new, st.k_before, st.v_before)
+        assert np.array_equal(_bytes(to_host_bits(k, bb.dtype)), _bytes(ref_k)), f"replay {rep}"
+        assert np.array_equal(_bytes(to_host_bits(v, bb.dtype)), _bytes(ref_v)), f"replay {rep}"
+        compare(bb, out, None, ref[0], None, f"replay {rep}")
+        x = torch.randn(1 << 20, device="cuda:0")  # unrelated eager work between replays
+        float(x.sum())
+        torch.cuda.synchronize()
+
+
+def test_append_errors_and_empty_plan():
+    import torch
+    b = W.tiny_decode(keep_dense=True)
+    st = W.append_step(b)
+    h = fl.PagedAttention(config_for(b), device=0)
+    k, v = to_device(st.k_before, b.dtype), to_device(st.v_before, b.dtype)
+    kn, vn = to_device(st.k_new, b.dtype), to_device(st.v_new, b.dtype)
+    with pytest.raises(fl.FlError) as e:
+        h.append(kn, vn, k, v)
+    assert e.value.status == fl.FL_ERR_NOT_PLANNED
+    h.plan(b.qo_indptr, b.kv_indptr, b.kv_indices, b.last_page_len, b.num_pages)
+    with pytest.raises(fl.FlError) as e:
+        fl.fl_paged_kv_append(h.handle, kn.data_ptr() + 2, vn.data_ptr(), k.data_ptr(), v.data_ptr())
+    assert e.value.status == fl.FL_ERR_INVALID_ARG
+    with pytest.raises(fl.FlError) as e:
+        fl.fl_paged_kv_append(h.handle, 0, vn.data_ptr(), k.data_ptr(), v.data_ptr())
+    assert e.value.status == fl.FL_ERR_INVALID_ARG
+    # a plan whose newest tokens share a slot: refused, pools untouched
+    before = to_host_bits(k, b.dtype).copy()
+    h.plan(None, np.array([0, 1, 2]), np.array([5, 5]), np.array([7, 7]), b.num_pages)
+    with pytest.raises(fl.FlError) as e:
+        h.append(kn, vn, k, v)
+    assert e.value.status == fl.FL_ERR_INVALID_ARG
+    # empty plan: a no-op
+    h.plan(np.zeros(1, np.int32), np.zeros(1, np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32),
+           b.num_pages)
+    h.append(kn, vn, k, v)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bytes(to_host_bits(k, b.dtype)), _bytes(before))

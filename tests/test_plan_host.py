@@ -309,3 +309,61 @@ def test_run_needs_a_device_handle_and_a_plan():
     h = host_handle()
     msg = _expect(fl.FL_ERR_UNSUPPORTED, fl.fl_paged_attn_run, h.handle, 16, 16, 16, 16)
     assert "host-only" in msg
+
+
+# ---------------------------------------------------------------------------------------
+# KV append destinations
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", sorted(W.WORKLOADS))
+def test_append_slots_point_where_the_generator_put_the_new_tokens(name):
+    """The generator scattered every request's whole history into the pool; the slot the
+    plan gives each query row must hold exactly that row's token (compared byte for byte
+    with the newest tokens cut from the dense history)."""
+    b = W.WORKLOADS[name](keep_dense=True)
+    st = W.append_step(b)
+    h = host_handle(Hq=b.num_qo_heads, Hkv=b.num_kv_heads, D=b.head_dim, P=b.page_size,
+                    dtype=b.dtype, max_batch=b.batch_size, max_rows=b.rows,
+                    max_pages=int(b.kv_indptr[-1]))
+    plan_batch(h, b)
+    slots = h.append_slots()
+    assert slots.shape == (b.rows,)
+    assert len(np.unique(slots)) == b.rows
+    flat_k = b.k_pool.reshape(b.num_pages * b.page_size, b.num_kv_heads, b.head_dim)
+    flat_v = b.v_pool.reshape(b.num_pages * b.page_size, b.num_kv_heads, b.head_dim)
+    assert np.array_equal(flat_k[slots].view(np.uint8), st.k_new.view(np.uint8))
+    assert np.array_equal(flat_v[slots].view(np.uint8), st.v_new.view(np.uint8))
+
+
+def test_append_slots_worked_out_by_hand():
+    """r0: pages [2, 0], 17 tokens -> token 16 at page 0 slot 0; r1: page [3], 16 tokens ->
+    token 15 at page 3 slot 15; r2: page [1], 5 tokens, 3 new rows -> page 1 slots 2, 3, 4."""
+    h = host_handle(Hq=2, Hkv=1)
+    h.plan(np.array([0, 1, 2, 5]), np.array([0, 2, 3, 4]), np.array([2, 0, 3, 1]),
+           np.array([1, 16, 5]), 4)
+    assert h.append_slots().tolist() == [0 * 16 + 0, 3 * 16 + 15, 1 * 16 + 2, 1 * 16 + 3, 1 * 16 + 4]
+
+
+def test_append_slots_refused_but_attention_planned():
+    h = host_handle(Hq=2, Hkv=1)
+    # non-causal: 3 query rows on a 2-token history is fine for attention, not for append
+    h.plan(np.array([0, 3]), np.array([0, 1]), np.array([0]), np.array([2]), 1, causal=False)
+    assert h.info()[0] > 0
+    msg = _expect(fl.FL_ERR_INVALID_ARG, h.append_slots)
+    assert "no slot" in msg
+    # two requests whose newest token sits in one shared page slot
+    h.plan(None, np.array([0, 1, 2]), np.array([5, 5]), np.array([7, 7]), 8)
+    assert h.info()[0] > 0
+    msg = _expect(fl.FL_ERR_INVALID_ARG, h.append_slots)
+    assert "page 5 slot 6" in msg
+    # requests sharing a page but appending to their own pages are fine
+    h.plan(None, np.array([0, 2, 4]), np.array([5, 1, 5, 2]), np.array([3, 3]), 8)
+    assert h.append_slots().tolist() == [1 * 16 + 2, 2 * 16 + 2]
+
+
+def test_append_on_empty_plan_and_host_handle():
+    h = host_handle()
+    _expect(fl.FL_ERR_NOT_PLANNED, h.append_slots)
+    h.plan(np.zeros(1, np.int32), np.zeros(1, np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32), 1)
+    assert h.append_slots().size == 0
+    msg = _expect(fl.FL_ERR_UNSUPPORTED, fl.fl_paged_kv_append, h.handle, 16, 16, 16, 16)
+    assert "host-only" in msg
