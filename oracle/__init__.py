@@ -9,7 +9,8 @@ The arithmetic lives in ``paged_attn_oracle.c`` (plain C, double precision): a g
 each request's pages into dense K/V followed by plain softmax attention, plus an optional
 split-and-merge mode. ``attention(batch)`` returns unrounded fp64 results.
 ``kv_append(...)`` writes a step's new K/V rows into copies of the pools (a byte copy to
-each new token's page slot).
+each new token's page slot); ``paged_kv_poison(...)`` fills freed pages with NaN.
+``page_pool.PagePoolModel`` is the page allocator's reference bookkeeping.
 """
 from __future__ import annotations
 
@@ -61,6 +62,10 @@ def load(path: Optional[str] = None):
         ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.oracle_paged_kv_poison.restype = ctypes.c_int
+    lib.oracle_paged_kv_poison.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_void_p]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     if path is None or path == _LIB_OVERRIDE:
@@ -149,6 +154,21 @@ def kv_append(batch, k_new, v_new, k_pool=None, v_pool=None, lib=None):
                            batch.head_dim, batch.page_size, k_new, v_new,
                            batch.k_pool if k_pool is None else k_pool,
                            batch.v_pool if v_pool is None else v_pool, lib=lib)
+
+
+def paged_kv_poison(dtype_code: int, page_ids, k_pool, v_pool=None, lib=None):
+    """Copies of the pools ``[num_pages, ...]`` with every element of the listed pages set to
+    the storage type's quiet NaN."""
+    lib = lib or load()
+    ids = np.ascontiguousarray(page_ids, dtype=np.int32)
+    k_out = np.array(k_pool, copy=True, order="C")
+    v_out = None if v_pool is None else np.array(v_pool, copy=True, order="C")
+    page_elems = int(np.prod(k_out.shape[1:]))
+    rc = lib.oracle_paged_kv_poison(int(dtype_code), page_elems, _ptr(ids), int(ids.size),
+                                    int(k_out.shape[0]), _ptr(k_out), _ptr(v_out))
+    if rc != 0:
+        raise OracleError(f"oracle_paged_kv_poison returned {rc}")
+    return k_out, v_out
 
 
 def decode(dtype_code: int, values: np.ndarray, lib=None) -> np.ndarray:

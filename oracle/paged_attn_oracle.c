@@ -332,3 +332,39 @@ int oracle_paged_kv_append(int elem_bytes, int batch, const int32_t *qo_indptr,
     }
     return ORACLE_OK;
 }
+
+/*
+ * Poisoning freed pages ("A library kernel for decode", closing paragraph: the engine's
+ * gates poison pages when they return to the free list, so a kernel that still reads a
+ * freed page produces NaN instead of stale numbers).
+ *
+ * Every element of each listed page (page_size * num_kv_heads * head_dim values, in
+ * both pools) becomes the storage type's quiet NaN with a clear sign bit and a zero
+ * payload: binary16 0x7E00, bfloat16 0x7FC0, binary32 0x7FC00000. Other pages are not
+ * touched; a page listed twice is poisoned once. v_pool may be NULL.
+ * Returns 0, or a negative code (pools untouched) for a page id outside [0, num_pages).
+ */
+int oracle_paged_kv_poison(int dtype, int64_t page_elems, const int32_t *page_ids, int n,
+                           int64_t num_pages, void *k_pool, void *v_pool)
+{
+    if (dtype < 1 || dtype > 3 || page_elems <= 0 || n < 0 || (n > 0 && (!page_ids || !k_pool)))
+        return ORACLE_BAD_ARG;
+    for (int j = 0; j < n; ++j)
+        if (page_ids[j] < 0 || page_ids[j] >= num_pages)
+            return ORACLE_BAD_ARG;
+    for (int j = 0; j < n; ++j) {
+        for (int pool = 0; pool < 2; ++pool) {
+            void *base = pool ? v_pool : k_pool;
+            if (!base)
+                continue;
+            const size_t first = (size_t)page_ids[j] * (size_t)page_elems;
+            for (int64_t e = 0; e < page_elems; ++e) {
+                if (dtype == 3)
+                    ((uint32_t *)base)[first + (size_t)e] = 0x7FC00000u;
+                else
+                    ((uint16_t *)base)[first + (size_t)e] = dtype == 1 ? 0x7E00u : 0x7FC0u;
+            }
+        }
+    }
+    return ORACLE_OK;
+}

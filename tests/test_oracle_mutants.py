@@ -40,6 +40,11 @@ MUTANTS = {
                                     "const int64_t page = kv_indices[pos / P];"),
     "append_rows_ignore_request": ("const size_t src = (size_t)(row0 + i) * token_bytes;",
                                    "const size_t src = (size_t)i * token_bytes;"),
+    # poisoning freed pages
+    "poison_k_pool_only": ("            if (!base)\n                continue;\n            const size_t first",
+                           "            if (!base || pool)\n                continue;\n            const size_t first"),
+    "poison_half_page": ("for (int64_t e = 0; e < page_elems; ++e) {", "for (int64_t e = 0; e < page_elems / 2; ++e) {"),
+    "poison_negative_bf16_nan": ("dtype == 1 ? 0x7E00u : 0x7FC0u", "dtype == 1 ? 0x7E00u : 0xFFC0u"),
     "append_k_v_swapped": ("memcpy((char *)v_pool + dst, (const char *)v_new + src, token_bytes);",
                            "memcpy((char *)v_pool + dst, (const char *)k_new + src, token_bytes);"),
 }

@@ -442,3 +442,79 @@ def test_append_rejects_bad_metadata():
     bad = b.kv_indices.copy(); bad[0] = -1
     with pytest.raises(oracle.OracleError):
         run(kvi=bad)
+
+
+# ---------------------------------------------------------------------------------------
+# freed-page poisoning and the page allocator's reference bookkeeping
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_poison_fills_listed_pages_with_nan_only(dtype):
+    b = W.make_batch([40, 7], num_qo_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
+                     dtype=dtype, num_pages=8, seed=23, poison=False)
+    k, v = oracle.paged_kv_poison(b.dtype_code, [5, 1, 5], b.k_pool, b.v_pool)
+    kf, vf = W.storage_to_f32(k, dtype), W.storage_to_f32(v, dtype)
+    for p in range(8):
+        if p in (1, 5):
+            assert np.isnan(kf[p]).all() and np.isnan(vf[p]).all()
+        else:
+            assert np.array_equal(as_bytes(k[p]), as_bytes(b.k_pool[p]))
+            assert np.array_equal(as_bytes(v[p]), as_bytes(b.v_pool[p]))
+    # the canonical quiet NaN of each type, as numpy / torch spell it
+    ref = {"bf16": torch.tensor(float("nan"), dtype=torch.bfloat16).view(torch.int16).item() & 0xFFFF,
+           "f16": int(np.float16(np.nan).view(np.uint16)),
+           "f32": int(np.float32(np.nan).view(np.uint32))}[dtype]
+    assert int(np.ascontiguousarray(k[1]).reshape(-1).view(
+        np.uint32 if dtype == "f32" else np.uint16)[0]) == ref
+
+
+def test_poisoned_page_makes_attention_nan():
+    """A request whose page table still names a freed (poisoned) page reads NaN."""
+    b = W.make_batch([40, 7], num_qo_heads=4, num_kv_heads=2, head_dim=64, page_size=16,
+                     dtype="bf16", num_pages=8, seed=24)
+    freed = int(b.kv_indices[b.kv_indptr[1]])   # the page of request 1
+    k, v = oracle.paged_kv_poison(b.dtype_code, [freed], b.k_pool, b.v_pool)
+    out, _ = oracle.attention(dataclasses.replace(b, k_pool=k, v_pool=v))
+    assert np.isfinite(out[0]).all() and np.isnan(out[1]).all()
+
+
+def test_poison_rejects_pages_outside_the_pool():
+    b = W.tiny_decode()
+    with pytest.raises(oracle.OracleError):
+        oracle.paged_kv_poison(b.dtype_code, [b.num_pages], b.k_pool, b.v_pool)
+
+
+def test_pool_model_whole_page_reservation():
+    from oracle.page_pool import PagePoolModel
+    m = PagePoolModel(64, 256)
+    # 300 slots on 256-slot pages hold two pages (512 slots); on 64-slot pages five (320)
+    assert m.pages_for(300) == 2 and PagePoolModel(64, 64).pages_for(300) == 5
+    assert m.pages_for(0) == 0 and m.pages_for(1) == 1 and m.pages_for(256) == 1 and m.pages_for(257) == 2
+
+
+def test_pool_model_worked_sequence():
+    """Four pages. Request A takes pages 0, 1; B adopts A's first page (prefix sharing) and
+    takes page 2 of its own; A finishes: only page 1 frees (page 0 is still B's); B finishes:
+    pages 0 and 2 free, in list order."""
+    from oracle.page_pool import PagePoolModel, PoolModelError
+    m = PagePoolModel(4, 16)
+    m.alloc([0, 1])
+    m.retain([0])
+    m.alloc([2])
+    assert m.refs == [2, 1, 1, 0] and m.num_free == 1 and m.num_live == 3
+    assert m.release([0, 1]) == [1]
+    assert m.refs == [1, 0, 1, 0]
+    assert m.release([2, 0]) == [2, 0]
+    assert m.num_free == 4
+    with pytest.raises(PoolModelError):
+        m.release([3])                  # never held
+    m.alloc([3])
+    with pytest.raises(PoolModelError):
+        m.release([3, 3])               # released twice, held once: nothing changes
+    assert m.refs[3] == 1
+    with pytest.raises(PoolModelError):
+        m.alloc([3])                    # handed out while held
+    with pytest.raises(PoolModelError):
+        m.alloc([0, 0])                 # the same page twice
+    with pytest.raises(PoolModelError):
+        m.retain([1])                   # adopt a free page
+    assert not m.can_alloc(4) and m.can_alloc(3)
