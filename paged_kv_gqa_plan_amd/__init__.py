@@ -50,7 +50,10 @@ class FlError(RuntimeError):
 EXPORTED = ("fl_paged_attn_create", "fl_paged_attn_destroy", "fl_paged_attn_plan",
             "fl_paged_attn_run", "fl_paged_kv_append", "fl_paged_kv_append_slots",
             "fl_paged_attn_plan_info",
-            "fl_paged_attn_get_work_items", "fl_last_error")
+            "fl_paged_attn_get_work_items", "fl_page_pool_create", "fl_page_pool_destroy",
+            "fl_page_pool_alloc", "fl_page_pool_reserve", "fl_page_pool_retain",
+            "fl_page_pool_release", "fl_page_pool_refcounts", "fl_page_pool_info",
+            "fl_paged_kv_poison", "fl_last_error")
 
 _lib = None
 
@@ -75,6 +78,15 @@ def load_library(path: Optional[str] = None):
     lib.fl_paged_attn_plan_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                             ctypes.POINTER(i32), ctypes.POINTER(i64)]
     lib.fl_paged_attn_get_work_items.argtypes = [vp, vp, i32, ctypes.POINTER(i32)]
+    lib.fl_page_pool_create.argtypes = [i64, i32, ctypes.POINTER(vp)]
+    lib.fl_page_pool_destroy.argtypes = [vp]
+    lib.fl_page_pool_alloc.argtypes = [vp, i32, vp]
+    lib.fl_page_pool_reserve.argtypes = [vp, i64, vp, i32, ctypes.POINTER(i32)]
+    lib.fl_page_pool_retain.argtypes = [vp, vp, i32]
+    lib.fl_page_pool_release.argtypes = [vp, vp, i32, vp, ctypes.POINTER(i32)]
+    lib.fl_page_pool_refcounts.argtypes = [vp, vp, i32, vp]
+    lib.fl_page_pool_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.fl_paged_kv_poison.argtypes = [i32, i32, i32, i32, i64, vp, i32, vp, vp, vp]
     for name in EXPORTED[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.fl_last_error.argtypes = []
@@ -234,3 +246,110 @@ class PagedAttention:
 
     def work_items(self) -> np.ndarray:
         return fl_paged_attn_get_work_items(self.handle)
+
+
+# ---------------------------------------------------------------------------------------
+# page allocator and freed-page poisoning (fl_page_pool.h)
+# ---------------------------------------------------------------------------------------
+def fl_page_pool_create(num_pages: int, page_size: int) -> ctypes.c_void_p:
+    p = ctypes.c_void_p()
+    _check(load_library().fl_page_pool_create(int(num_pages), int(page_size), ctypes.byref(p)),
+           "fl_page_pool_create")
+    return p
+
+
+def fl_page_pool_destroy(p) -> None:
+    _check(load_library().fl_page_pool_destroy(p), "fl_page_pool_destroy")
+
+
+def fl_page_pool_alloc(p, n: int) -> np.ndarray:
+    ids = np.zeros(max(int(n), 1), dtype=np.int32)
+    _check(load_library().fl_page_pool_alloc(p, int(n), _p(ids)), "fl_page_pool_alloc")
+    return ids[:int(n)]
+
+
+def fl_page_pool_reserve(p, tokens: int, capacity: int = 1 << 20) -> np.ndarray:
+    ids = np.zeros(max(int(capacity), 1), dtype=np.int32)
+    n = ctypes.c_int32()
+    _check(load_library().fl_page_pool_reserve(p, int(tokens), _p(ids), int(capacity),
+                                               ctypes.byref(n)), "fl_page_pool_reserve")
+    return ids[:n.value]
+
+
+def fl_page_pool_retain(p, page_ids) -> None:
+    ids = _i32(page_ids)
+    _check(load_library().fl_page_pool_retain(p, _p(ids), int(ids.size)), "fl_page_pool_retain")
+
+
+def fl_page_pool_release(p, page_ids) -> np.ndarray:
+    """Returns the ids that became free, in the order their counts reached zero."""
+    ids = _i32(page_ids)
+    freed = np.zeros(max(ids.size, 1), dtype=np.int32)
+    n = ctypes.c_int32()
+    _check(load_library().fl_page_pool_release(p, _p(ids), int(ids.size), _p(freed), ctypes.byref(n)),
+           "fl_page_pool_release")
+    return freed[:n.value]
+
+
+def fl_page_pool_refcounts(p, page_ids) -> np.ndarray:
+    ids = _i32(page_ids)
+    refs = np.zeros(max(ids.size, 1), dtype=np.int32)
+    _check(load_library().fl_page_pool_refcounts(p, _p(ids), int(ids.size), _p(refs)),
+           "fl_page_pool_refcounts")
+    return refs[:ids.size]
+
+
+def fl_page_pool_info(p) -> Tuple[int, int]:
+    """(free pages, held pages)."""
+    f, h = ctypes.c_int64(), ctypes.c_int64()
+    _check(load_library().fl_page_pool_info(p, ctypes.byref(f), ctypes.byref(h)), "fl_page_pool_info")
+    return f.value, h.value
+
+
+def fl_paged_kv_poison(dtype: str, page_size: int, num_kv_heads: int, head_dim: int,
+                       num_pages: int, page_ids, k_pool: int, v_pool: Optional[int] = None,
+                       stream: int = 0) -> None:
+    """Device pool pointers as integers; page ids a host array."""
+    ids = _i32(page_ids)
+    _check(load_library().fl_paged_kv_poison(DTYPE_CODES[dtype], int(page_size), int(num_kv_heads),
+                                             int(head_dim), int(num_pages), _p(ids), int(ids.size),
+                                             ctypes.c_void_p(k_pool), ctypes.c_void_p(v_pool or 0),
+                                             ctypes.c_void_p(int(stream))),
+           "fl_paged_kv_poison")
+
+
+class PagePool:
+    """The allocator handle with numpy in and out."""
+
+    def __init__(self, num_pages: int, page_size: int):
+        self.num_pages, self.page_size = int(num_pages), int(page_size)
+        self.handle = fl_page_pool_create(num_pages, page_size)
+
+    def close(self):
+        if self.handle is not None:
+            fl_page_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc(self, n: int) -> np.ndarray:
+        return fl_page_pool_alloc(self.handle, n)
+
+    def reserve(self, tokens: int) -> np.ndarray:
+        return fl_page_pool_reserve(self.handle, tokens)
+
+    def retain(self, page_ids) -> None:
+        fl_page_pool_retain(self.handle, page_ids)
+
+    def release(self, page_ids) -> np.ndarray:
+        return fl_page_pool_release(self.handle, page_ids)
+
+    def refcounts(self, page_ids) -> np.ndarray:
+        return fl_page_pool_refcounts(self.handle, page_ids)
+
+    def info(self) -> Tuple[int, int]:
+        return fl_page_pool_info(self.handle)

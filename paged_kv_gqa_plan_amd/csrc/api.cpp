@@ -25,10 +25,7 @@ namespace {
 
 thread_local std::string g_last_error;
 
-fl_status set_err(fl_status st, const std::string &msg) {
-    g_last_error = msg;
-    return st;
-}
+fl_status set_err(fl_status st, const std::string &msg) { return fl::set_error(st, msg); }
 
 fl_status hip_err(hipError_t e, const char *what) {
     return set_err(FL_ERR_HIP, std::string(what) + ": " + hipGetErrorName(e) + " (" +
@@ -68,6 +65,13 @@ struct fl_paged_attn {
     int32_t causal = 1;
     float scale_log2 = 0.f;
 };
+
+fl_status fl::set_error(fl_status st, const std::string &msg) {
+    g_last_error = msg;
+    return st;
+}
+
+void fl::clear_error() { g_last_error.clear(); }
 
 namespace {
 

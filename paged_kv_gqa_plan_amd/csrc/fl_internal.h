@@ -11,6 +11,10 @@
 
 namespace fl {
 
+// The thread's last error message (fl_last_error): set it and return st; clear it.
+fl_status set_error(fl_status st, const std::string &msg);
+void clear_error();
+
 // Keys per MFMA tile: the 16-row M dimension of the 16x16xK matrix instructions.
 constexpr int kTileTokens = 16;
 // Flattened query rows (query row * G + head in group) per row block: the 16-column N
@@ -159,6 +163,18 @@ struct AppendArgs {
     int32_t row_bytes;
 };
 int launch_kv_append(const AppendArgs &a, void *stream);
+
+// Poison: fill whole pages of one or two pools with a 16-byte pattern (kv_poison.hip).
+constexpr int kPoisonIdsPerLaunch = 256;
+struct PoisonArgs {
+    const int32_t *page_ids;   // host
+    int32_t n;
+    void *k_pool;
+    void *v_pool;              // may be NULL
+    int64_t page_bytes;        // a multiple of 16
+    uint32_t pattern[4];
+};
+int launch_kv_poison(const PoisonArgs &a, void *stream);
 
 // Copy byte ranges [off, off + bytes) from pinned host memory to the same offsets of a
 // device buffer with one kernel (offsets 16-byte aligned, sizes multiples of 4).

@@ -17,7 +17,8 @@ HEADER = os.path.join(ROOT, "include", "fl_paged_attn.h")
 
 
 def test_library_exports_every_declared_function():
-    text = open(HEADER).read()
+    import glob
+    text = "".join(open(h).read() for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
     declared = set(re.findall(r"^\s*(?:fl_status|const char \*)\s*(fl_\w+)\s*\(", text, re.M))
     assert declared == set(fl.EXPORTED)
     lib = fl.load_library()
