@@ -279,6 +279,9 @@ def main(argv=None):
     ap.add_argument("--groups-per-cu", type=int, default=0)
     ap.add_argument("--min-group-tokens", type=int, default=0)
     ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup (4; 0 = default)")
+    ap.add_argument("--whole-rows", type=int, default=0, choices=[-1, 0, 1],
+                    help="whole-row blocks: 0 where they apply and pay off, 1 wherever they "
+                         "apply, -1 never (one block per kv head)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch layer runs without a HIP graph")
@@ -336,7 +339,7 @@ def main(argv=None):
     cfg = fl.make_config(b.num_qo_heads, b.num_kv_heads, b.head_dim, b.page_size, b.dtype,
                          b.batch_size, b.rows, int(b.kv_indptr[-1]),
                          groups_per_cu=args.groups_per_cu, min_group_tokens=args.min_group_tokens,
-                         waves_per_group=args.waves)
+                         waves_per_group=args.waves, whole_rows=args.whole_rows)
     h = fl.PagedAttention(cfg, device=0)
     stream = torch.cuda.current_stream()
 
@@ -414,6 +417,7 @@ def main(argv=None):
                    "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
                    "page_size": b.page_size, "pool_pages": b.num_pages, "layers": L,
                    "seed": args.seed, "splits": args.splits, "waves": args.waves,
+                   "whole_rows": args.whole_rows,
                    "parallelism": "single GPU"},
         "us_per_call": round(us_call, 3),
         "us_per_call_median": round(us_call_med, 3),

@@ -89,6 +89,14 @@ typedef struct {
     int32_t waves_per_group;   /* wavefronts per workgroup: 4 (0 = the same)              */
     int64_t max_tiles;         /* most 16-key tiles (over all row blocks) one plan may
                                   hold; 0 = a bound derived from the other capacities     */
+    int32_t whole_rows;        /* Whole-row blocks: one row block holds all query heads
+                                  of a request and streams whole token rows (every kv
+                                  head) at once. They apply to decode-only steps (every
+                                  request has at most one query row) with num_kv_heads *
+                                  head_dim = 128, num_kv_heads > 1, at most 16 query heads
+                                  and a 16-bit type. 0: used where they apply and the step
+                                  has at least one query row per compute unit; 1: used
+                                  wherever they apply; -1: never (one block per kv head) */
 } fl_config;
 
 /*
@@ -194,8 +202,11 @@ fl_status fl_paged_attn_plan_info(fl_handle h, int32_t *num_work_items, int32_t 
  * one request and kv head, over one range of keys. The plan lays every row block's 16-key
  * tiles in one sequence and gives each workgroup an equal contiguous share, so a
  * workgroup runs a few segments back to back and a long row block may span several
- * workgroups (its pieces are merged by log-sum-exp). *num_items receives the item count;
- * at most `capacity` items are written.
+ * workgroups (its pieces are merged by log-sum-exp). On decode-only steps that qualify for
+ * whole_rows (fl_config), a block holds all query heads of one request instead (flattened
+ * row query row * num_qo_heads + head, FL_WI_KV_HEAD = -1) and streams every kv head's
+ * slice of each token row at once. *num_items receives the item count; at most `capacity`
+ * items are written.
  */
 #define FL_WORK_ITEM_INTS 16
 enum {
@@ -203,7 +214,8 @@ enum {
     FL_WI_QO_LEN = 1,    /* query rows of the request                                   */
     FL_WI_KV_LEN = 2,    /* cached tokens of the request                                */
     FL_WI_PAGE_BASE = 3, /* kv_indptr[request]                                          */
-    FL_WI_KV_HEAD = 4,
+    FL_WI_KV_HEAD = 4,   /* -1: the block covers every kv head (whole token rows); its
+                            flattened row is query row * num_qo_heads + head            */
     FL_WI_ROW_BEGIN = 5, /* first flattened row of the block                            */
     FL_WI_NUM_ROWS = 6,  /* rows in the block (<= 16)                                   */
     FL_WI_TOK_BEGIN = 7, /* key range [tok_begin, tok_end)                               */

@@ -38,7 +38,7 @@ class fl_config(ctypes.Structure):
                 ("max_qo_rows", ctypes.c_int32), ("max_kv_pages", ctypes.c_int64),
                 ("num_cus", ctypes.c_int32), ("groups_per_cu", ctypes.c_int32),
                 ("min_group_tokens", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
-                ("max_tiles", ctypes.c_int64)]
+                ("max_tiles", ctypes.c_int64), ("whole_rows", ctypes.c_int32)]
 
 
 class FlError(RuntimeError):
@@ -190,10 +190,10 @@ def fl_paged_attn_get_work_items(h) -> np.ndarray:
 def make_config(num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
                 dtype: str, max_batch: int, max_qo_rows: int, max_kv_pages: int,
                 num_cus: int = 0, groups_per_cu: int = 0, min_group_tokens: int = 0,
-                waves_per_group: int = 0, max_tiles: int = 0) -> fl_config:
+                waves_per_group: int = 0, max_tiles: int = 0, whole_rows: int = 0) -> fl_config:
     return fl_config(num_qo_heads, num_kv_heads, head_dim, page_size, DTYPE_CODES[dtype],
                      max_batch, max_qo_rows, max_kv_pages, num_cus, groups_per_cu,
-                     min_group_tokens, waves_per_group, max_tiles)
+                     min_group_tokens, waves_per_group, max_tiles, whole_rows)
 
 
 class PagedAttention:

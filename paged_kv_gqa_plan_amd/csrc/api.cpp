@@ -51,6 +51,7 @@ struct fl_paged_attn {
     float *d_part_lse = nullptr; // [part_rows_cap]
     int64_t off_wg_rec = 0, off_tickets = 0, off_steps = 0, off_append = 0, meta_bytes = 0;
     int32_t waves = 4;
+    int32_t part_width = 64;     // floats per partial row: head_dim, or 128 for whole rows
 
     // pinned staging, double-buffered
     char *h_stage[2] = {nullptr, nullptr};
@@ -94,6 +95,8 @@ fl_status check_config(const fl_config *c) {
                                            "max_tiles must be >= 0");
     if (c->waves_per_group != 0 && c->waves_per_group != 4)
         return set_err(FL_ERR_UNSUPPORTED, "waves_per_group must be 0 or 4");
+    if (c->whole_rows < -1 || c->whole_rows > 1)
+        return set_err(FL_ERR_INVALID_ARG, "whole_rows must be -1, 0 or 1");
     // the kernels divide flattened rows of a request (below max_qo_rows * G + 16) by G
     // with a 32-bit reciprocal multiply, exact while the dividend stays below 2^32 / G
     const uint64_t g = (uint64_t)(c->num_qo_heads / c->num_kv_heads);
@@ -178,6 +181,13 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
     L.waves = h->waves;
     L.min_group_tiles =
         cfg->min_group_tokens > 0 ? (int32_t)((cfg->min_group_tokens + 15) / 16) : 8;
+    L.whole_rows_always = cfg->whole_rows == 1;
+    L.whole_rows_ok = cfg->whole_rows >= 0 && cfg->dtype != FL_F32 &&
+                      cfg->num_kv_heads * cfg->head_dim == 128 && cfg->num_kv_heads > 1 &&
+                      cfg->num_qo_heads <= fl::kBlockRows &&
+                      ((uint64_t)cfg->max_qo_rows * cfg->num_qo_heads + 16) * cfg->num_qo_heads <
+                          (1ull << 32);  // the kernels' division of flattened rows by Hq
+    h->part_width = L.whole_rows_ok ? 128 : cfg->head_dim;
     const int64_t blocks = fl::row_block_bound(L);
     L.group_cap = std::max<int64_t>((int64_t)num_cus * std::max(L.groups_per_cu, 2), 16384);
     L.seg_cap = blocks + L.group_cap;
@@ -188,7 +198,7 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
     L.max_tiles = cfg->max_tiles > 0 ? cfg->max_tiles : std::min<int64_t>(tiles_bound, 1LL << 24);
     // partial rows are addressed with 32-bit byte offsets: keep the workspace under 2 GiB
     L.part_rows_cap = std::min<int64_t>(L.seg_cap * fl::kBlockRows,
-                                        (INT32_MAX / 4) / (cfg->head_dim + 1));
+                                        (INT32_MAX / 4) / (h->part_width + 1));
     if (L.seg_cap > INT32_MAX / FL_WORK_ITEM_INTS || L.max_tiles > INT32_MAX) {
         release(h);
         return set_err(FL_ERR_CAPACITY, "capacities too large");
@@ -203,7 +213,7 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
     if (!h->host_only) {
         hipError_t e;
         if ((e = hipMalloc((void **)&h->d_meta, h->meta_bytes)) != hipSuccess ||
-            (e = hipMalloc((void **)&h->d_part_o, L.part_rows_cap * cfg->head_dim * 4)) !=
+            (e = hipMalloc((void **)&h->d_part_o, L.part_rows_cap * h->part_width * 4)) !=
                 hipSuccess ||
             (e = hipMalloc((void **)&h->d_part_lse, L.part_rows_cap * 4)) != hipSuccess) {
             release(h);
@@ -317,14 +327,18 @@ fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, cons
     a.part_o = h->d_part_o;
     a.part_lse = h->d_part_lse;
     a.num_qo_heads = h->cfg.num_qo_heads;
-    a.num_kv_heads = h->cfg.num_kv_heads;
-    a.group = h->group;
-    a.group_magic = h->group > 1 ? (uint32_t)(((1ull << 32) + h->group - 1) / h->group) : 0u;
+    // whole-row blocks: one virtual kv head of Hkv * D values shared by every query head
+    const int32_t group = p.whole_rows ? h->cfg.num_qo_heads : h->group;
+    a.num_kv_heads = p.whole_rows ? 1 : h->cfg.num_kv_heads;
+    a.group = group;
+    a.group_magic = group > 1 ? (uint32_t)(((1ull << 32) + group - 1) / group) : 0u;
+    a.real_group = h->group;
     a.causal = h->causal;
     a.scale_log2 = h->scale_log2;
+    const int head_dim = p.whole_rows ? h->cfg.num_kv_heads * h->cfg.head_dim : h->cfg.head_dim;
     // two workgroups per compute unit are chosen for steps bound by the per-tile arithmetic
-    const int e = fl::launch_attention(h->cfg.dtype, h->cfg.head_dim, h->waves,
-                                       p.groups_per_cu == 1, p.num_groups, a, stream);
+    const int e = fl::launch_attention(h->cfg.dtype, head_dim, h->waves, p.groups_per_cu == 1,
+                                       p.whole_rows, p.num_groups, a, stream);
     if (e != (int)hipSuccess) return hip_err((hipError_t)e, "attention launch");
     return FL_OK;
 }
@@ -377,7 +391,8 @@ fl_status fl_paged_attn_plan_info(fl_handle h, int32_t *num_work_items, int32_t 
     if (num_work_items) *num_work_items = h->plan.num_segs;
     if (num_groups) *num_groups = h->plan.num_groups;
     if (max_splits) *max_splits = h->plan.max_splits;
-    if (workspace_bytes) *workspace_bytes = h->plan.part_rows * ((int64_t)h->cfg.head_dim + 1) * 4;
+    const int64_t width = h->plan.whole_rows ? h->part_width : h->cfg.head_dim;
+    if (workspace_bytes) *workspace_bytes = h->plan.part_rows * (width + 1) * 4;
     return FL_OK;
 }
 
@@ -390,6 +405,8 @@ fl_status fl_paged_attn_get_work_items(fl_handle h, int32_t *items, int32_t capa
         return set_err(FL_ERR_INVALID_ARG, "items is NULL or capacity < 0");
     const int32_t n = std::min(capacity, h->plan.num_segs);
     if (n > 0) std::memcpy(items, h->plan.segs.data(), (size_t)n * FL_WORK_ITEM_INTS * 4);
+    if (h->plan.whole_rows)  // the kernel's virtual kv head 0 is every real kv head
+        for (int32_t i = 0; i < n; ++i) items[(size_t)i * FL_WORK_ITEM_INTS + FL_WI_KV_HEAD] = -1;
     if (num_items) *num_items = h->plan.num_segs;
     return FL_OK;
 }

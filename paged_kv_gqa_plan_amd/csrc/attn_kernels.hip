@@ -417,22 +417,33 @@ struct HalfTile {
         return (uint32_t)(t * 2 * D + 16 * (piece ^ swz(t)) + 8 * (j & 1));
     }
 
-    // Q rows of block segment w into LDS (rows past num_rows repeat row 0)
+    // Q rows of block segment w into LDS (rows past num_rows repeat row 0).
+    // Whole-row blocks (WR): block row h is query head h, whose D/2 values belong in the half
+    // of the D-wide operand row that its kv head occupies in a token row (two kv heads of
+    // D/2). Both halves of the LDS row receive the head's values; q_fetch zeroes the other
+    // half, so the contraction over a whole token row only sees the head's own kv head.
+    template <bool WR>
     __device__ static void q_stage(const lds_char *qb, const AttnArgs &a, const Seg &w, int lane) {
-        const char *base = (const char *)a.q + q_block_base(w, a) * (2 * D);
+        constexpr int kRowB = WR ? D : 2 * D;           // bytes of one q row in memory
+        constexpr int kPieces = WR ? S / 2 : S;         // 16-byte pieces of it
+        const char *base = (const char *)a.q + q_block_base(w, a) * kRowB;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int r = KPL * c + lane / S;
-            const int piece = (lane % S) ^ swz(r);
-            dma_b128(base, (uint32_t)(q_block_row(w, a, r) * 2 * D + 16 * piece), qb + 1024 * c);
+            const int piece = ((lane % S) ^ swz(r)) & (kPieces - 1);
+            dma_b128(base, (uint32_t)(q_block_row(w, a, r) * kRowB + 16 * piece), qb + 1024 * c);
         }
     }
-    __device__ static QOp q_fetch(const lds_char *qb, const RowInfo &ri, int col, int grp) {
+    // kv_half: for whole-row blocks, the half (0 or 1) of the operand row this lane's block
+    // row keeps; -1 keeps everything
+    __device__ static QOp q_fetch(const lds_char *qb, const RowInfo &ri, int col, int grp, int kv_half = -1) {
         QOp op;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)(qb + op_off(c, col, grp));
-            op.q[c] = ri.ok ? v : u32x4{0, 0, 0, 0};
+            // piece 4c + grp of the row lies in half (4c + grp) / (S / 2) = c / (NC / 2)
+            const bool keep = ri.ok && (kv_half < 0 || c / (NC / 2) == kv_half);
+            op.q[c] = keep ? v : u32x4{0, 0, 0, 0};
         }
         return op;
     }
@@ -571,7 +582,9 @@ struct F32Tile {
     static constexpr int RPL = 64 / P4;                   // rows per 1 KB load
     static constexpr int kQBytes = kBlockRows * 4 * D;
     static constexpr int kLoads = D / 8;                  // 16-byte loads per lane per tile
+    template <bool WR>
     __device__ static void q_stage(const lds_char *qb, const AttnArgs &a, const Seg &w, int lane) {
+        static_assert(!WR, "whole-row blocks are 16-bit only");
         const char *base = (const char *)a.q + q_block_base(w, a) * (4 * D);
 #pragma unroll
         for (int c = 0; c < kQBytes / 1024; ++c) {
@@ -579,7 +592,7 @@ struct F32Tile {
             dma_b128(base, (uint32_t)(q_block_row(w, a, r) * 4 * D + 16 * (lane % P4)), qb + 1024 * c);
         }
     }
-    __device__ static QOp q_fetch(const lds_char *qb, const RowInfo &ri, int col, int grp) {
+    __device__ static QOp q_fetch(const lds_char *qb, const RowInfo &ri, int col, int grp, int = -1) {
         QOp op;
         const lds_char *row = qb + col * 4 * D + grp * NS * 4;
 #pragma unroll
@@ -762,7 +775,29 @@ struct RowSplit {
 // of pieces at a time with every load of a batch issued before any is used (the running max
 // carries across batches by rescaling, as in the online softmax). Partial-row byte
 // offsets fit in 32 bits: the workspace is sized from the handle's capacities.
-template <int DT, int D, int TPR, int MB>
+// Final row `row` (q row * Hq + head) from the D fp32 values a thread holds: every chunk,
+// or for whole-row blocks only the chunks in the half of the row that the head's kv head
+// owns, stored at their column within that half.
+template <int DT, int D, int TPR, bool WR>
+__device__ __forceinline__ void store_row(const AttnArgs &a, int64_t row, int head, int t, const float *res) {
+    using RS = RowSplit<D, TPR>;
+    constexpr int CW = RS::CW;
+    if constexpr (WR) {
+        constexpr int HD = D / 2;  // head_dim of the real kv heads
+        static_assert(HD % CW == 0, "chunks do not straddle the halves");
+        const int half = head / a.real_group;
+#pragma unroll
+        for (int q = 0; q < RS::NCH; ++q) {
+            const int c0 = RS::col(t, q);
+            if (c0 / HD == half) store_out<DT, CW>(a.out, row * HD + (c0 - half * HD), res + q * CW);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < RS::NCH; ++q) store_out<DT, CW>(a.out, row * D + RS::col(t, q), res + q * CW);
+    }
+}
+
+template <int DT, int D, int TPR, int MB, bool WR>
 __device__ __forceinline__ void merge_pieces(const Seg &w, const AttnArgs &a, int r, int t) {
     using RS = RowSplit<D, TPR>;
     constexpr int EPT = RS::EPT, CW = RS::CW;
@@ -815,14 +850,13 @@ __device__ __forceinline__ void merge_pieces(const Seg &w, const AttnArgs &a, in
     const int qi = div_group(f, a);
     const int qh = f - qi * a.group;
     const int64_t row = (int64_t)(w.q_start + qi) * a.num_qo_heads + w.kv_head * a.group + qh;
-#pragma unroll
-    for (int q = 0; q < RS::NCH; ++q) store_out<DT, CW>(a.out, row * D + RS::col(t, q), acc + q * CW);
+    store_row<DT, D, TPR, WR>(a, row, w.kv_head * a.group + qh, t, acc);
     if (a.lse && t == 0) a.lse[row] = (M + fast_log2(L)) * kLn2;
 }
 
 // Fold of one segment across the waves (all waves call it at the same step), then the
 // output rows: final rows for a whole row block, device-scope fp32 partial rows for a piece.
-template <class T, int DT, int D, int NW>
+template <class T, int DT, int D, int NW, bool WR>
 __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, const Seg &cs, int k,
                                              float &m_run, float &l_run, f32x4 *o, int &npend,
                                              int wave, int col, int grp) {
@@ -866,8 +900,7 @@ __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, con
             const int qi = div_group(f, a);
             const int qh = f - qi * a.group;
             const int64_t row = (int64_t)(cs.q_start + qi) * a.num_qo_heads + cs.kv_head * a.group + qh;
-#pragma unroll
-            for (int q = 0; q < RS::NCH; ++q) store_out<DT, CW>(a.out, row * D + RS::col(t, q), res + q * CW);
+            store_row<DT, D, TPR, WR>(a, row, cs.kv_head * a.group + qh, t, res);
             if (a.lse && t == 0) a.lse[row] = lse2 * kLn2;
         } else {
 #pragma unroll
@@ -910,7 +943,7 @@ __device__ __forceinline__ void stage_rows(const lds_char *dst, const int32_t *r
 // The record and the pools come as separate leading arguments as well: those arrive in
 // SGPRs with the dispatch (kernel-argument preloading), so the record's loads go out at
 // once, beside the loads of the other arguments instead of after them.
-template <class T, int DT, int D, int NW, bool EARLY>
+template <class T, int DT, int D, int NW, bool EARLY, bool WR>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, const void *k_pool,
                                                       const void *v_pool, int hkv, const AttnArgs a) {
     static_assert(NW == 4 && NW <= kMaxWaves, "four waves per workgroup");
@@ -971,15 +1004,17 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     T::ring_init(ring, ring_b, lane, hkv);
     constexpr int kAhead = T::kTileFirst ? 1 : 0;  // ring slots issued before Q
     static_for<0, kAhead>([&](auto si) { T::ring_issue(ring, si, k_pool, v_pool, row_first[si]); });
-    T::q_stage(q_b, a, cs, lane);
+    T::template q_stage<WR>(q_b, a, cs, lane);
     stage_header(hdr_slot(seg_b + 1), a.segs, min(seg_b + 1, seg_e - 1), lane);
     stage_header(hdr_slot(seg_b + 2), a.segs, min(seg_b + 2, seg_e - 1), lane);
     stage_rows(rows_b, rows, 0, nsteps, lane);
     stage_rows(rows_b + 256, rows, 64, nsteps, lane);
     static_for<kAhead, PF>([&](auto si) { T::ring_issue(ring, si, k_pool, v_pool, row_first[si]); });
     wait_vm<(PF - kAhead) * kLoads>();
+    // whole-row blocks: block row h keeps the half of the operand row of its kv head
+    auto kv_half = [&](const RowInfo &x) { return WR ? x.qh / a.real_group : -1; };
     RowInfo ri = row_info(cs, a, col);
-    typename T::QOp qc = T::q_fetch(q_b, ri, col, grp);
+    typename T::QOp qc = T::q_fetch(q_b, ri, col, grp, kv_half(ri));
     int ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
     int full_end = seg_full_end(cs, a);
 
@@ -1001,12 +1036,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
         constexpr bool kRefill = decltype(refill)::value;
         wait_vm<PF * kLoads>();
         if (p0 == seg_end) {  // the same step in every wave: segment k is done
-            fold_segment<T, DT, D, NW>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);
+            fold_segment<T, DT, D, NW, WR>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);
             ++k;
             cs = seg_fields_lds(hdr_slot(k));
             seg_end = k + 1 < seg_e ? lds_int(hdr_slot(k + 1) + 4 * FL_WI_POS_BEGIN) : nsteps;
             ri = row_info(cs, a, col);
-            qc = T::q_fetch(q_b, ri, col, grp);
+            qc = T::q_fetch(q_b, ri, col, grp, kv_half(ri));
             ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
             full_end = seg_full_end(cs, a);
             wait_lds();  // the slot of header k - 2 is free
@@ -1017,7 +1052,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
             // group's refills, so they have landed at the next group's top
             const Seg ns = seg_fields_lds(hdr_slot(k + 1));
             wait_lds();  // this wave's reads of the Q rows are done
-            T::q_stage(q_b, a, ns, lane);
+            T::template q_stage<WR>(q_b, a, ns, lane);
         }
         int nrow[PF];  // pool rows of this group's refills
         if constexpr (kRefill) {
@@ -1060,7 +1095,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     int p0 = 0;
     for (; p0 + PF < nsteps; p0 += PF) group(p0, std::true_type{});
     group(p0, std::false_type{});
-    fold_segment<T, DT, D, NW>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);
+    fold_segment<T, DT, D, NW, WR>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);
 
     // ---- merge tickets of the partial pieces (at most the first and the last) -----------
     // The partial rows went out as device-scope stores; each wave waits for their
@@ -1104,11 +1139,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
             const Seg ps = pend_seg(i);
             if (ps.num_rows > kBlockRows / 2) {
                 const int r = threadIdx.x / TPR;
-                if (r < ps.num_rows) merge_pieces<DT, D, TPR, 8>(ps, a, r, threadIdx.x % TPR);
+                if (r < ps.num_rows) merge_pieces<DT, D, TPR, 8, WR>(ps, a, r, threadIdx.x % TPR);
             } else {  // up to 8 rows: twice the threads per row, up to 16 pieces per batch
                 constexpr int TPR2 = 2 * TPR;
                 const int r2 = threadIdx.x / TPR2;
-                if (r2 < ps.num_rows) merge_pieces<DT, D, TPR2, 16>(ps, a, r2, threadIdx.x % TPR2);
+                if (r2 < ps.num_rows) merge_pieces<DT, D, TPR2, 16, WR>(ps, a, r2, threadIdx.x % TPR2);
             }
         }
     }
@@ -1123,10 +1158,10 @@ struct TileFor<FL_F32, D> {
     using type = F32Tile<D>;
 };
 
-template <int DT, int D, int NW, bool EARLY>
+template <int DT, int D, int NW, bool EARLY, bool WR = false>
 hipError_t launch_t(int n, const AttnArgs &a, hipStream_t s) {  // n: workgroups
     using T = typename TileFor<DT, D>::type;
-    hipLaunchKernelGGL((attn_kernel<T, DT, D, NW, EARLY>), dim3(n), dim3(NW * 64), 0, s, a.wg_rec,
+    hipLaunchKernelGGL((attn_kernel<T, DT, D, NW, EARLY, WR>), dim3(n), dim3(NW * 64), 0, s, a.wg_rec,
                        a.k, a.v, a.num_kv_heads, a);
     return hipGetLastError();
 }
@@ -1143,9 +1178,15 @@ hipError_t launch_w(int waves, bool early, int n, const AttnArgs &a, hipStream_t
 
 }  // namespace
 
-int launch_attention(int dtype, int head_dim, int waves, bool early, int n, const AttnArgs &a,
-                     void *stream) {
+int launch_attention(int dtype, int head_dim, int waves, bool early, bool whole_rows, int n,
+                     const AttnArgs &a, void *stream) {
     hipStream_t s = (hipStream_t)stream;
+    if (whole_rows) {  // two kv heads of 64 as one row of 128 (refilled early, as at 128)
+        if (waves != 4 || head_dim != 128) return (int)hipErrorInvalidValue;
+        if (dtype == FL_BF16) return (int)launch_t<FL_BF16, 128, 4, true, true>(n, a, s);
+        if (dtype == FL_F16) return (int)launch_t<FL_F16, 128, 4, true, true>(n, a, s);
+        return (int)hipErrorInvalidValue;
+    }
     switch (dtype * 1000 + head_dim) {
     case FL_BF16 * 1000 + 64: return (int)launch_w<FL_BF16, 64>(waves, early, n, a, s);
     case FL_BF16 * 1000 + 128: return (int)launch_w<FL_BF16, 128>(waves, early, n, a, s);

@@ -55,6 +55,16 @@ constexpr int kOddHalfPercent = 20;
 #ifndef FL_CUT_TILES_MIXED
 #define FL_CUT_TILES_MIXED 0
 #endif
+// Whole-row tiles move twice the bytes of a per-kv-head tile, so the same fold and cut
+// costs are half as many of them.
+#ifndef FL_FOLD_TILES_WHOLE
+#define FL_FOLD_TILES_WHOLE 3
+#endif
+#ifndef FL_CUT_TILES_WHOLE
+#define FL_CUT_TILES_WHOLE 2
+#endif
+constexpr int kFoldCostWhole = kStreamTileCost * FL_FOLD_TILES_WHOLE;
+constexpr int kCutCostWhole = kStreamTileCost * FL_CUT_TILES_WHOLE;
 constexpr int kFoldCostDecode = kStreamTileCost * FL_FOLD_TILES_DECODE;
 constexpr int kCutCostDecode = kStreamTileCost * FL_CUT_TILES_DECODE;
 constexpr int kFoldCostMixed = kStreamTileCost * FL_FOLD_TILES_MIXED;
@@ -84,6 +94,10 @@ struct PlanLimits {
     int64_t seg_cap;              // segments one plan may hold
     int64_t group_cap;            // workgroups one plan may launch
     int64_t part_rows_cap;        // fp32 partial rows one plan may use
+    bool whole_rows_ok;           // decode-only steps may use whole-row blocks (Hkv * D = 128,
+                                  // Hq <= 16, 16-bit type, not switched off)
+    bool whole_rows_always;       // ... on every decode-only step, not only those with at
+                                  // least one query row per compute unit
 };
 
 struct PlanInput {
@@ -107,6 +121,8 @@ struct Plan {
     int32_t groups_per_cu = 1;      // workgroups per compute unit the shares were cut for
     int32_t num_segs = 0;
     int32_t num_merges = 0;
+    bool whole_rows = false;        // blocks hold every query head of a request and read whole
+                                    // token rows (one virtual kv head of Hkv * D values)
     int32_t max_splits = 0;
     int64_t part_rows = 0;
     std::vector<int32_t> append_rows;  // per query row: token row page * P + slot of the
@@ -143,13 +159,16 @@ struct AttnArgs {
     uint32_t group_magic;      // ceil(2^32 / group) (unused when group == 1)
     int32_t causal;
     float scale_log2;          // sm_scale * log2(e)
+    int32_t real_group;        // whole-row blocks: query heads per real kv head (the kv head
+                               // of block row h is h / real_group); otherwise unused
 };
 
 // Return hipSuccess or the launch error (as int to keep HIP headers out of this file).
 // early_refill: refill a K/V slot as soon as its tile is in registers (memory-bound steps)
 // rather than after the tile's arithmetic (steps bound by the arithmetic).
-int launch_attention(int dtype, int head_dim, int waves, bool early_refill, int num_groups,
-                     const AttnArgs &a, void *stream);
+// whole_rows: head_dim is the virtual row width Hkv * D (128) of whole-row blocks.
+int launch_attention(int dtype, int head_dim, int waves, bool early_refill, bool whole_rows,
+                     int num_groups, const AttnArgs &a, void *stream);
 
 // KV append: copy row r of k_new / v_new (row_bytes each, a multiple of 16) to token row
 // dst_rows[r] of k_pool / v_pool (kv_append.hip).

@@ -62,8 +62,7 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
     out = Plan();
     const int32_t B = in.batch;
     const int32_t P = lim.page_size;
-    const int32_t Hkv = lim.num_kv_heads;
-    const int32_t G = lim.num_qo_heads / lim.num_kv_heads;
+    const int32_t Hkv_real = lim.num_kv_heads;
     if (B < 0) return fail(err, FL_ERR_INVALID_ARG, "batch %lld < 0", B);
     if (B > lim.max_batch)
         return fail(err, FL_ERR_CAPACITY, "batch %lld exceeds max_batch %lld", B, lim.max_batch);
@@ -81,10 +80,10 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         return fail(err, FL_ERR_INVALID_ARG, "qo_indptr[0] = %lld, expected 0", in.qo_indptr[0]);
     if (in.num_pages <= 0 || in.num_pages > INT32_MAX)
         return fail(err, FL_ERR_INVALID_ARG, "num_pages %lld outside [1, 2^31)", in.num_pages);
-    if (in.num_pages * P * Hkv > INT32_MAX)
+    if (in.num_pages * P * Hkv_real > INT32_MAX)
         return fail(err, FL_ERR_UNSUPPORTED,
                     "pool of %lld pages x %lld slots x %lld kv heads exceeds 2^31 rows", in.num_pages,
-                    P, Hkv);
+                    P, Hkv_real);
 
     // ---- validate every request -----------------------------------------------------
     for (int32_t r = 0; r < B; ++r) {
@@ -163,13 +162,34 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         }
     }
 
+    // ---- block shape ------------------------------------------------------------------
+    // Decode-only steps may give each request one block of all its query heads over whole
+    // token rows: a virtual single kv head of Hkv * D values whose operand rows are zero
+    // outside the row's own kv head. The tiles then read every kv head's slice of a token
+    // row together (whole 4 KB pages at page size 16) at the same MFMA count.
+    // Measured (saturated-style decode, 300 tokens, 14/2 heads, d 64, bf16): whole rows take
+    // 10.98 vs 11.19 us at 256 requests and 18.97 vs 20.00 at 512, but at 128 requests they
+    // leave half the compute units idle (8.59 vs 7.17 us, one request per workgroup) or cut
+    // every request in two (10.41 us), so by default they need a request per compute unit.
+    bool decode_only = true;
+    int64_t decode_rows = 0;
+    for (int32_t r = 0; r < B && decode_only; ++r) {
+        const int32_t ql = in.qo_indptr ? in.qo_indptr[r + 1] - in.qo_indptr[r] : 1;
+        decode_only = ql <= 1;
+        decode_rows += ql;
+    }
+    out.whole_rows = lim.whole_rows_ok && decode_only &&
+                     (lim.whole_rows_always || decode_rows >= lim.num_cus);
+    const int32_t Hkv = out.whole_rows ? 1 : Hkv_real;
+    const int32_t G = out.whole_rows ? lim.num_qo_heads : lim.num_qo_heads / Hkv_real;
+
     // ---- row blocks -------------------------------------------------------------------
     // per kv head: the share of its row slice in odd 256-byte halves, in percent; 50 (no
     // tilt) unless token rows span whole 512-byte units
     const int64_t elem = lim.dtype == FL_F32 ? 4 : 2;
     const int64_t slice = (int64_t)lim.head_dim * elem, row_bytes = slice * Hkv;
     std::vector<int64_t> odd_pct(Hkv, 50);
-    if (row_bytes % 512 == 0)
+    if (row_bytes % 512 == 0 && !out.whole_rows)
         for (int32_t h = 0; h < Hkv; ++h) {
             int64_t odd = 0;
             for (int64_t x = h * slice; x < (h + 1) * slice; x += 16) odd += (x / 256) & 1;
@@ -232,8 +252,8 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
             prefill = in.qo_indptr && in.qo_indptr[r + 1] - in.qo_indptr[r] > 1;
         int gpc = lim.groups_per_cu;
         if (gpc <= 0) gpc = prefill && lim.head_dim <= 64 && lim.dtype != FL_F32 ? 2 : 1;
-        const int64_t kFoldCost = prefill ? kFoldCostMixed : kFoldCostDecode;
-        const int64_t kCutCost = prefill ? kCutCostMixed : kCutCostDecode;
+        const int64_t kFoldCost = prefill ? kFoldCostMixed : out.whole_rows ? kFoldCostWhole : kFoldCostDecode;
+        const int64_t kCutCost = prefill ? kCutCostMixed : out.whole_rows ? kCutCostWhole : kCutCostDecode;
         out.groups_per_cu = gpc;
         const int64_t want = (int64_t)lim.num_cus * gpc;
         const int64_t G_max = std::min(std::max<int64_t>(1, std::min(want, ceil_div(T, lim.min_group_tiles))), T);

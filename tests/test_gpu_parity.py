@@ -33,7 +33,23 @@ def test_tiny_decode():
 
 
 def test_saturated_decode_full():
-    _check(W.saturated_decode())
+    _check(W.saturated_decode())      # one block per kv head (128 requests < 256 compute units)
+
+
+def test_saturated_decode_full_whole_rows():
+    _check(W.saturated_decode(), what="saturated_decode in whole rows", whole_rows=1)
+
+
+def test_tiny_decode_whole_rows():
+    _check(W.tiny_decode(), what="tiny_decode in whole rows", whole_rows=1)
+
+
+def test_decode_512_requests_whole_rows_by_default():
+    """A decode batch with a request per compute unit takes whole rows without asking."""
+    b = W.make_batch([300] * 512, num_qo_heads=14, num_kv_heads=2, head_dim=64, page_size=16,
+                     dtype="bf16", num_pages=512 * 19 + 40, seed=9)
+    d, _ = _check(b, what="512 x 300 decode")
+    assert (d.h.work_items()[:, fl.WORK_ITEM_FIELDS.index("kv_head")] == -1).all()
 
 
 def test_mixed_length_decode_full():
@@ -54,6 +70,16 @@ def test_split_counts(splits):
     b = W.make_batch([1, 17, 100, 300, 777], [1, 1, 1, 40, 1], num_qo_heads=14, num_kv_heads=2,
                      head_dim=64, page_size=16, dtype="bf16", seed=21, num_pages=120)
     _check(b, num_splits=splits, what=f"splits{splits}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 1000])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_split_counts_whole_rows(splits, dtype):
+    """Decode-only batch in whole-row blocks: cut pieces write 128-wide partial rows and the
+    merge stores each head's own half."""
+    b = W.make_batch([1, 17, 100, 300, 777, 64], num_qo_heads=12 if dtype == "f16" else 14,
+                     num_kv_heads=2, head_dim=64, page_size=16, dtype=dtype, seed=22, num_pages=90)
+    _check(b, num_splits=splits, what=f"whole-rows splits{splits} {dtype}", whole_rows=1)
 
 
 # ---- dtype / head_dim / page_size / group coverage ----------------------------------------
@@ -173,14 +199,17 @@ def _plant(b, r, t, rows=None):
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("P", [16, 64, 256])
 @pytest.mark.parametrize("splits", [0, 1, 4])
-def test_needles_bit_exact(dtype, P, splits):
+@pytest.mark.parametrize("whole_rows", [1, -1])
+def test_needles_bit_exact(dtype, P, splits, whole_rows):
+    if dtype == "f32" and whole_rows == 1:
+        pytest.skip("whole-row blocks are 16-bit only; fp32 runs one block per kv head")
     kv = [1, P, P + 1, 3 * P - 1, 300, 1000]
     spots = [0, P - 1, P, 3 * P - 2, 299, 517]
     b = _needle_batch(kv, None, P, dtype)
     for r, t in enumerate(spots):
         _plant(b, r, t)
-    announce(f"needles dtype={dtype} P={P} splits={splits}")
-    d = DeviceBatch(b, num_splits=splits)
+    announce(f"needles dtype={dtype} P={P} splits={splits} whole_rows={whole_rows}")
+    d = DeviceBatch(b, num_splits=splits, whole_rows=whole_rows)
     out, _ = d.run()
     got = to_host_bits(out, dtype)
     for r, t in enumerate(spots):

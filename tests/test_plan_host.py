@@ -40,10 +40,14 @@ def plan_batch(h, b, num_splits=0, causal=None):
 
 def check_coverage(items, b, causal=True):
     """Every (request, kv head, flattened row) sees exactly its causal key range, once, in
-    16-aligned non-empty slices; split items own disjoint partial rows."""
-    G = b.group
+    16-aligned non-empty slices; split items own disjoint partial rows. Whole-row items
+    (kv_head -1) cover every kv head at once, their rows flattened over all query heads."""
     idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
     col = lambda n: items[:, idx[n]]
+    whole = bool((col("kv_head") == -1).any())
+    assert not whole or (col("kv_head") == -1).all()
+    G = b.num_qo_heads if whole else b.group
+    kv_heads = [-1] if whole else range(b.num_kv_heads)
     assert (col("num_rows") >= 1).all() and (col("num_rows") <= 16).all()
     assert (col("tok_end") > col("tok_begin")).all()
     assert (col("tok_begin") % 16 == 0).all()
@@ -74,7 +78,7 @@ def check_coverage(items, b, causal=True):
         for f in range(f0, f0 + nr):
             seen_rows[(r, h, f)] = seen_rows.get((r, h, f), 0) + 1
     for r in range(b.batch_size):
-        for h in range(b.num_kv_heads):
+        for h in kv_heads:
             for f in range(int(b.qo_lens[r]) * G):
                 assert seen_rows.get((r, h, f)) == 1, (r, h, f)
     # a workgroup holds at most two cut pieces, its first and its last segment (the kernel
@@ -166,7 +170,7 @@ def test_long_histories_are_spread_and_shares_are_balanced():
     lens = W.long_context_lengths(0)
     b = W.make_batch(lens, num_qo_heads=12, num_kv_heads=2, head_dim=64, page_size=256,
                      dtype="f16", num_pages=1200, poison=False)
-    h = host_handle(Hq=12, Hkv=2, P=256, dtype="f16", max_pages=4096, num_cus=256)
+    h = host_handle(Hq=12, Hkv=2, P=256, dtype="f16", max_pages=4096, num_cus=256, whole_rows=-1)
     items = plan_batch(h, b)
     idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
     kvl = items[:, idx["kv_len"]]
@@ -210,7 +214,8 @@ def test_odd_half_kv_heads_get_smaller_shares():
     # with d 64 the rows are 256 bytes, each head's slice spans both halves: no tilt
     b2 = W.make_batch(lens, num_qo_heads=12, num_kv_heads=2, head_dim=64, page_size=256,
                       dtype="f16", num_pages=1100, poison=False)
-    h2 = host_handle(Hq=12, Hkv=2, D=64, P=256, dtype="f16", max_pages=4096, num_cus=256)
+    h2 = host_handle(Hq=12, Hkv=2, D=64, P=256, dtype="f16", max_pages=4096, num_cus=256,
+                     whole_rows=-1)
     it2 = plan_batch(h2, b2)
     t2 = -(-(it2[:, idx["tok_end"]] - it2[:, idx["tok_begin"]]) // 16)
     w2 = it2[:, idx["num_splits"]] > 2
@@ -220,11 +225,42 @@ def test_odd_half_kv_heads_get_smaller_shares():
 
 def test_decode_batch_of_equal_histories_is_not_split():
     b = W.saturated_decode()
-    h = host_handle(num_cus=256)
+    h = host_handle(num_cus=256, whole_rows=-1)
     items = plan_batch(h, b)
     idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
     assert (items[:, idx["num_splits"]] == 1).all()
     assert len(items) == 256 and (tiles_per_group(items) == 19).all()
+
+
+def test_whole_rows_only_where_they_apply():
+    """Decode-only steps with Hkv * D = 128, Hq <= 16 and a 16-bit type take whole-row
+    blocks (all query heads of a request, every kv head's slice of each token row); steps
+    with a prefill chunk, fp32, wider rows, more heads, or whole_rows = -1 do not."""
+    idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
+    b = W.saturated_decode()
+    items = plan_batch(host_handle(num_cus=256, whole_rows=1), b)
+    assert (items[:, idx["kv_head"]] == -1).all() and (items[:, idx["num_rows"]] == 14).all()
+    check_coverage(items, b)
+    assert (plan_batch(host_handle(num_cus=256, whole_rows=-1), b)[:, idx["kv_head"]] >= 0).all()
+    # by default only with a query row per compute unit: 128 requests on 256 units do not,
+    # on 128 units they do
+    assert (plan_batch(host_handle(num_cus=256), b)[:, idx["kv_head"]] >= 0).all()
+    assert (plan_batch(host_handle(num_cus=128), b)[:, idx["kv_head"]] == -1).all()
+    r = W.make_batch([40, 300, 17], [5, 1, 1], num_qo_heads=14, num_kv_heads=2, head_dim=64,
+                     page_size=16)
+    assert (plan_batch(host_handle(whole_rows=1), r)[:, idx["kv_head"]] >= 0).all()  # prefill rows
+    for kw, shape in ((dict(dtype="f32"), dict(dtype="f32")),                    # fp32
+                      (dict(D=128), dict(head_dim=128)),                         # 2 x 128 wide
+                      (dict(Hq=32), dict(num_qo_heads=32))):                     # 32 heads
+        bb = W.make_batch([40, 300, 17], **{**dict(num_qo_heads=14, num_kv_heads=2, head_dim=64,
+                                                   page_size=16), **shape})
+        it = plan_batch(host_handle(whole_rows=1, **kw), bb)
+        assert (it[:, idx["kv_head"]] >= 0).all(), kw
+        check_coverage(it, bb)
+    # one kv head of 128 already reads whole rows: no change there either
+    bb = W.make_batch([40, 300], num_qo_heads=8, num_kv_heads=1, head_dim=128, page_size=16)
+    assert (plan_batch(host_handle(Hq=8, Hkv=1, D=128, whole_rows=1), bb)[:, idx["kv_head"]] == 0).all()
+    _expect(fl.FL_ERR_INVALID_ARG, host_handle, whole_rows=2)
 
 
 def test_forced_splits_are_capped_by_tiles():
