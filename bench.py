@@ -160,10 +160,13 @@ def summarize_profiles(workload: str, kt: str, pf: str, pw: str, cf: str, cw: st
     benchmark (pf, pw) and of a plain copy of known size (cf, cw)."""
     import glob
     stats = None
+    others = []
     for path in glob.glob(os.path.join(kt, "**", "*kernel_stats.csv"), recursive=True):
         for r in _csv_rows(path):
             if "attn_kernel" in r["Name"]:
                 stats = r
+            else:
+                others.append(r)
     if stats is None:
         raise SystemExit(f"no attention kernel in the kernel stats under {kt}")
     fetch, nf = _counter_per_dispatch(pf, "attn_kernel", "FETCH_SIZE")
@@ -194,7 +197,13 @@ def summarize_profiles(workload: str, kt: str, pf: str, pw: str, cf: str, cw: st
           "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
           "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|",
           f"| {stats['Name'][:80]} | {stats['Calls']} | {avg_ns / 1e3:.3f} | "
-          f"{float(stats['MinNs']) / 1e3:.3f} | {float(stats['MaxNs']) / 1e3:.3f} |", "",
+          f"{float(stats['MinNs']) / 1e3:.3f} | {float(stats['MaxNs']) / 1e3:.3f} |"] + [
+          f"| {r['Name'][:80]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+          f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} |"
+          for r in sorted(others, key=lambda r: -float(r["TotalDurationNs"]))[:6]] + ["",
+          "The attention kernel is one launch per layer; kv_append_kernel is the same step's KV "
+          "append (one launch per layer, timed after the attention runs); stage_copy_kernel "
+          "copies each plan's metadata (one launch per step).", "",
           f"Algorithmic K+V bytes per call: {algo} -> {algo / avg_ns:.1f} GB/s at the average "
           f"duration ({algo / avg_ns / 8000.0 * 100:.1f}% of 8 TB/s).", "",
           "## HBM traffic (rocprofv3 --pmc, one counter per run)", "",
