@@ -88,6 +88,15 @@ def cpu_baseline(b, gpu_out0, budget_s: float):
         if el >= budget_s or (calls >= 3 and el + el / calls > 1.5 * budget_s):
             break
     per_call = el / calls
+    # the same oracle on one host thread, over a few seconds
+    calls1, t1 = 0, time.perf_counter()
+    while True:
+        oracle.attention(b, num_threads=1)
+        calls1 += 1
+        el1 = time.perf_counter() - t1
+        if el1 >= min(3.0, budget_s) or calls1 >= 1000:
+            break
+    per_call1 = el1 / calls1
     got = gpu_out0.to(torch.float64).cpu().numpy()
     err = float(np.abs(got - ref).max())
     return {"value": round(b.kv_bytes() / per_call / 1e9, 3), "unit": "GB/s",
@@ -95,7 +104,52 @@ def cpu_baseline(b, gpu_out0, budget_s: float):
             "sample": f"the full {b.name} batch (one layer call), {calls} repeats over "
                       f"{el:.1f} s, {per_call * 1e3:.2f} ms per call (first call {first * 1e3:.1f} ms)",
             "ms_per_call": round(per_call * 1e3, 4),
+            "one_thread": {"ms_per_call": round(per_call1 * 1e3, 3),
+                           "value": round(b.kv_bytes() / per_call1 / 1e9, 3), "calls": calls1},
             "gpu_vs_oracle_max_abs": err}
+
+
+def cold_call_us(h, q, k, v, out, stream, flush_mib: int = 1024, reps: int = 5):
+    """One layer call after the caches were flushed: a 1 GiB buffer is written (more than the
+    256 MB Infinity Cache and the L2s hold), then a single eager call is timed with events on
+    the launch stream; median of `reps`."""
+    import torch
+    junk = torch.empty(flush_mib << 18, dtype=torch.float32, device="cuda:0")
+    ts = []
+    for _ in range(reps):
+        junk.fill_(1.0)
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        h.run(q, k, v, out)
+        e.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(e) * 1e3)
+    del junk
+    return sorted(ts)[len(ts) // 2]
+
+
+def stream_probe_gbs(mib: int = 1024, reps: int = 10):
+    """The streaming rate this GPU sustains on a plain device copy of `mib` MiB (bytes read
+    plus bytes written per second, median of `reps`): a measured ceiling to set beside the
+    8 TB/s specification. (torch's sum reads the same buffer slower than the copy moves
+    twice the bytes, so it is no read ceiling.)"""
+    import torch
+    x = torch.ones(mib << 18, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+
+    def median_s(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(e) * 1e-3)
+        return sorted(ts)[len(ts) // 2]
+    return 2 * x.numel() * 4 / median_s(lambda: y.copy_(x)) / 1e9
 
 
 def time_kv_append(h, b, ks, vs, L: int, stream, replays: int = 20):
@@ -443,6 +497,12 @@ def main(argv=None):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
     }
+    cold = cold_call_us(h, q, ks[0], vs[0], outs[0], stream)
+    probe = stream_probe_gbs()
+    res["cold_call_us"] = round(cold, 3)
+    res["stream_probe"] = {"GB_per_s": round(probe, 1),
+                           "kind": "device copy of 1 GiB, bytes read + written per second",
+                           "achieved_frac_of_probe": round(achieved / probe, 4)}
     res["kv_append"] = time_kv_append(h, b, ks, vs, L, stream)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(b, outs[0], args.cpu_budget)

@@ -174,9 +174,11 @@ int oracle_paged_attention(int dtype, int batch, const int32_t *qo_indptr,
     int status = ORACLE_OK;
 
 #ifdef _OPENMP
-    if (num_threads > 0)
-        omp_set_num_threads(num_threads);
-#pragma omp parallel for schedule(dynamic, 1)
+    /* this call's thread count only; the process default stays as it was */
+    const int nt = num_threads > 0 ? num_threads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+#else
+    (void)num_threads;
 #endif
     for (int pr = 0; pr < pairs; ++pr) {
         const int r = pr / Hkv, g = pr % Hkv;
