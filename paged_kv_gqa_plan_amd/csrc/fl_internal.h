@@ -69,6 +69,13 @@ constexpr int kFoldCostDecode = kStreamTileCost * FL_FOLD_TILES_DECODE;
 constexpr int kCutCostDecode = kStreamTileCost * FL_CUT_TILES_DECODE;
 constexpr int kFoldCostMixed = kStreamTileCost * FL_FOLD_TILES_MIXED;
 constexpr int kCutCostMixed = kStreamTileCost * FL_CUT_TILES_MIXED;
+// XCDs of the GPU (MI355X: 8 of 32 compute units), which take a launch's workgroups in
+// turn; the plan places runs of neighbouring shares on one XCD (one L2).
+constexpr int kXcds = 8;
+#ifndef FL_XCD_AWARE
+#define FL_XCD_AWARE 1
+#endif
+constexpr bool kXcdAwareLayout = FL_XCD_AWARE != 0;
 // Per-workgroup record (int32): the first segment's header, the segment range, the step
 // range, the first segment's end step and the pool rows of every wave's first kRingDepth
 // steps, so every load a workgroup issues first (Q, K/V, step rows) depends on this record

@@ -347,8 +347,24 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
     out.step_rows.assign((size_t)total, 0);
     size_t k = 0;
     int64_t off = 0;
+    // Workgroup b runs on XCD b % kXcds (workgroups are handed to the XCDs in turn), and
+    // each XCD has its own L2. Shares next to each other in the tile sequence hold
+    // neighbouring row blocks, which for a prefill chunk read the same K/V, so share s goes
+    // to the workgroup that puts runs of consecutive shares on one XCD: the first
+    // ceil(G / kXcds) shares on XCD 0, the next on XCD 1, and so on.
+    const auto workgroup_of = [&](int64_t share) -> int64_t {
+        if (!kXcdAwareLayout) return share;
+        int64_t first = 0;
+        for (int64_t x = 0; x < kXcds; ++x) {
+            const int64_t n_x = (G_wg - x + kXcds - 1) / kXcds;  // workgroups on XCD x
+            if (share < first + n_x) return (share - first) * kXcds + x;
+            first += n_x;
+        }
+        return share;  // not reached
+    };
     for (int64_t g = 0; g < G_wg; ++g) {
-        int32_t *rec = &out.wg_rec[g * kRecInts];
+        const int64_t wg = workgroup_of(g);
+        int32_t *rec = &out.wg_rec[wg * kRecInts];
         size_t k_end = k;
         int64_t steps = 0;
         while (k_end < pieces.size() && pieces[k_end].group == g) steps += seg_steps[k_end++];
@@ -384,7 +400,7 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
             it[FL_WI_SPLIT] = piece_idx[k];
             it[FL_WI_NUM_SPLITS] = npieces[pc.block];
             it[FL_WI_MERGE] = merge_of[pc.block];
-            it[FL_WI_GROUP] = (int32_t)g;
+            it[FL_WI_GROUP] = (int32_t)wg;
             it[FL_WI_POS_BEGIN] = (int32_t)pos;
             const int32_t *pages = in.kv_indices + in.kv_indptr[bl.req];
             const int64_t nt = pc.hi - pc.lo;

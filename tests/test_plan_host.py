@@ -404,3 +404,20 @@ def test_append_on_empty_plan_and_host_handle():
     assert h.append_slots().size == 0
     msg = _expect(fl.FL_ERR_UNSUPPORTED, fl.fl_paged_kv_append, h.handle, 16, 16, 16, 16)
     assert "host-only" in msg
+
+
+def test_neighbouring_shares_share_an_xcd():
+    """Workgroup b runs on XCD b % 8: the plan hands runs of consecutive shares (neighbouring
+    row blocks, which for a prefill chunk read the same K/V) to one XCD, in equal numbers."""
+    b = W.ragged_mixed_step()
+    h = host_handle(num_cus=256)
+    items = plan_batch(h, b)
+    idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
+    g = items[:, idx["group"]]
+    order = g[np.r_[True, g[1:] != g[:-1]]]          # workgroups in share order
+    n = h.info()[1]
+    assert sorted(order.tolist()) == list(range(n))   # a permutation of the workgroups
+    xcd = order % 8
+    assert (np.diff(xcd) >= 0).all()                  # XCD 0's run, then XCD 1's, ...
+    counts = np.bincount(xcd, minlength=8)
+    assert counts.max() - counts.min() <= 1
