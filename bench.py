@@ -187,6 +187,51 @@ def time_kv_append(h, b, ks, vs, L: int, stream, replays: int = 20):
             "launch": "hip_graph", "layers": L}
 
 
+def time_append_attention(h, b, q, ks, vs, outs, L: int, stream, replays: int = 20):
+    """A layer's KV append plus its attention, per layer: one fl_paged_attn_run_append call
+    (one launch on decode-only 16-bit plans) against fl_paged_kv_append then
+    fl_paged_attn_run, each as L calls captured in one HIP graph. Timed after the attention
+    measurement (both overwrite the new tokens' slots)."""
+    import numpy as np
+    import torch
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(8)
+    shape = (b.rows, b.num_kv_heads, b.head_dim)
+    kn = [torch.randn(shape, dtype=ks[0].dtype, device="cuda:0", generator=gen) for _ in range(L)]
+    vn = [torch.randn(shape, dtype=ks[0].dtype, device="cuda:0", generator=gen) for _ in range(L)]
+
+    def graph_us(body):
+        body()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(replays)]
+        for a, e in ev:
+            a.record(stream)
+            g.replay()
+            e.record(stream)
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(e) / L * 1e3 for a, e in ev)
+        return us[len(us) // 2]
+
+    def fused():
+        for l in range(L):
+            h.run_append(q, kn[l], vn[l], ks[l], vs[l], outs[l])
+
+    def separate():
+        for l in range(L):
+            h.append(kn[l], vn[l], ks[l], vs[l])
+            h.run(q, ks[l], vs[l], outs[l])
+    f_us, s_us = graph_us(fused), graph_us(separate)
+    one_launch = all(x == 1 for x in np.diff(b.qo_indptr)) and b.dtype != "f32"
+    return {"fused_us_per_layer": round(f_us, 3), "separate_us_per_layer": round(s_us, 3),
+            "fused_launches_per_layer": 1 if one_launch else 2, "launch": "hip_graph", "layers": L}
+
+
 def _csv_rows(path):
     import csv
     with open(path, newline="") as f:
@@ -497,6 +542,7 @@ def main(argv=None):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
     }
+    out0 = outs[0].clone()  # layer 0's result, before the extra legs below overwrite it
     cold = cold_call_us(h, q, ks[0], vs[0], outs[0], stream)
     probe = stream_probe_gbs()
     res["cold_call_us"] = round(cold, 3)
@@ -504,8 +550,9 @@ def main(argv=None):
                            "kind": "device copy of 1 GiB, bytes read + written per second",
                            "achieved_frac_of_probe": round(achieved / probe, 4)}
     res["kv_append"] = time_kv_append(h, b, ks, vs, L, stream)
+    res["append_attention"] = time_append_attention(h, b, q, ks, vs, outs, L, stream)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(b, outs[0], args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(b, out0, args.cpu_budget)
     print(json.dumps(res), flush=True)
     h.close()
     return 0

@@ -179,6 +179,23 @@ fl_status fl_paged_kv_append(fl_handle h, const void *k_new, const void *v_new, 
                              void *v_pool, void *stream);
 
 /*
+ * Append one layer's new K/V rows and compute that layer's attention in one call: the
+ * result equals fl_paged_kv_append followed by fl_paged_attn_run (same pointers, same
+ * plan), up to the floating-point summation order. On decode-only plans (every request has
+ * at most one query row) in a 16-bit type it is one kernel launch: the new token is the
+ * newest key of its request, so the workgroup whose tiles hold that key takes its K and V
+ * from k_new / v_new instead of the pool and also writes them to the pool for later steps
+ * (flashlet README, design bullets: the NHD pool is written in place before attention reads
+ * it; one launch less per layer). Other plans (prefill chunks, whose new keys many
+ * workgroups read; fp32) make the two launches in order.
+ * Device pointers as for fl_paged_kv_append and fl_paged_attn_run; all 16-byte aligned.
+ * Errors: those of the two calls (FL_ERR_INVALID_ARG when the plan has no valid append
+ * slots). Enqueues on `stream`; never synchronises or allocates (graph-capturable).
+ */
+fl_status fl_paged_attn_run_append(fl_handle h, const void *q, const void *k_new, const void *v_new,
+                                   void *k_pool, void *v_pool, void *out, float *lse, void *stream);
+
+/*
  * Copy the current plan's append destinations to host memory: for each query row, the
  * token row page * page_size + slot that fl_paged_kv_append writes it to. *num_rows
  * receives the row count; at most `capacity` entries are written. Works on host-only

@@ -48,7 +48,8 @@ class FlError(RuntimeError):
 
 
 EXPORTED = ("fl_paged_attn_create", "fl_paged_attn_destroy", "fl_paged_attn_plan",
-            "fl_paged_attn_run", "fl_paged_kv_append", "fl_paged_kv_append_slots",
+            "fl_paged_attn_run", "fl_paged_kv_append", "fl_paged_attn_run_append",
+            "fl_paged_kv_append_slots",
             "fl_paged_attn_plan_info",
             "fl_paged_attn_get_work_items", "fl_page_pool_create", "fl_page_pool_destroy",
             "fl_page_pool_alloc", "fl_page_pool_reserve", "fl_page_pool_retain",
@@ -74,6 +75,7 @@ def load_library(path: Optional[str] = None):
     lib.fl_paged_attn_plan.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, ctypes.c_float, i32, vp]
     lib.fl_paged_attn_run.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.fl_paged_kv_append.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.fl_paged_attn_run_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fl_paged_kv_append_slots.argtypes = [vp, vp, i32, ctypes.POINTER(i32)]
     lib.fl_paged_attn_plan_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                             ctypes.POINTER(i32), ctypes.POINTER(i64)]
@@ -153,6 +155,16 @@ def fl_paged_kv_append(h, k_new: int, v_new: int, k_pool: int, v_pool: int,
                                              ctypes.c_void_p(k_pool), ctypes.c_void_p(v_pool),
                                              ctypes.c_void_p(int(stream))),
            "fl_paged_kv_append")
+
+
+def fl_paged_attn_run_append(h, q: int, k_new: int, v_new: int, k_pool: int, v_pool: int, out: int,
+                             lse: Optional[int] = None, stream: int = 0) -> None:
+    """Device pointers as integers: append the new K/V rows and attend, in one launch on
+    decode-only 16-bit plans."""
+    _check(load_library().fl_paged_attn_run_append(
+        h, ctypes.c_void_p(q), ctypes.c_void_p(k_new), ctypes.c_void_p(v_new), ctypes.c_void_p(k_pool),
+        ctypes.c_void_p(v_pool), ctypes.c_void_p(out), ctypes.c_void_p(lse or 0),
+        ctypes.c_void_p(int(stream))), "fl_paged_attn_run_append")
 
 
 def fl_paged_kv_append_slots(h) -> np.ndarray:
@@ -237,6 +249,11 @@ class PagedAttention:
     def append(self, k_new, v_new, k_pool, v_pool, stream=None):
         fl_paged_kv_append(self.handle, k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
                            v_pool.data_ptr(), self._stream(stream))
+
+    def run_append(self, q, k_new, v_new, k_pool, v_pool, out, lse=None, stream=None):
+        fl_paged_attn_run_append(self.handle, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                 k_pool.data_ptr(), v_pool.data_ptr(), out.data_ptr(),
+                                 None if lse is None else lse.data_ptr(), self._stream(stream))
 
     def append_slots(self) -> np.ndarray:
         return fl_paged_kv_append_slots(self.handle)

@@ -125,6 +125,34 @@ void release(fl_paged_attn *h) {
     delete h;
 }
 
+// Kernel arguments of the current plan (whole-row blocks: one virtual kv head of Hkv * D
+// values shared by every query head).
+fl::AttnArgs attn_args(const fl_paged_attn *h, const void *q, const void *k_pool, const void *v_pool,
+                       void *out, float *lse) {
+    const Plan &p = h->plan;
+    fl::AttnArgs a{};
+    a.segs = (const int32_t *)h->d_meta;
+    a.wg_rec = (const int32_t *)(h->d_meta + h->off_wg_rec);
+    a.step_rows = (const int32_t *)(h->d_meta + h->off_steps);
+    a.tickets = (int32_t *)(h->d_meta + h->off_tickets);
+    a.q = q;
+    a.k = k_pool;
+    a.v = v_pool;
+    a.out = out;
+    a.lse = lse;
+    a.part_o = h->d_part_o;
+    a.part_lse = h->d_part_lse;
+    a.num_qo_heads = h->cfg.num_qo_heads;
+    const int32_t group = p.whole_rows ? h->cfg.num_qo_heads : h->group;
+    a.num_kv_heads = p.whole_rows ? 1 : h->cfg.num_kv_heads;
+    a.group = group;
+    a.group_magic = group > 1 ? (uint32_t)(((1ull << 32) + group - 1) / group) : 0u;
+    a.real_group = h->group;
+    a.causal = h->causal;
+    a.scale_log2 = h->scale_log2;
+    return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -314,32 +342,43 @@ fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, cons
     if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)out) & 15)
         return set_err(FL_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
 
-    fl::AttnArgs a{};
-    a.segs = (const int32_t *)h->d_meta;
-    a.wg_rec = (const int32_t *)(h->d_meta + h->off_wg_rec);
-    a.step_rows = (const int32_t *)(h->d_meta + h->off_steps);
-    a.tickets = (int32_t *)(h->d_meta + h->off_tickets);
-    a.q = q;
-    a.k = k_pool;
-    a.v = v_pool;
-    a.out = out;
-    a.lse = lse;
-    a.part_o = h->d_part_o;
-    a.part_lse = h->d_part_lse;
-    a.num_qo_heads = h->cfg.num_qo_heads;
-    // whole-row blocks: one virtual kv head of Hkv * D values shared by every query head
-    const int32_t group = p.whole_rows ? h->cfg.num_qo_heads : h->group;
-    a.num_kv_heads = p.whole_rows ? 1 : h->cfg.num_kv_heads;
-    a.group = group;
-    a.group_magic = group > 1 ? (uint32_t)(((1ull << 32) + group - 1) / group) : 0u;
-    a.real_group = h->group;
-    a.causal = h->causal;
-    a.scale_log2 = h->scale_log2;
+    const fl::AttnArgs a = attn_args(h, q, k_pool, v_pool, out, lse);
     const int head_dim = p.whole_rows ? h->cfg.num_kv_heads * h->cfg.head_dim : h->cfg.head_dim;
     // two workgroups per compute unit are chosen for steps bound by the per-tile arithmetic
     const int e = fl::launch_attention(h->cfg.dtype, head_dim, h->waves, p.groups_per_cu == 1,
-                                       p.whole_rows, p.num_groups, a, stream);
+                                       p.whole_rows, false, p.num_groups, a, stream);
     if (e != (int)hipSuccess) return hip_err((hipError_t)e, "attention launch");
+    return FL_OK;
+}
+
+fl_status fl_paged_attn_run_append(fl_handle h, const void *q, const void *k_new, const void *v_new,
+                                   void *k_pool, void *v_pool, void *out, float *lse, void *stream) {
+    g_last_error.clear();
+    if (!h) return set_err(FL_ERR_INVALID_ARG, "handle is NULL");
+    if (h->host_only) return set_err(FL_ERR_UNSUPPORTED, "run_append on a host-only handle");
+    if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "run_append before a successful plan()");
+    const Plan &p = h->plan;
+    if (!p.append_ok) return set_err(FL_ERR_INVALID_ARG, "the plan has no append slots: " + p.append_err);
+    if (p.num_groups == 0) return FL_OK;
+    if (!p.decode_only || h->cfg.dtype == FL_F32) {
+        // a prefill chunk's new keys are read by many workgroups: append first, then attend
+        fl_status st = fl_paged_kv_append(h, k_new, v_new, k_pool, v_pool, stream);
+        if (st != FL_OK) return st;
+        return fl_paged_attn_run(h, q, k_pool, v_pool, out, lse, stream);
+    }
+    if (!q || !k_new || !v_new || !k_pool || !v_pool || !out)
+        return set_err(FL_ERR_INVALID_ARG, "q, k_new, v_new, k_pool, v_pool and out must not be NULL");
+    if (((uintptr_t)q | (uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_pool | (uintptr_t)v_pool |
+         (uintptr_t)out) & 15)
+        return set_err(FL_ERR_INVALID_ARG, "q, k_new, v_new, k_pool, v_pool and out must be 16-byte aligned");
+    fl::AttnArgs a = attn_args(h, q, k_pool, v_pool, out, lse);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.append_rows = (const int32_t *)(h->d_meta + h->off_append);
+    const int head_dim = p.whole_rows ? h->cfg.num_kv_heads * h->cfg.head_dim : h->cfg.head_dim;
+    const int e = fl::launch_attention(h->cfg.dtype, head_dim, h->waves, true, p.whole_rows, true,
+                                       p.num_groups, a, stream);
+    if (e != (int)hipSuccess) return hip_err((hipError_t)e, "attention + append launch");
     return FL_OK;
 }
 

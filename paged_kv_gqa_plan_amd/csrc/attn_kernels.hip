@@ -509,12 +509,38 @@ struct HalfTile {
     // 128 (2-6%), slower at 64 (where the second tile then leaves later).
     static constexpr bool kTileFirst = D >= 128;
 
+    // nrow, kt: with a fused append, the tile's key kt (0..15; -1: none) is the step's new
+    // token, whose K and V rows sit in LDS at nrow and nrow + 256 (its pool slot may not hold
+    // them yet): the lanes of that key take their operand pieces from there instead.
     __device__ static void compute(const Frag &f, const QOp &q, int t0, int col, int grp, int tok_end,
                                    int limit, bool full, float scale_log2, float &m_run, float &l_run,
-                                   f32x4 *o) {
+                                   f32x4 *o, const lds_char *nrow = nullptr, int kt = -1) {
+        u32x4 kk[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kk[c] = f.k[c];
+        u32x2 vt[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) vt[j] = f.vt[j];
+        if (kt >= 0) {  // wave-uniform
+            if (col == kt) {  // K piece 4c + grp of the key: d = 32c + 8grp .. +7
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    kk[c] = *(const __attribute__((address_space(3))) u32x4 *)(nrow + 16 * (4 * c + grp));
+            }
+            if (grp == (kt >> 2)) {  // element kt % 4 of V block j: column 32(j/2) + 8(i/4) + 4(j%2) + i%4
+                const int e = kt & 3;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int d = 32 * (j >> 1) + 8 * (col >> 2) + 4 * (j & 1) + (col & 3);
+                    const uint32_t val = *(const __attribute__((address_space(3))) uint16_t *)(nrow + 256 + 2 * d);
+                    const uint32_t w = vt[j][e >> 1];
+                    vt[j][e >> 1] = (e & 1) ? ((w & 0xFFFFu) | (val << 16)) : ((w & 0xFFFF0000u) | val);
+                }
+            }
+        }
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) s = H::mma_k32(f.k[c], q.q[c], s);
+        for (int c = 0; c < NC; ++c) s = H::mma_k32(kk[c], q.q[c], s);
         float p[4], alpha;
         bool rescaled;
         softmax_tile(s, t0, grp, tok_end, limit, full, scale_log2, m_run, l_run, p, alpha, rescaled);
@@ -529,9 +555,6 @@ struct HalfTile {
         const uint32_t l01 = H::pack(p[0] - H::lo_f(h01), p[1] - H::hi_f(h01));
         const uint32_t l23 = H::pack(p[2] - H::lo_f(h23), p[3] - H::hi_f(h23));
         // keys at or past tok_end may hold anything (NaN included): their V becomes 0
-        u32x2 vt[NJ];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) vt[j] = f.vt[j];
         if (t0 + kTileTokens > tok_end) {
             const int k0 = t0 + 4 * grp;
             const u32x2 vmask = {(k0 < tok_end ? 0xFFFFu : 0u) | (k0 + 1 < tok_end ? 0xFFFF0000u : 0u),
@@ -649,7 +672,7 @@ struct F32Tile {
 
     __device__ static void compute(const Frag &f, const QOp &q, int t0, int, int grp, int tok_end,
                                    int limit, bool full, float scale_log2, float &m_run, float &l_run,
-                                   f32x4 *o) {
+                                   f32x4 *o, const lds_char * = nullptr, int = -1) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NS / 4; ++c) {
@@ -943,7 +966,33 @@ __device__ __forceinline__ void stage_rows(const lds_char *dst, const int32_t *r
 // The record and the pools come as separate leading arguments as well: those arrive in
 // SGPRs with the dispatch (kernel-argument preloading), so the record's loads go out at
 // once, beside the loads of the other arguments instead of after them.
-template <class T, int DT, int D, int NW, bool EARLY, bool WR>
+// The new K/V rows of a decode segment (fused append) into a per-wave LDS slot: K at
+// [0, 2D), V at [256, 256 + 2D) (4 bytes per lane, the row repeated where 2D < 256).
+template <int D>
+__device__ __forceinline__ void stage_new_rows(const lds_char *slot, const AttnArgs &a, const Seg &w,
+                                               int hkv, int lane) {
+    constexpr int kRowB = 2 * D;
+    const int64_t off = ((int64_t)w.q_start * hkv + w.kv_head) * kRowB;
+    const uint32_t lo = 4u * (uint32_t)(lane % (kRowB / 4));
+    dma_b32((const char *)a.k_new + off, lo, slot);
+    dma_b32((const char *)a.v_new + off, lo, slot + 256);
+}
+// ... and from there to the new token's pool slot, by the workgroup that runs the block's
+// last piece (the one whose tiles include the new token)
+template <int D>
+__device__ __forceinline__ void write_new_rows(const lds_char *slot, const AttnArgs &a, const Seg &w,
+                                               int hkv, int lane) {
+    constexpr int kRowB = 2 * D;
+    if (lane < kRowB / 16) {
+        const int64_t off = ((int64_t)a.append_rows[w.q_start] * hkv + w.kv_head) * kRowB + 16 * lane;
+        const u32x4 kv = *(const __attribute__((address_space(3))) u32x4 *)(slot + 16 * lane);
+        const u32x4 vv = *(const __attribute__((address_space(3))) u32x4 *)(slot + 256 + 16 * lane);
+        *reinterpret_cast<u32x4 *>((char *)a.k + off) = kv;
+        *reinterpret_cast<u32x4 *>((char *)a.v + off) = vv;
+    }
+}
+
+template <class T, int DT, int D, int NW, bool EARLY, bool WR, bool FUSE>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, const void *k_pool,
                                                       const void *v_pool, int hkv, const AttnArgs a) {
     static_assert(NW == 4 && NW <= kMaxWaves, "four waves per workgroup");
@@ -960,7 +1009,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     // a ring of four segment headers and two 64-step windows of pool rows.
     constexpr int kRingB = T::template ring_bytes<PF>();
     constexpr int kQB = T::kQBytes;
-    constexpr int kWaveB = kRingB + kQB + 4 * kHdrSlot + 2 * 256;
+    static_assert(!FUSE || DT != FL_F32, "the fused append runs with 16-bit types");
+    constexpr int kNewB = FUSE ? 2 * 512 : 0;  // two slots of new K and V rows
+    constexpr int kWaveB = kRingB + kQB + 4 * kHdrSlot + 2 * 256 + kNewB;
     __shared__ Smem<D> sm;
     __shared__ __attribute__((aligned(16))) char wave_lds[NW * kWaveB];
 
@@ -996,6 +1047,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     const lds_char *hdr_b = q_b + kQB;
     const lds_char *rows_b = hdr_b + 4 * kHdrSlot;
     auto hdr_slot = [&](int seg) { return hdr_b + kHdrSlot * ((seg - seg_b) & 3); };
+    const lds_char *new_b = rows_b + 2 * 256;
+    auto new_slot = [&](int seg) { return new_b + 512 * ((seg - seg_b) & 1); };
 
     // Q, the next two headers and the first row windows go out ahead of the ring, or just
     // behind its first tile (whose addresses need the least arithmetic); the first
@@ -1005,6 +1058,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     constexpr int kAhead = T::kTileFirst ? 1 : 0;  // ring slots issued before Q
     static_for<0, kAhead>([&](auto si) { T::ring_issue(ring, si, k_pool, v_pool, row_first[si]); });
     T::template q_stage<WR>(q_b, a, cs, lane);
+    if constexpr (FUSE) stage_new_rows<D>(new_slot(seg_b), a, cs, hkv, lane);
     stage_header(hdr_slot(seg_b + 1), a.segs, min(seg_b + 1, seg_e - 1), lane);
     stage_header(hdr_slot(seg_b + 2), a.segs, min(seg_b + 2, seg_e - 1), lane);
     stage_rows(rows_b, rows, 0, nsteps, lane);
@@ -1015,6 +1069,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     auto kv_half = [&](const RowInfo &x) { return WR ? x.qh / a.real_group : -1; };
     RowInfo ri = row_info(cs, a, col);
     typename T::QOp qc = T::q_fetch(q_b, ri, col, grp, kv_half(ri));
+    // the piece that holds the block's newest key writes the new rows to the pools
+    if constexpr (FUSE)
+        if (wv == 0 && cs.tok_end == cs.kv_len) write_new_rows<D>(new_slot(seg_b), a, cs, hkv, lane);
     int ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
     int full_end = seg_full_end(cs, a);
 
@@ -1042,6 +1099,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
             seg_end = k + 1 < seg_e ? lds_int(hdr_slot(k + 1) + 4 * FL_WI_POS_BEGIN) : nsteps;
             ri = row_info(cs, a, col);
             qc = T::q_fetch(q_b, ri, col, grp, kv_half(ri));
+            if constexpr (FUSE)
+                if (wv == 0 && cs.tok_end == cs.kv_len) write_new_rows<D>(new_slot(k), a, cs, hkv, lane);
             ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
             full_end = seg_full_end(cs, a);
             wait_lds();  // the slot of header k - 2 is free
@@ -1053,6 +1112,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
             const Seg ns = seg_fields_lds(hdr_slot(k + 1));
             wait_lds();  // this wave's reads of the Q rows are done
             T::template q_stage<WR>(q_b, a, ns, lane);
+            if constexpr (FUSE) stage_new_rows<D>(new_slot(k + 1), a, ns, hkv, lane);
         }
         int nrow[PF];  // pool rows of this group's refills
         if constexpr (kRefill) {
@@ -1085,8 +1145,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
             if constexpr (kEarly) refill();
             if (j < ntile) {
                 const int t0 = cs.tok_begin + j * kTileTokens;
+                // fused append: the newest key (kv_len - 1) comes from the staged new rows
+                const int kt = FUSE && cs.kv_len - 1 - t0 < kTileTokens ? cs.kv_len - 1 - t0 : -1;
                 T::compute(T::ring_frag(ring, s), qc, t0, col, grp, cs.tok_end, ri.limit,
-                           t0 + kTileTokens <= full_end, a.scale_log2, m_run, l_run, o);
+                           t0 + kTileTokens <= full_end, a.scale_log2, m_run, l_run, o,
+                           new_slot(k), kt);
             }
             if constexpr (!kEarly) refill();
             __builtin_amdgcn_sched_barrier(0);
@@ -1158,12 +1221,21 @@ struct TileFor<FL_F32, D> {
     using type = F32Tile<D>;
 };
 
-template <int DT, int D, int NW, bool EARLY, bool WR = false>
+template <int DT, int D, int NW, bool EARLY, bool WR = false, bool FUSE = false>
 hipError_t launch_t(int n, const AttnArgs &a, hipStream_t s) {  // n: workgroups
     using T = typename TileFor<DT, D>::type;
-    hipLaunchKernelGGL((attn_kernel<T, DT, D, NW, EARLY, WR>), dim3(n), dim3(NW * 64), 0, s, a.wg_rec,
+    hipLaunchKernelGGL((attn_kernel<T, DT, D, NW, EARLY, WR, FUSE>), dim3(n), dim3(NW * 64), 0, s, a.wg_rec,
                        a.k, a.v, a.num_kv_heads, a);
     return hipGetLastError();
+}
+
+// Fused append: decode-only plans (one workgroup per compute unit, early refill), 16-bit.
+template <int DT>
+hipError_t launch_fused(int head_dim, bool whole_rows, int n, const AttnArgs &a, hipStream_t s) {
+    if (whole_rows) return head_dim == 128 ? launch_t<DT, 128, 4, true, true, true>(n, a, s) : hipErrorInvalidValue;
+    if (head_dim == 64) return launch_t<DT, 64, 4, true, false, true>(n, a, s);
+    if (head_dim == 128) return launch_t<DT, 128, 4, true, false, true>(n, a, s);
+    return hipErrorInvalidValue;
 }
 
 // One instantiation where the refill point cannot vary: always early at head_dim 128,
@@ -1178,9 +1250,15 @@ hipError_t launch_w(int waves, bool early, int n, const AttnArgs &a, hipStream_t
 
 }  // namespace
 
-int launch_attention(int dtype, int head_dim, int waves, bool early, bool whole_rows, int n,
-                     const AttnArgs &a, void *stream) {
+int launch_attention(int dtype, int head_dim, int waves, bool early, bool whole_rows, bool fuse_append,
+                     int n, const AttnArgs &a, void *stream) {
     hipStream_t s = (hipStream_t)stream;
+    if (fuse_append) {
+        if (waves != 4) return (int)hipErrorInvalidValue;
+        if (dtype == FL_BF16) return (int)launch_fused<FL_BF16>(head_dim, whole_rows, n, a, s);
+        if (dtype == FL_F16) return (int)launch_fused<FL_F16>(head_dim, whole_rows, n, a, s);
+        return (int)hipErrorInvalidValue;
+    }
     if (whole_rows) {  // two kv heads of 64 as one row of 128 (refilled early, as at 128)
         if (waves != 4 || head_dim != 128) return (int)hipErrorInvalidValue;
         if (dtype == FL_BF16) return (int)launch_t<FL_BF16, 128, 4, true, true>(n, a, s);

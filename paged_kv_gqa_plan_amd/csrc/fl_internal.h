@@ -130,6 +130,7 @@ struct Plan {
     int32_t num_merges = 0;
     bool whole_rows = false;        // blocks hold every query head of a request and read whole
                                     // token rows (one virtual kv head of Hkv * D values)
+    bool decode_only = false;       // every request has at most one query row
     int32_t max_splits = 0;
     int64_t part_rows = 0;
     std::vector<int32_t> append_rows;  // per query row: token row page * P + slot of the
@@ -168,14 +169,21 @@ struct AttnArgs {
     float scale_log2;          // sm_scale * log2(e)
     int32_t real_group;        // whole-row blocks: query heads per real kv head (the kv head
                                // of block row h is h / real_group); otherwise unused
+    // fused KV append (decode-only steps): the step's new K/V rows [rows, Hkv, D], and per
+    // query row the token row (page * P + slot) they go to; NULL when not fused
+    const void *k_new;
+    const void *v_new;
+    const int32_t *append_rows;
 };
 
 // Return hipSuccess or the launch error (as int to keep HIP headers out of this file).
 // early_refill: refill a K/V slot as soon as its tile is in registers (memory-bound steps)
 // rather than after the tile's arithmetic (steps bound by the arithmetic).
 // whole_rows: head_dim is the virtual row width Hkv * D (128) of whole-row blocks.
+// fuse_append: the launch also appends the new K/V rows (a.k_new, a.v_new; decode-only
+// plans, 16-bit types): it writes them to the pools and uses them for the newest key.
 int launch_attention(int dtype, int head_dim, int waves, bool early_refill, bool whole_rows,
-                     int num_groups, const AttnArgs &a, void *stream);
+                     bool fuse_append, int num_groups, const AttnArgs &a, void *stream);
 
 // KV append: copy row r of k_new / v_new (row_bytes each, a multiple of 16) to token row
 // dst_rows[r] of k_pool / v_pool (kv_append.hip).

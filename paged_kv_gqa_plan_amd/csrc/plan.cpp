@@ -178,6 +178,7 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         decode_only = ql <= 1;
         decode_rows += ql;
     }
+    out.decode_only = decode_only;
     out.whole_rows = lim.whole_rows_ok && decode_only &&
                      (lim.whole_rows_always || decode_rows >= lim.num_cus);
     const int32_t Hkv = out.whole_rows ? 1 : Hkv_real;

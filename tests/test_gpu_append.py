@@ -172,3 +172,134 @@ def test_append_errors_and_empty_plan():
     h.append(kn, vn, k, v)
     torch.cuda.synchronize()
     assert np.array_equal(_bytes(to_host_bits(k, b.dtype)), _bytes(before))
+
+
+# ---- append + attention in one call ----------------------------------------------------------
+def _run_append_check(b, what, num_splits=0, **cfg_kw):
+    """fl_paged_attn_run_append on the before-pools must give the oracle's attention over the
+    full history and leave the oracle's appended pools."""
+    import torch
+    announce(f"run_append {what}: dtype={b.dtype} B={b.batch_size} rows={b.rows} "
+             f"D={b.head_dim} P={b.page_size} splits={num_splits} {cfg_kw}")
+    st = W.append_step(b)
+    ref_out, ref_lse = oracle.attention(b)
+    ref_k, ref_v = oracle.kv_append(b, st.k_new, st.v_new, st.k_before, st.v_before)
+    h = fl.PagedAttention(config_for(b, **cfg_kw), device=0)
+    h.plan(b.qo_indptr, b.kv_indptr, b.kv_indices, b.last_page_len, b.num_pages,
+           causal=b.causal, sm_scale=b.sm_scale, num_splits=num_splits)
+    k, v = to_device(st.k_before, b.dtype), to_device(st.v_before, b.dtype)
+    kn, vn = to_device(st.k_new, b.dtype), to_device(st.v_new, b.dtype)
+    q = to_device(b.q, b.dtype)
+    out = torch.full(q.shape, float("nan"), dtype=torch_dtype(b.dtype), device="cuda:0")
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device="cuda:0")
+    h.run_append(q, kn, vn, k, v, out, lse)
+    torch.cuda.synchronize()
+    compare(b, out, lse, ref_out, ref_lse, what)
+    assert np.array_equal(_bytes(to_host_bits(k, b.dtype)), _bytes(ref_k)), f"{what}: K pool"
+    assert np.array_equal(_bytes(to_host_bits(v, b.dtype)), _bytes(ref_v)), f"{what}: V pool"
+    return h
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "saturated_decode", "mixed_length_decode",
+                                  "long_context_skew"])
+def test_run_append_decode_workloads(name):
+    _run_append_check(W.WORKLOADS[name](keep_dense=True), name)
+
+
+@pytest.mark.parametrize("whole_rows", [1, -1])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_run_append_modes_and_pieces(whole_rows, splits, dtype):
+    b = W.make_batch([1, 15, 16, 17, 300, 1000, 257], num_qo_heads=14, num_kv_heads=2, head_dim=64,
+                     page_size=16, dtype=dtype, seed=91, num_pages=120, keep_dense=True)
+    _run_append_check(b, f"modes wr{whole_rows} s{splits} {dtype}", num_splits=splits,
+                      whole_rows=whole_rows)
+
+
+@pytest.mark.parametrize("case", ["ragged", "f32", "d128-p256"])
+def test_run_append_other_plans(case):
+    kw = dict(num_qo_heads=14, num_kv_heads=2, head_dim=64, page_size=16, dtype="bf16")
+    kv, qo = [80, 17, 300, 33], None
+    if case == "ragged":      # a prefill chunk: append first, then attend (two launches)
+        qo = [37, 1, 1, 5]
+    elif case == "f32":
+        kw["dtype"] = "f32"
+    else:                     # fused at head_dim 128, 256-slot pages
+        kw.update(num_qo_heads=12, head_dim=128, page_size=256, dtype="f16")
+        kv = [1, 256, 257, 700]
+    b = W.make_batch(kv, qo, seed=92, num_pages=40, keep_dense=True, **kw)
+    _run_append_check(b, f"run_append {case}")
+
+
+@pytest.mark.parametrize("whole_rows", [1, -1])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_run_append_needle_in_the_new_token_bit_exact(whole_rows, dtype):
+    """The new token's K is a needle (its score beats every other key by > 100 in log2
+    units), so each head's output is exactly the new token's V row: checks that the
+    fused kernel takes both K and V of the newest key from the new rows, at every position
+    in its tile (first slot of a page, last slot, middle)."""
+    import torch
+    kv = [1, 16, 17, 31, 300, 1000, 513]
+    b = W.make_batch(kv, num_qo_heads=14, num_kv_heads=2, head_dim=64, page_size=16, dtype=dtype,
+                     seed=93, num_pages=140, keep_dense=True)
+    st = W.append_step(b)
+    zero = W.to_storage(np.zeros(1, np.float32), dtype)[0]
+    big = W.to_storage(np.array([256.0], np.float32), dtype)[0]
+    for r in range(len(kv)):            # history keys 0, new key a needle on dim 0
+        pages = b.kv_indices[b.kv_indptr[r]:b.kv_indptr[r + 1]]
+        for t in range(kv[r] - 1):
+            st.k_before[pages[t // 16], t % 16] = zero
+    st.k_new[:] = zero
+    st.k_new[:, :, 0] = big
+    b.q[:] = zero
+    b.q[:, :, 0] = W.to_storage(np.array([32.0], np.float32), dtype)[0]
+    announce(f"run_append needle {dtype} whole_rows={whole_rows}")
+    h = fl.PagedAttention(config_for(b, whole_rows=whole_rows), device=0)
+    h.plan(b.qo_indptr, b.kv_indptr, b.kv_indices, b.last_page_len, b.num_pages)
+    k, v = to_device(st.k_before, dtype), to_device(st.v_before, dtype)
+    kn, vn = to_device(st.k_new, dtype), to_device(st.v_new, dtype)
+    q = to_device(b.q, dtype)
+    out = torch.full(q.shape, float("nan"), dtype=torch_dtype(dtype), device="cuda:0")
+    h.run_append(q, kn, vn, k, v, out)
+    torch.cuda.synchronize()
+    got = to_host_bits(out, dtype)
+    for r in range(len(kv)):
+        for hq in range(14):
+            assert np.array_equal(np.ascontiguousarray(got[r, hq]).view(np.uint8),
+                                  np.ascontiguousarray(st.v_new[r, hq // 7]).view(np.uint8)), (r, hq)
+
+
+def test_run_append_graph_replay_across_replans():
+    import torch
+    b1 = W.make_batch([40, 300, 17, 1, 64], num_qo_heads=14, num_kv_heads=2, head_dim=64,
+                      page_size=16, dtype="bf16", seed=94, num_pages=64, keep_dense=True)
+    b2 = W.relabel_pages(b1, W.rng_for(95, 0, 0).permutation(b1.num_pages))
+    sts = [W.append_step(b1), W.append_step(b2)]
+    announce("run_append graph replay across re-plans")
+    h = fl.PagedAttention(config_for(b1), device=0)
+    h.plan(b1.qo_indptr, b1.kv_indptr, b1.kv_indices, b1.last_page_len, b1.num_pages)
+    k, v = to_device(sts[0].k_before, "bf16"), to_device(sts[0].v_before, "bf16")
+    kn, vn = to_device(sts[0].k_new, "bf16"), to_device(sts[0].v_new, "bf16")
+    q = to_device(b1.q, "bf16")
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda:0")
+    h.run_append(q, kn, vn, k, v, out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h.run_append(q, kn, vn, k, v, out)
+    ref = oracle.attention(b1)
+    for rep in range(4):
+        bb, st = (b2, sts[1]) if rep % 2 else (b1, sts[0])
+        h.plan(bb.qo_indptr, bb.kv_indptr, bb.kv_indices, bb.last_page_len, bb.num_pages)
+        k.copy_(to_device(st.k_before, "bf16"))
+        v.copy_(to_device(st.v_before, "bf16"))
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        ref_k, ref_v = oracle.kv_append(bb, st.k_new, st.v_new, st.k_before, st.v_before)
+        assert np.array_equal(_bytes(to_host_bits(k, "bf16")), _bytes(ref_k)), f"replay {rep}"
+        assert np.array_equal(_bytes(to_host_bits(v, "bf16")), _bytes(ref_v)), f"replay {rep}"
+        compare(bb, out, None, ref[0], None, f"replay {rep}")
+        x = torch.randn(1 << 20, device="cuda:0")
+        float(x.sum())
+        torch.cuda.synchronize()
