@@ -879,7 +879,9 @@ __device__ __forceinline__ void merge_pieces(const Seg &w, const AttnArgs &a, in
 
 // Fold of one segment across the waves (all waves call it at the same step), then the
 // output rows: final rows for a whole row block, device-scope fp32 partial rows for a piece.
-template <class T, int DT, int D, int NW, bool WR>
+// LAST: the workgroup's final fold: no segment follows, so the LDS slots need no release
+// (the merge phase has a barrier of its own before it reads the pending pieces' fields).
+template <class T, int DT, int D, int NW, bool WR, bool LAST = false>
 __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, const Seg &cs, int k,
                                              float &m_run, float &l_run, f32x4 *o, int &npend,
                                              int wave, int col, int grp) {
@@ -946,11 +948,13 @@ __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, con
         }
         ++npend;
     }
-    __syncthreads();  // the LDS slots are free again
-    m_run = kNegInf;
-    l_run = 0.f;
+    if constexpr (!LAST) {
+        __syncthreads();  // the LDS slots are free again
+        m_run = kNegInf;
+        l_run = 0.f;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NJ; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 }
 
 // Pool rows of 64 steps of this wave (win .. win+63; past the end: the last step's row)
@@ -977,14 +981,16 @@ __device__ __forceinline__ void stage_new_rows(const lds_char *slot, const AttnA
     dma_b32((const char *)a.k_new + off, lo, slot);
     dma_b32((const char *)a.v_new + off, lo, slot + 256);
 }
-// ... and from there to the new token's pool slot, by the workgroup that runs the block's
-// last piece (the one whose tiles include the new token)
+// ... and from there to the new token's pool slot (token row app_row of the pools), by the
+// workgroup that runs the block's last piece (the one whose tiles include the new token).
+// The token row is loaded when the segment starts and the rows are written when it ends, so
+// the load's latency never sits in front of the loop.
 template <int D>
 __device__ __forceinline__ void write_new_rows(const lds_char *slot, const AttnArgs &a, const Seg &w,
-                                               int hkv, int lane) {
+                                               int app_row, int hkv, int lane) {
     constexpr int kRowB = 2 * D;
     if (lane < kRowB / 16) {
-        const int64_t off = ((int64_t)a.append_rows[w.q_start] * hkv + w.kv_head) * kRowB + 16 * lane;
+        const int64_t off = ((int64_t)app_row * hkv + w.kv_head) * kRowB + 16 * lane;
         const u32x4 kv = *(const __attribute__((address_space(3))) u32x4 *)(slot + 16 * lane);
         const u32x4 vv = *(const __attribute__((address_space(3))) u32x4 *)(slot + 256 + 16 * lane);
         *reinterpret_cast<u32x4 *>((char *)a.k + off) = kv;
@@ -1069,9 +1075,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     auto kv_half = [&](const RowInfo &x) { return WR ? x.qh / a.real_group : -1; };
     RowInfo ri = row_info(cs, a, col);
     typename T::QOp qc = T::q_fetch(q_b, ri, col, grp, kv_half(ri));
-    // the piece that holds the block's newest key writes the new rows to the pools
-    if constexpr (FUSE)
-        if (wv == 0 && cs.tok_end == cs.kv_len) write_new_rows<D>(new_slot(seg_b), a, cs, hkv, lane);
+    // the piece that holds the block's newest key writes the new rows to the pools (at its end)
+    auto new_token_row = [&](const Seg &w) {
+        return FUSE && wv == 0 && w.tok_end == w.kv_len ? a.append_rows[w.q_start] : -1;
+    };
+    int app_row = new_token_row(cs);
     int ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
     int full_end = seg_full_end(cs, a);
 
@@ -1093,14 +1101,15 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
         constexpr bool kRefill = decltype(refill)::value;
         wait_vm<PF * kLoads>();
         if (p0 == seg_end) {  // the same step in every wave: segment k is done
+            if constexpr (FUSE)
+                if (app_row >= 0) write_new_rows<D>(new_slot(k), a, cs, app_row, hkv, lane);
             fold_segment<T, DT, D, NW, WR>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);
             ++k;
             cs = seg_fields_lds(hdr_slot(k));
             seg_end = k + 1 < seg_e ? lds_int(hdr_slot(k + 1) + 4 * FL_WI_POS_BEGIN) : nsteps;
             ri = row_info(cs, a, col);
             qc = T::q_fetch(q_b, ri, col, grp, kv_half(ri));
-            if constexpr (FUSE)
-                if (wv == 0 && cs.tok_end == cs.kv_len) write_new_rows<D>(new_slot(k), a, cs, hkv, lane);
+            app_row = new_token_row(cs);
             ntile = (cs.tok_end - cs.tok_begin + kTileTokens - 1) / kTileTokens;
             full_end = seg_full_end(cs, a);
             wait_lds();  // the slot of header k - 2 is free
@@ -1158,7 +1167,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     int p0 = 0;
     for (; p0 + PF < nsteps; p0 += PF) group(p0, std::true_type{});
     group(p0, std::false_type{});
-    fold_segment<T, DT, D, NW, WR>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);
+    if constexpr (FUSE)
+        if (app_row >= 0) write_new_rows<D>(new_slot(k), a, cs, app_row, hkv, lane);
+    fold_segment<T, DT, D, NW, WR, true>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);
 
     // ---- merge tickets of the partial pieces (at most the first and the last) -----------
     // The partial rows went out as device-scope stores; each wave waits for their
