@@ -69,7 +69,9 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // lane l and of lane l^16 (or l^32) in some order, so max and + of the pair are the same in
 // both lanes of it (bit-identical: both operations are commutative).
 // max of two values that are never NaN (scores are finite or -inf): one instruction, with
-// none of the quieting that fmaxf adds for operands of unknown origin
+// none of the quieting that fmaxf adds for operands of unknown origin. Only for operands
+// produced by ordinary VALU instructions: the compiler does not count inline asm among the
+// readers of an MFMA result that must wait for it.
 __device__ __forceinline__ float max_nonan(float a, float b) {
     float r;
     asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
@@ -280,41 +282,52 @@ constexpr float kSlack = 8.f;
 
 // full: every key of the tile is below tok_end and visible to every real row of the block
 // (rows past the block's end see garbage-free zeros and are never stored), so no mask.
+// The max is taken on the raw scores and scaled once (scale_log2 > 0 and rounding is
+// monotonic, so it equals the max of the scaled scores). The rescale factor is computed
+// only in the rare tiles where some row's running max moves (a wave-uniform branch).
+// FMA: p = exp2(fma(s, scale, -m)) in one rounding (16-bit outputs, where the last bit of
+// p vanishes in the output's rounding); otherwise exp2(s * scale - m), which is exactly 1
+// for the key that sets the max (fp32 outputs keep single-key results exact).
+template <bool FMA>
 __device__ __forceinline__ void softmax_tile(const f32x4 &s, int t0, int grp, int tok_end,
                                              int limit, bool full, float scale_log2, float &m_run,
                                              float &l_run, float p[4], float &alpha,
                                              bool &rescaled) {
-    float sv[4];
-    float mt = kNegInf;
-    if (full) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sv[e] = s[e] * scale_log2;
-            mt = fmaxf(mt, sv[e]);
-        }
-    } else {
+    f32x4 x = s;  // masked in place on tiles that need it
+    if (!full) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = t0 + 4 * grp + e;
-            const bool ok = (t < tok_end) && (t <= limit);
-            sv[e] = ok ? s[e] * scale_log2 : kNegInf;
-            mt = fmaxf(mt, sv[e]);
+            x[e] = (t < tok_end) && (t <= limit) ? x[e] : kNegInf;
         }
     }
-    mt = max_xor32(max_xor16(mt));
+    // fmaxf, not the inline-asm max: x may be the MFMA accumulator itself, and the compiler
+    // inserts the wait states an MFMA result needs before a VALU read only for instructions
+    // it can see (an asm max read stale accumulator values).
+    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mt = max_xor32(max_xor16(mt)) * scale_log2;
+    alpha = 1.f;
     const bool move = mt > m_run + kSlack;  // false while both are -inf
-    const float m_new = move ? mt : m_run;
     rescaled = __builtin_amdgcn_ballot_w64(move) != 0;
-    alpha = move ? fast_exp2(m_run - m_new) : 1.f;
-    const float base = (m_new == kNegInf) ? 0.f : m_new;
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        p[e] = fast_exp2(sv[e] - base);
-        ps += p[e];
+    if (rescaled) {
+        const float m_new = move ? mt : m_run;
+        alpha = move ? fast_exp2(m_run - m_new) : 1.f;  // 0 while m_run is -inf
+        l_run *= alpha;
+        m_run = m_new;
     }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
+    // a full tile makes every row's running max finite
+    const float base = (full || m_run != kNegInf) ? m_run : 0.f;
+    if constexpr (FMA) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(x[e], scale_log2, -base));
+    } else {
+        // two roundings, kept apart (no contraction into an FMA): the key that sets the max
+        // then gets exactly exp2(0) = 1
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(x[e] * scale_log2 - base);
+    }
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
 }
 
 // Query row of column `col` in the block, and the last key it may see (-1: padding column).
@@ -543,7 +556,7 @@ struct HalfTile {
         for (int c = 0; c < NC; ++c) s = H::mma_k32(kk[c], q.q[c], s);
         float p[4], alpha;
         bool rescaled;
-        softmax_tile(s, t0, grp, tok_end, limit, full, scale_log2, m_run, l_run, p, alpha, rescaled);
+        softmax_tile<true>(s, t0, grp, tok_end, limit, full, scale_log2, m_run, l_run, p, alpha, rescaled);
         if (rescaled) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) o[j] = o[j] * alpha;
@@ -683,7 +696,7 @@ struct F32Tile {
         }
         float p[4], alpha;
         bool rescaled;
-        softmax_tile(s, t0, grp, tok_end, limit, full, scale_log2, m_run, l_run, p, alpha, rescaled);
+        softmax_tile<false>(s, t0, grp, tok_end, limit, full, scale_log2, m_run, l_run, p, alpha, rescaled);
         if (rescaled) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) o[j] = o[j] * alpha;
