@@ -336,3 +336,53 @@ def test_run_errors():
     with pytest.raises(fl.FlError) as e:
         fl.fl_paged_attn_run(h.handle, 0, x.data_ptr(), x.data_ptr(), x.data_ptr())
     assert e.value.status == fl.FL_ERR_INVALID_ARG
+
+
+def test_pool_beyond_4_gib():
+    """One layer's pools of 40960 pages of 128 KB (5.4 GB each, fp16, d 128, page size 256):
+    the requests' pages sit past byte offset 2^32, so every address must be formed in 64
+    bits (attention, append and poisoning). Only the used pages are filled."""
+    import torch
+    P, Hkv, D, Hq, N = 256, 2, 128, 12, 40960
+    kv = [300, 1000, 5000, 257]
+    small = W.make_batch(kv, num_qo_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P,
+                         dtype="f16", seed=97, num_pages=sum(-(-k // P) for k in kv), keep_dense=True)
+    # move the used pages to the far end of a large pool (ids N - n .. N - 1, shuffled)
+    n_used = small.num_pages
+    perm = (N - n_used) + W.rng_for(97, 0, 7).permutation(n_used)
+    indices = perm[small.kv_indices].astype(np.int32)
+    announce(f"pool beyond 4 GiB: {N} pages x {P * Hkv * D * 2} B, pages {indices.min()}..{indices.max()}")
+    k = torch.full((N, P, Hkv, D), float("nan"), dtype=torch.float16, device="cuda:0")
+    v = torch.full((N, P, Hkv, D), float("nan"), dtype=torch.float16, device="cuda:0")
+    idx = torch.from_numpy(perm.astype(np.int64)).to("cuda:0")
+    k.index_copy_(0, idx, torch.from_numpy(small.k_pool).to("cuda:0"))
+    v.index_copy_(0, idx, torch.from_numpy(small.v_pool).to("cuda:0"))
+    assert int(indices.max()) * P * Hkv * D * 2 > (1 << 32)
+    # the oracle on the small pool with the original page ids: the same logical batch
+    ref_out, ref_lse = oracle.attention(small)
+    big = W.Batch(**{**small.__dict__, "kv_indices": indices, "num_pages": N})
+    h = fl.PagedAttention(fl.make_config(Hq, Hkv, D, P, "f16", 8, 8, 64), device=0)
+    h.plan(big.qo_indptr, big.kv_indptr, big.kv_indices, big.last_page_len, N)
+    q = torch.from_numpy(small.q).to("cuda:0")
+    out = torch.full(q.shape, float("nan"), dtype=torch.float16, device="cuda:0")
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device="cuda:0")
+    h.run(q, k, v, out, lse)
+    torch.cuda.synchronize()
+    compare(small, out, lse, ref_out, ref_lse, "pool beyond 4 GiB")
+    # append: the step's new rows written past 4 GiB, byte for byte
+    st = W.append_step(small)
+    k.index_copy_(0, idx, torch.from_numpy(st.k_before).to("cuda:0"))
+    v.index_copy_(0, idx, torch.from_numpy(st.v_before).to("cuda:0"))
+    kn = torch.from_numpy(st.k_new).to("cuda:0")
+    vn = torch.from_numpy(st.v_new).to("cuda:0")
+    h.append(kn, vn, k, v)
+    torch.cuda.synchronize()
+    got_k = k.index_select(0, idx).cpu().numpy()
+    assert np.array_equal(got_k.view(np.uint16), small.k_pool.view(np.uint16))
+    # poison the big pages of small pages 0..2: exactly those become NaN, in both pools
+    fl.fl_paged_kv_poison("f16", P, Hkv, D, N, perm[:3].astype(np.int32), k.data_ptr(), v.data_ptr())
+    torch.cuda.synchronize()
+    assert torch.isnan(k.index_select(0, idx[:3]).float()).all()
+    assert torch.isnan(v.index_select(0, idx[:3]).float()).all()
+    rest = k.index_select(0, idx[3:]).cpu().numpy()
+    assert np.array_equal(rest.view(np.uint16), small.k_pool[3:].view(np.uint16))
