@@ -288,7 +288,8 @@ constexpr float kSlack = 8.f;
 // FMA: p = exp2(fma(s, scale, -m)) in one rounding (16-bit outputs, where the last bit of
 // p vanishes in the output's rounding); otherwise exp2(s * scale - m), which is exactly 1
 // for the key that sets the max (fp32 outputs keep single-key results exact).
-template <bool FMA>
+// SUM: add the tile's p to l_run here (else the caller sums them itself).
+template <bool FMA, bool SUM = true>
 __device__ __forceinline__ void softmax_tile(const f32x4 &s, int t0, int grp, int tok_end,
                                              int limit, bool full, float scale_log2, float &m_run,
                                              float &l_run, float p[4], float &alpha,
@@ -327,7 +328,7 @@ __device__ __forceinline__ void softmax_tile(const f32x4 &s, int t0, int grp, in
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] = fast_exp2(x[e] * scale_log2 - base);
     }
-    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    if constexpr (SUM) l_run += (p[0] + p[1]) + (p[2] + p[3]);
 }
 
 // Query row of column `col` in the block, and the last key it may see (-1: padding column).
@@ -385,6 +386,11 @@ struct HalfTile {
     using H = Half<DT>;
     static constexpr int NC = D / 32;
     static constexpr int NJ = D / 16;
+    // accumulator blocks: the output's NJ, then one more whose every element holds the row's
+    // running sum of p (the PV contraction against a block of ones: the sum costs two MFMAs
+    // instead of a VALU add per score, and needs no reduction across lanes at the fold)
+    static constexpr int NO = NJ + 1;
+    static constexpr bool kSumInMma = true;
     struct Frag {
         u32x4 k[NC];   // K piece c of this lane's key
         u32x2 vt[NJ];  // V of keys 4grp .. 4grp+3 at this lane's output column of block j
@@ -556,15 +562,19 @@ struct HalfTile {
         for (int c = 0; c < NC; ++c) s = H::mma_k32(kk[c], q.q[c], s);
         float p[4], alpha;
         bool rescaled;
-        softmax_tile<true>(s, t0, grp, tok_end, limit, full, scale_log2, m_run, l_run, p, alpha, rescaled);
+        softmax_tile<true, false>(s, t0, grp, tok_end, limit, full, scale_log2, m_run, l_run, p, alpha,
+                                  rescaled);
         if (rescaled) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) o[j] = o[j] * alpha;
+            for (int j = 0; j < NO; ++j) o[j] = o[j] * alpha;
         }
         // P = P_hi + P_lo, both in the 16-bit type: the pair carries p to ~16 bits more
         // than one rounding would, so the product with the exact 16-bit V loses nothing
         // measurable. Two K=16 instructions contract V^T with P_hi and with P_lo.
-        const uint32_t h01 = H::pack(p[0], p[1]), h23 = H::pack(p[2], p[3]);
+        uint32_t h01 = H::pack(p[0], p[1]), h23 = H::pack(p[2], p[3]);
+        // opaque to the optimiser (no instruction): the lo parts then unpack these packed
+        // values instead of converting every p a second time
+        asm("" : "+v"(h01), "+v"(h23));
         const uint32_t l01 = H::pack(p[0] - H::lo_f(h01), p[1] - H::hi_f(h01));
         const uint32_t l23 = H::pack(p[2] - H::lo_f(h23), p[3] - H::hi_f(h23));
         // keys at or past tok_end may hold anything (NaN included): their V becomes 0
@@ -580,6 +590,9 @@ struct HalfTile {
             o[j] = H::mma_k16(vt[j], u32x2{h01, h23}, o[j]);
             o[j] = H::mma_k16(vt[j], u32x2{l01, l23}, o[j]);
         }
+        constexpr uint32_t kOnes = H::kOne | H::kOne << 16;
+        o[NJ] = H::mma_k16(u32x2{kOnes, kOnes}, u32x2{h01, h23}, o[NJ]);
+        o[NJ] = H::mma_k16(u32x2{kOnes, kOnes}, u32x2{l01, l23}, o[NJ]);
     }
 
     // accumulator element (block j, element e) of lane (col, grp) -> output column d
@@ -605,6 +618,8 @@ template <int D>
 struct F32Tile {
     static constexpr int NS = D / 4;
     static constexpr int NJ = D / 16;
+    static constexpr int NO = NJ;            // accumulator blocks: the output's only
+    static constexpr bool kSumInMma = false;  // row sums kept per lane (l_run)
     struct Frag {
         float4 k[NS / 4];
         float4 v[4][NJ / 4];
@@ -901,7 +916,7 @@ __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, con
     constexpr int NJ = D / 16;
     constexpr int TPR = NW * 64 / kBlockRows;
     constexpr int EPT = D / TPR;
-    l_run = sum_xor32(sum_xor16(l_run));
+    l_run = T::kSumInMma ? o[NJ][0] : sum_xor32(sum_xor16(l_run));
     T::to_smem(o, sm.o[wave][col], grp);
     if (grp == 0) {
         sm.m[wave][col] = m_run;
@@ -966,7 +981,7 @@ __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, con
         m_run = kNegInf;
         l_run = 0.f;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < T::NO; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 }
 
@@ -1097,9 +1112,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     int full_end = seg_full_end(cs, a);
 
     float m_run = kNegInf, l_run = 0.f;
-    f32x4 o[NJ];
+    f32x4 o[T::NO];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < T::NO; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     int npend = 0;  // pieces whose merge ticket is still to be drawn (fields in sm.pend)
 
     // ---- the step stream: PF tiles of K and V in flight per wave -------------------------
