@@ -1235,17 +1235,36 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
             ps.kv_head = lds_int(pd + 4 * PD_KV_HEAD);
             return ps;
         };
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            if (i >= npend || !lds_int((const lds_char *)&sm.last[i])) continue;
+        const bool both = npend == 2 && lds_int((const lds_char *)&sm.last[0]) &&
+                          lds_int((const lds_char *)&sm.last[1]);
+        if (both) {
+            // both pieces merge here: each half of the workgroup (two waves) takes one, so
+            // the two merges' loads are in flight together instead of one after the other
+            constexpr int kHalf = NW * 64 / 2;
+            const int i = threadIdx.x / kHalf;
+            const int u = threadIdx.x % kHalf;
             const Seg ps = pend_seg(i);
             if (ps.num_rows > kBlockRows / 2) {
-                const int r = threadIdx.x / TPR;
-                if (r < ps.num_rows) merge_pieces<DT, D, TPR, 8, WR>(ps, a, r, threadIdx.x % TPR);
-            } else {  // up to 8 rows: twice the threads per row, up to 16 pieces per batch
-                constexpr int TPR2 = 2 * TPR;
-                const int r2 = threadIdx.x / TPR2;
-                if (r2 < ps.num_rows) merge_pieces<DT, D, TPR2, 16, WR>(ps, a, r2, threadIdx.x % TPR2);
+                constexpr int TPRH = TPR / 2;
+                const int r = u / TPRH;
+                if (r < ps.num_rows) merge_pieces<DT, D, TPRH, 4, WR>(ps, a, r, u % TPRH);
+            } else {
+                const int r = u / TPR;
+                if (r < ps.num_rows) merge_pieces<DT, D, TPR, 8, WR>(ps, a, r, u % TPR);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if (i >= npend || !lds_int((const lds_char *)&sm.last[i])) continue;
+                const Seg ps = pend_seg(i);
+                if (ps.num_rows > kBlockRows / 2) {
+                    const int r = threadIdx.x / TPR;
+                    if (r < ps.num_rows) merge_pieces<DT, D, TPR, 8, WR>(ps, a, r, threadIdx.x % TPR);
+                } else {  // up to 8 rows: twice the threads per row, up to 16 pieces per batch
+                    constexpr int TPR2 = 2 * TPR;
+                    const int r2 = threadIdx.x / TPR2;
+                    if (r2 < ps.num_rows) merge_pieces<DT, D, TPR2, 16, WR>(ps, a, r2, threadIdx.x % TPR2);
+                }
             }
         }
     }
