@@ -802,7 +802,7 @@ enum { PD_MERGE, PD_NUM_SPLITS, PD_NUM_ROWS, PD_PART_ROW, PD_SPLIT, PD_ROW_BEGIN
        PD_KV_HEAD, PD_INTS };
 template <int D>
 struct Smem {
-    float o[4][kBlockRows][D + 4];
+    alignas(16) float o[4][kBlockRows][D + 4];  // rows of 16-byte multiples
     float m[4][kBlockRows];
     float l[4][kBlockRows];
     int pend[2][PD_INTS];
@@ -894,7 +894,7 @@ __device__ __forceinline__ void merge_pieces(const Seg &w, const AttnArgs &a, in
         }
         M = bm;
     }
-    const float inv = 1.f / L;
+    const float inv = __builtin_amdgcn_rcpf(L);  // L >= 1 (the largest piece weighs 1)
 #pragma unroll
     for (int e = 0; e < EPT; ++e) acc[e] *= inv;
     const int f = w.row_begin + r;
@@ -928,25 +928,38 @@ __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, con
     using RS = RowSplit<D, TPR>;
     constexpr int CW = RS::CW;
     if (r < cs.num_rows) {
+        // every LDS read of the row first (one round trip), then the arithmetic
+        static_assert(CW == 4, "the fold reads whole 16-byte chunks");
+        float mv[4], lv[4];
+        f32x4 ov[4][RS::NCH];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            mv[v] = sm.m[v][r];
+            lv[v] = sm.l[v][r];
+#pragma unroll
+            for (int q = 0; q < RS::NCH; ++q) ov[v][q] = *reinterpret_cast<const f32x4 *>(&sm.o[v][r][RS::col(t, q)]);
+        }
         float M = kNegInf;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) M = fmaxf(M, sm.m[v][r]);
+        for (int v = 0; v < 4; ++v) M = fmaxf(M, mv[v]);
         float wt[4];
         float L = 0.f;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            wt[v] = (M == kNegInf) ? 0.f : fast_exp2(sm.m[v][r] - M);
-            L += sm.l[v][r] * wt[v];
+            wt[v] = (M == kNegInf) ? 0.f : fast_exp2(mv[v] - M);
+            L += lv[v] * wt[v];
         }
-        const float inv = L > 0.f ? 1.f / L : 0.f;
+        const float inv = L > 0.f ? __builtin_amdgcn_rcpf(L) : 0.f;  // exact for powers of two
         float res[EPT];
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            float acc = 0.f;
+        for (int q = 0; q < RS::NCH; ++q)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc += sm.o[v][r][RS::col(t, e / CW) + e % CW] * wt[v];
-            res[e] = acc * inv;
-        }
+            for (int c = 0; c < 4; ++c) {
+                float acc = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc += ov[v][q][c] * wt[v];
+                res[q * 4 + c] = acc * inv;
+            }
         const float lse2 = L > 0.f ? M + fast_log2(L) : kNegInf;  // log2 domain
         if (cs.part_row < 0) {
             const int f = cs.row_begin + r;
