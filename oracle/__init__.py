@@ -9,7 +9,9 @@ The arithmetic lives in ``paged_attn_oracle.c`` (plain C, double precision): a g
 each request's pages into dense K/V followed by plain softmax attention, plus an optional
 split-and-merge mode. ``attention(batch)`` returns unrounded fp64 results.
 ``kv_append(...)`` writes a step's new K/V rows into copies of the pools (a byte copy to
-each new token's page slot); ``paged_kv_poison(...)`` fills freed pages with NaN.
+each new token's page slot); ``rope(...)`` rotates head vectors by their positions (the
+rotary embedding of the append fused with RoPE); ``paged_kv_poison(...)`` fills freed pages
+with NaN.
 ``page_pool.PagePoolModel`` is the page allocator's reference bookkeeping.
 """
 from __future__ import annotations
@@ -66,6 +68,9 @@ def load(path: Optional[str] = None):
     lib.oracle_paged_kv_poison.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
                                            ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
                                            ctypes.c_void_p]
+    lib.oracle_rope.restype = ctypes.c_int
+    lib.oracle_rope.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     if path is None or path == _LIB_OVERRIDE:
@@ -154,6 +159,38 @@ def kv_append(batch, k_new, v_new, k_pool=None, v_pool=None, lib=None):
                            batch.head_dim, batch.page_size, k_new, v_new,
                            batch.k_pool if k_pool is None else k_pool,
                            batch.v_pool if v_pool is None else v_pool, lib=lib)
+
+
+def rope(dtype_code: int, x, positions, theta: float, lib=None) -> np.ndarray:
+    """Rotary embedding of ``x`` ``[rows, heads, D]`` (storage values) at per-row
+    ``positions``; float64 result of the same shape."""
+    lib = lib or load()
+    a = np.ascontiguousarray(x)
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    rows, heads, d = a.shape
+    if pos.shape != (rows,):
+        raise OracleError("one position per row")
+    y = np.zeros(a.shape, dtype=np.float64)
+    rc = lib.oracle_rope(int(dtype_code), rows, heads, d, _ptr(a), _ptr(pos), float(theta), _ptr(y))
+    if rc != 0:
+        raise OracleError(f"oracle_rope returned {rc}")
+    return y
+
+
+def append_positions(qo_indptr, kv_indptr, last_page_len, page_size: int) -> np.ndarray:
+    """Position of every query row: row i of a request with qo_len rows and kv_len cached
+    tokens is token kv_len - qo_len + i (the same reading as the append's slots and the
+    bottom-right causal mask)."""
+    kv_indptr = np.asarray(kv_indptr, dtype=np.int64)
+    last = np.asarray(last_page_len, dtype=np.int64)
+    B = kv_indptr.shape[0] - 1
+    qo = np.arange(B + 1) if qo_indptr is None else np.asarray(qo_indptr, dtype=np.int64)
+    kv_len = (np.diff(kv_indptr) - 1) * page_size + last
+    out = np.zeros(int(qo[-1]), dtype=np.int32)
+    for r in range(B):
+        ql = int(qo[r + 1] - qo[r])
+        out[qo[r]:qo[r + 1]] = kv_len[r] - ql + np.arange(ql)
+    return out
 
 
 def paged_kv_poison(dtype_code: int, page_ids, k_pool, v_pool=None, lib=None):

@@ -370,3 +370,45 @@ int oracle_paged_kv_poison(int dtype, int64_t page_elems, const int32_t *page_id
     }
     return ORACLE_OK;
 }
+
+/*
+ * Rotary position embedding (RoPE), for the KV append fused with RoPE.
+ *
+ * The pages name RoPE as one of the layers of the Qwen2.5-style decoder they run (Torchlet
+ * README, the running example; flashlet README, roadmap: a RoPE fusion kernel) without
+ * writing it out. Reading taken, the rotate-half form of that model family: a head vector
+ * x of head_dim D pairs element i with element i + D/2 (i < D/2), and the pair turns by
+ * the angle a_i = pos * f_i with f_i = theta^(-2i/D):
+ *     y[i]       = x[i] cos(a_i) - x[i + D/2] sin(a_i)
+ *     y[i + D/2] = x[i + D/2] cos(a_i) + x[i] sin(a_i)
+ * Precision reading: f_i is rounded to binary32 and a_i is the binary32 product of
+ * (float)pos and f_i, as model code builds its tables; cos, sin and the rotation are in
+ * double. x holds rows x heads x D storage values, positions[r] is row r's position, and
+ * y receives the rotated values in double.
+ * Returns 0, or a negative code for bad arguments (odd head_dim, theta <= 0, ...).
+ */
+int oracle_rope(int dtype, int rows, int heads, int head_dim, const void *x,
+                const int32_t *positions, double theta, double *y)
+{
+    if (dtype < 1 || dtype > 3 || rows < 0 || heads <= 0 || head_dim <= 0 || head_dim % 2 ||
+        !(theta > 0.0))
+        return ORACLE_BAD_ARG;
+    if (rows > 0 && (!x || !positions || !y))
+        return ORACLE_BAD_ARG;
+    const int half = head_dim / 2;
+    for (int r = 0; r < rows; ++r) {
+        for (int h = 0; h < heads; ++h) {
+            const size_t base = ((size_t)r * heads + h) * (size_t)head_dim;
+            for (int i = 0; i < half; ++i) {
+                const float f = (float)pow(theta, -2.0 * i / head_dim);
+                const float a = (float)positions[r] * f;
+                const double c = cos((double)a), s = sin((double)a);
+                const size_t i1 = base + (size_t)i, i2 = base + (size_t)i + (size_t)half;
+                const double x1 = load_elem(x, dtype, i1), x2 = load_elem(x, dtype, i2);
+                y[i1] = x1 * c - x2 * s;
+                y[i2] = x2 * c + x1 * s;
+            }
+        }
+    }
+    return ORACLE_OK;
+}

@@ -45,6 +45,15 @@ MUTANTS = {
                            "            if (!base || pool)\n                continue;\n            const size_t first"),
     "poison_half_page": ("for (int64_t e = 0; e < page_elems; ++e) {", "for (int64_t e = 0; e < page_elems / 2; ++e) {"),
     "poison_negative_bf16_nan": ("dtype == 1 ? 0x7E00u : 0x7FC0u", "dtype == 1 ? 0x7E00u : 0xFFC0u"),
+    # rotary embedding
+    "rope_sin_sign": ("y[i1] = x1 * c - x2 * s;", "y[i1] = x1 * c + x2 * s;"),
+    "rope_interleaved_pairs": ("const size_t i1 = base + (size_t)i, i2 = base + (size_t)i + (size_t)half;",
+                               "const size_t i1 = base + 2 * (size_t)i, i2 = base + 2 * (size_t)i + 1;"),
+    "rope_frequency_exponent": ("pow(theta, -2.0 * i / head_dim)", "pow(theta, -1.0 * i / head_dim)"),
+    "rope_angle_in_double": ("const float a = (float)positions[r] * f;",
+                             "const double a = (double)positions[r] * (double)f;"),
+    "rope_position_off_by_one": ("const float a = (float)positions[r] * f;",
+                                 "const float a = (float)(positions[r] + 1) * f;"),
     "append_k_v_swapped": ("memcpy((char *)v_pool + dst, (const char *)v_new + src, token_bytes);",
                            "memcpy((char *)v_pool + dst, (const char *)k_new + src, token_bytes);"),
 }

@@ -518,3 +518,75 @@ def test_pool_model_worked_sequence():
     with pytest.raises(PoolModelError):
         m.retain([1])                   # adopt a free page
     assert not m.can_alloc(4) and m.can_alloc(3)
+
+
+# ---- rotary embedding (the append fused with RoPE) ---------------------------------------
+
+def _rope_angles(pos, d, theta):
+    """The reading's angles: f_i = theta^(-2i/D) in binary32, a_i = binary32(pos) * f_i."""
+    f = (float(theta) ** (-2.0 * np.arange(d // 2) / d)).astype(np.float32)
+    return (np.asarray(pos, dtype=np.float32)[:, None] * f[None, :]).astype(np.float64)
+
+
+def test_rope_textbook_values():
+    """head_dim 2: one pair, frequency 1, so position 1 turns (1, 0) by one radian onto
+    (cos 1, sin 1) = (0.5403023058681398, 0.8414709848078965), and (0, 1) onto (-sin 1, cos 1)."""
+    x = np.array([[[1.0, 0.0]], [[0.0, 1.0]]], np.float32)
+    y = oracle.rope(3, x, [1, 1], 10000.0)
+    assert np.allclose(y[0, 0], [0.5403023058681398, 0.8414709848078965], rtol=0, atol=1e-15)
+    assert np.allclose(y[1, 0], [-0.8414709848078965, 0.5403023058681398], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("d,theta", [(64, 1e4), (128, 1e6), (8, 500.0)])
+def test_rope_is_complex_multiplication(d, theta):
+    """Independent form: z_i = x[i] + j x[i + D/2] times e^(j a_i) (numpy complex
+    exponential) gives the rotate-half result; positions up to 40k."""
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((9, 3, d)).astype(np.float32)
+    pos = np.array([0, 1, 2, 17, 300, 1535, 4096, 32767, 40000], np.int32)
+    y = oracle.rope(3, x, pos, theta)
+    a = _rope_angles(pos, d, theta)
+    z = (x[..., : d // 2] + 1j * x[..., d // 2:].astype(np.float64)) * np.exp(1j * a)[:, None, :]
+    assert np.abs(y[..., : d // 2] - z.real).max() < 1e-12
+    assert np.abs(y[..., d // 2:] - z.imag).max() < 1e-12
+
+
+def test_rope_position_zero_is_identity_and_pairs_keep_their_norm():
+    rng = np.random.default_rng(3)
+    x = W.to_storage(rng.standard_normal((5, 2, 64)).astype(np.float32), "bf16")
+    xd = W.storage_to_f32(x, "bf16").astype(np.float64)
+    y0 = oracle.rope(2, x, [0] * 5, 1e4)
+    assert np.array_equal(y0, xd)
+    y = oracle.rope(2, x, [3, 70, 511, 2048, 9999], 1e4)
+    n_in = xd[..., :32] ** 2 + xd[..., 32:] ** 2
+    n_out = y[..., :32] ** 2 + y[..., 32:] ** 2
+    assert np.abs(n_out - n_in).max() < 1e-12 * max(1.0, n_in.max())
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    """<R(q, m), R(k, n)> = <R(q, m + s), R(k, n + s)>: with theta = 16 and D = 4 the
+    frequencies 1 and 1/4 are exact in binary32, so the angles of integer positions are
+    exact and the identity holds to rounding."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 1, 4)).astype(np.float32)
+    k = rng.standard_normal((1, 1, 4)).astype(np.float32)
+    for m, n, s in [(5, 2, 7), (100, 0, 33), (1000, 999, 4000)]:
+        d0 = np.dot(oracle.rope(3, q, [m], 16.0).ravel(), oracle.rope(3, k, [n], 16.0).ravel())
+        d1 = np.dot(oracle.rope(3, q, [m + s], 16.0).ravel(), oracle.rope(3, k, [n + s], 16.0).ravel())
+        assert abs(d0 - d1) < 1e-9, (m, n, s)
+
+
+def test_rope_rejects_bad_arguments():
+    x = np.zeros((1, 1, 4), np.float32)
+    for kw in (dict(theta=0.0), dict(theta=-1.0)):
+        with pytest.raises(oracle.OracleError):
+            oracle.rope(3, x, [0], **kw)
+    with pytest.raises(oracle.OracleError):
+        oracle.rope(3, np.zeros((1, 1, 3), np.float32), [0], 1e4)
+
+
+def test_append_positions_follow_the_bottom_right_reading():
+    """Request 0: 3 new rows over 40 cached tokens -> positions 37, 38, 39; request 1: one
+    decode row over 17 tokens -> 16."""
+    pos = oracle.append_positions([0, 3, 4], [0, 3, 5], [8, 1], 16)
+    assert pos.tolist() == [37, 38, 39, 16]
