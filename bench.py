@@ -152,24 +152,34 @@ def stream_probe_gbs(mib: int = 1024, reps: int = 10):
     return 2 * x.numel() * 4 / median_s(lambda: y.copy_(x)) / 1e9
 
 
-def time_kv_append(h, b, ks, vs, L: int, stream, replays: int = 20):
+def time_kv_append(h, b, ks, vs, L: int, stream, replays: int = 20, rope_theta=None):
     """The KV append of the same step: each layer's new K/V rows ([rows, Hkv, D], seeded
     device data) written into that layer's pools by one launch, the L launches captured in
     one HIP graph. Timed after the attention measurement (it overwrites the new tokens'
-    slots). Bytes: the new rows read plus the same bytes written, for K and V."""
+    slots). Bytes: the new rows read plus the same bytes written, for K and V. With
+    rope_theta, the append fused with the rotary embedding (fl_paged_kv_append_rope), whose
+    query heads are rotated in place too: their bytes are read and written as well."""
     import torch
     gen = torch.Generator(device="cuda:0")
     gen.manual_seed(7)
     shape = (b.rows, b.num_kv_heads, b.head_dim)
     kn = [torch.randn(shape, dtype=ks[0].dtype, device="cuda:0", generator=gen) for _ in range(L)]
     vn = [torch.randn(shape, dtype=ks[0].dtype, device="cuda:0", generator=gen) for _ in range(L)]
+    qn = [torch.randn((b.rows, b.num_qo_heads, b.head_dim), dtype=ks[0].dtype, device="cuda:0",
+                      generator=gen) for _ in range(L)] if rope_theta else None
+
+    def call(l):
+        if rope_theta:
+            h.append_rope(qn[l], kn[l], vn[l], ks[l], vs[l], rope_theta)
+        else:
+            h.append(kn[l], vn[l], ks[l], vs[l])
     for l in range(L):
-        h.append(kn[l], vn[l], ks[l], vs[l])
+        call(l)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for l in range(L):
-            h.append(kn[l], vn[l], ks[l], vs[l])
+            call(l)
     g.replay()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -181,10 +191,14 @@ def time_kv_append(h, b, ks, vs, L: int, stream, replays: int = 20):
     torch.cuda.synchronize()
     us = sorted(a.elapsed_time(e) / L * 1e3 for a, e in ev)
     us_med = us[len(us) // 2]
-    nbytes = b.rows * b.num_kv_heads * b.head_dim * b.elem_bytes * 2 * 2
-    return {"us_per_call_median": round(us_med, 3), "bytes_per_call": nbytes,
-            "GB_per_s": round(nbytes / (us_med * 1e-6) / 1e9, 2), "rows": b.rows,
-            "launch": "hip_graph", "layers": L}
+    heads = 2 * b.num_kv_heads + (b.num_qo_heads if rope_theta else 0)
+    nbytes = b.rows * heads * b.head_dim * b.elem_bytes * 2
+    d = {"us_per_call_median": round(us_med, 3), "bytes_per_call": nbytes,
+         "GB_per_s": round(nbytes / (us_med * 1e-6) / 1e9, 2), "rows": b.rows,
+         "launch": "hip_graph", "layers": L}
+    if rope_theta:
+        d["rope_theta"] = rope_theta
+    return d
 
 
 def time_append_attention(h, b, q, ks, vs, outs, L: int, stream, replays: int = 20):
@@ -553,6 +567,7 @@ def main(argv=None):
                                "kind": "device copy of 1 GiB, bytes read + written per second",
                                "achieved_frac_of_probe": round(achieved / probe, 4)}
         res["kv_append"] = time_kv_append(h, b, ks, vs, L, stream)
+        res["kv_append_rope"] = time_kv_append(h, b, ks, vs, L, stream, rope_theta=1e4)
         res["append_attention"] = time_append_attention(h, b, q, ks, vs, outs, L, stream)
     if not args.no_cpu_baseline and not args.attention_only:
         res["cpu_baseline"] = cpu_baseline(b, out0, args.cpu_budget)

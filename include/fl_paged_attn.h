@@ -179,6 +179,33 @@ fl_status fl_paged_kv_append(fl_handle h, const void *k_new, const void *v_new, 
                              void *v_pool, void *stream);
 
 /*
+ * The same append fused with the rotary position embedding (RoPE) of the step's new rows:
+ * one kernel launch rotates each new row's key heads by its token's position before they
+ * are written to the pool, copies its value heads unchanged, and rotates its query heads in
+ * place for the run() that follows. The pages apply RoPE in the Qwen2.5-style decoder they
+ * run (Torchlet README, the running example; flashlet README, roadmap: a RoPE fusion
+ * kernel) without spelling it out; this follows that model family's rotate-half form.
+ *
+ * Row i of request r has position t = kv_len[r] - qo_len[r] + i (as for the plain append).
+ * For each head vector x (head_dim D) and i < D/2, with f_i = rope_theta^(-2i/D) rounded
+ * to fp32 and the fp32 angle a = (float)t * f_i:
+ *     x'[i]       = x[i] cos a - x[i + D/2] sin a
+ *     x'[i + D/2] = x[i + D/2] cos a + x[i] sin a
+ * computed in fp32 and rounded once to the element type. Then
+ *     k_pool[page, slot, :, :] = rotated k_new[qo_indptr[r] + i, :, :]
+ *     v_pool[page, slot, :, :] = v_new[qo_indptr[r] + i, :, :]
+ *     q[qo_indptr[r] + i, :, :] = rotated q[...]          (skipped when q is NULL)
+ * Device pointers: q [rows, num_qo_heads, head_dim] (read and written; may be NULL),
+ * k_new, v_new, k_pool, v_pool as for fl_paged_kv_append, each aligned to the element size.
+ * rope_theta: the base (e.g. 1e4, or 1e6 for Qwen2.5). Enqueues on `stream`; never
+ * synchronises or allocates (graph-capturable).
+ * Errors: as fl_paged_kv_append, plus FL_ERR_INVALID_ARG for rope_theta <= 0 or not finite
+ * and FL_ERR_UNSUPPORTED for an odd head_dim or one above 128.
+ */
+fl_status fl_paged_kv_append_rope(fl_handle h, void *q, const void *k_new, const void *v_new,
+                                  void *k_pool, void *v_pool, float rope_theta, void *stream);
+
+/*
  * Append one layer's new K/V rows and compute that layer's attention in one call: the
  * result equals fl_paged_kv_append followed by fl_paged_attn_run (same pointers, same
  * plan), up to the floating-point summation order. On decode-only plans (every request has

@@ -49,7 +49,7 @@ class FlError(RuntimeError):
 
 EXPORTED = ("fl_paged_attn_create", "fl_paged_attn_destroy", "fl_paged_attn_plan",
             "fl_paged_attn_run", "fl_paged_kv_append", "fl_paged_attn_run_append",
-            "fl_paged_kv_append_slots",
+            "fl_paged_kv_append_slots", "fl_paged_kv_append_rope",
             "fl_paged_attn_plan_info",
             "fl_paged_attn_get_work_items", "fl_page_pool_create", "fl_page_pool_destroy",
             "fl_page_pool_alloc", "fl_page_pool_reserve", "fl_page_pool_retain",
@@ -157,6 +157,16 @@ def fl_paged_kv_append(h, k_new: int, v_new: int, k_pool: int, v_pool: int,
            "fl_paged_kv_append")
 
 
+def fl_paged_kv_append_rope(h, q: Optional[int], k_new: int, v_new: int, k_pool: int, v_pool: int,
+                            rope_theta: float, stream: int = 0) -> None:
+    """Device pointers as integers: the append with the rotary embedding of the new rows'
+    key heads (written to the pool) and query heads (rotated in place; q may be None)."""
+    _check(load_library().fl_paged_kv_append_rope(
+        h, ctypes.c_void_p(q) if q else None, ctypes.c_void_p(k_new), ctypes.c_void_p(v_new),
+        ctypes.c_void_p(k_pool), ctypes.c_void_p(v_pool), ctypes.c_float(rope_theta),
+        ctypes.c_void_p(int(stream))), "fl_paged_kv_append_rope")
+
+
 def fl_paged_attn_run_append(h, q: int, k_new: int, v_new: int, k_pool: int, v_pool: int, out: int,
                              lse: Optional[int] = None, stream: int = 0) -> None:
     """Device pointers as integers: append the new K/V rows and attend, in one launch on
@@ -249,6 +259,11 @@ class PagedAttention:
     def append(self, k_new, v_new, k_pool, v_pool, stream=None):
         fl_paged_kv_append(self.handle, k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
                            v_pool.data_ptr(), self._stream(stream))
+
+    def append_rope(self, q, k_new, v_new, k_pool, v_pool, rope_theta, stream=None):
+        fl_paged_kv_append_rope(self.handle, None if q is None else q.data_ptr(), k_new.data_ptr(),
+                                v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                float(rope_theta), self._stream(stream))
 
     def run_append(self, q, k_new, v_new, k_pool, v_pool, out, lse=None, stream=None):
         fl_paged_attn_run_append(self.handle, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),

@@ -236,7 +236,8 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
     h->off_tickets = align_up(h->off_wg_rec + L.group_cap * fl::kRecInts * 4, 256);
     h->off_steps = align_up(h->off_tickets + blocks * 4, 256);
     h->off_append = align_up(h->off_steps + std::max<int64_t>(1, L.max_tiles) * 4, 256);
-    h->meta_bytes = align_up(h->off_append + std::max<int64_t>(1, cfg->max_qo_rows) * 4, 256);
+    // append region: the rows' token slots, then their positions (rows ints each)
+    h->meta_bytes = align_up(h->off_append + std::max<int64_t>(1, cfg->max_qo_rows) * 8, 256);
 
     if (!h->host_only) {
         hipError_t e;
@@ -312,8 +313,11 @@ fl_status fl_paged_attn_plan(fl_handle h, int32_t batch, const int32_t *qo_indpt
         std::memcpy(st_buf, p.segs.data(), p.segs.size() * 4);
         std::memcpy(st_buf + h->off_wg_rec, p.wg_rec.data(), p.wg_rec.size() * 4);
         std::memcpy(st_buf + h->off_steps, p.step_rows.data(), p.step_rows.size() * 4);
-        const int64_t append_bytes = p.append_ok ? (int64_t)p.append_rows.size() * 4 : 0;
-        if (append_bytes) std::memcpy(st_buf + h->off_append, p.append_rows.data(), append_bytes);
+        const int64_t append_bytes = p.append_ok ? (int64_t)p.append_rows.size() * 8 : 0;
+        if (append_bytes) {
+            std::memcpy(st_buf + h->off_append, p.append_rows.data(), append_bytes / 2);
+            std::memcpy(st_buf + h->off_append + append_bytes / 2, p.append_pos.data(), append_bytes / 2);
+        }
         fl::StageCopy sc{h->d_stage[slot], h->d_meta,
                          {0, h->off_wg_rec, h->off_steps, h->off_append},
                          {(int64_t)p.segs.size() * 4, (int64_t)p.wg_rec.size() * 4,
@@ -404,6 +408,47 @@ fl_status fl_paged_kv_append(fl_handle h, const void *k_new, const void *v_new, 
                      (int32_t)rows, (int32_t)row_bytes};
     const int le = fl::launch_kv_append(a, stream);
     if (le != (int)hipSuccess) return hip_err((hipError_t)le, "kv append launch");
+    return FL_OK;
+}
+
+fl_status fl_paged_kv_append_rope(fl_handle h, void *q, const void *k_new, const void *v_new,
+                                  void *k_pool, void *v_pool, float rope_theta, void *stream) {
+    g_last_error.clear();
+    if (!h) return set_err(FL_ERR_INVALID_ARG, "handle is NULL");
+    if (!(rope_theta > 0.f) || !std::isfinite(rope_theta))
+        return set_err(FL_ERR_INVALID_ARG, "rope_theta must be positive and finite");
+    if (h->cfg.head_dim > 2 * fl::kMaxRopePairs || h->cfg.head_dim % 2)
+        return set_err(FL_ERR_UNSUPPORTED, "rotary embedding needs an even head_dim <= 128");
+    if (h->host_only) return set_err(FL_ERR_UNSUPPORTED, "append on a host-only handle");
+    if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "append before a successful plan()");
+    const Plan &p = h->plan;
+    if (!p.append_ok) return set_err(FL_ERR_INVALID_ARG, "the plan has no append slots: " + p.append_err);
+    const int64_t rows = (int64_t)p.append_rows.size();
+    if (rows == 0) return FL_OK;
+    if (!k_new || !v_new || !k_pool || !v_pool)
+        return set_err(FL_ERR_INVALID_ARG, "k_new, v_new, k_pool and v_pool must not be NULL");
+    const int64_t elem = h->cfg.dtype == FL_F32 ? 4 : 2;
+    if (((uintptr_t)q | (uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_pool | (uintptr_t)v_pool) &
+        (uintptr_t)(elem - 1))
+        return set_err(FL_ERR_INVALID_ARG, "q, k_new, v_new, k_pool and v_pool must be aligned to the element size");
+    fl::RopeArgs a{};
+    a.dst_rows = (const int32_t *)(h->d_meta + h->off_append);
+    a.pos = a.dst_rows + rows;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.q = q;
+    a.rows = (int32_t)rows;
+    a.num_kv_heads = h->cfg.num_kv_heads;
+    a.num_qo_heads = h->cfg.num_qo_heads;
+    a.head_dim = h->cfg.head_dim;
+    a.dtype = h->cfg.dtype;
+    // pair frequencies theta^(-2i/D), formed in double and rounded once to fp32
+    for (int i = 0; i < h->cfg.head_dim / 2; ++i)
+        a.inv_freq[i] = (float)std::pow((double)rope_theta, -2.0 * i / h->cfg.head_dim);
+    const int le = fl::launch_kv_append_rope(a, stream);
+    if (le != (int)hipSuccess) return hip_err((hipError_t)le, "kv append + rope launch");
     return FL_OK;
 }
 

@@ -135,6 +135,7 @@ struct Plan {
     int64_t part_rows = 0;
     std::vector<int32_t> append_rows;  // per query row: token row page * P + slot of the
                                        // token it stands for (the KV append's destination)
+    std::vector<int32_t> append_pos;   // per query row: that token's position in its request
     bool append_ok = false;            // every row has a slot, no two rows share one
     std::string append_err;            // why not, when !append_ok
 };
@@ -197,6 +198,24 @@ struct AppendArgs {
     int32_t row_bytes;
 };
 int launch_kv_append(const AppendArgs &a, void *stream);
+
+// KV append fused with the rotary position embedding (kv_rope.hip): row r's K heads are
+// rotated by position pos[r] and written to token row dst_rows[r] of k_pool, its V heads
+// copied to v_pool, and (when q is not NULL) its query heads rotated in place. inv_freq[i]
+// (i < head_dim / 2) are the pair frequencies, already rounded to fp32 on the host.
+constexpr int kMaxRopePairs = 64;  // head_dim <= 128
+struct RopeArgs {
+    const int32_t *dst_rows;
+    const int32_t *pos;
+    const void *k_new;
+    const void *v_new;
+    void *k_pool;
+    void *v_pool;
+    void *q;
+    int32_t rows, num_kv_heads, num_qo_heads, head_dim, dtype;
+    float inv_freq[kMaxRopePairs];
+};
+int launch_kv_append_rope(const RopeArgs &a, void *stream);
 
 // Poison: fill whole pages of one or two pools with a 16-byte pattern (kv_poison.hip).
 constexpr int kPoisonIdsPerLaunch = 256;

@@ -127,6 +127,7 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
     // (the position the bottom-right causal mask gives it); its K/V row goes to that
     // token's page slot. Recorded as the token row page * P + slot (below 2^31 / Hkv).
     out.append_rows.assign((size_t)rows, 0);
+    out.append_pos.assign((size_t)rows, 0);
     out.append_ok = true;
     for (int32_t r = 0; r < B && out.append_ok; ++r) {
         const int32_t np = in.kv_indptr[r + 1] - in.kv_indptr[r];
@@ -145,6 +146,7 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         for (int32_t i = 0; i < ql; ++i) {
             const int32_t t = kv_len - ql + i;
             out.append_rows[q0 + i] = pages[t / P] * P + t % P;
+            out.append_pos[q0 + i] = t;
         }
     }
     if (out.append_ok && rows > 1) {

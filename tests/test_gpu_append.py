@@ -303,3 +303,113 @@ def test_run_append_graph_replay_across_replans():
         x = torch.randn(1 << 20, device="cuda:0")
         float(x.sum())
         torch.cuda.synchronize()
+
+
+# ---- the append fused with the rotary embedding (fl_paged_kv_append_rope) ----------------
+# The rotation is floating-point work: rotated K rows in the pool and rotated query heads
+# must be within one unit in the last place of the storage type of the oracle's double
+# result (the device rotates in fp32 and rounds once; the oracle's value, rounded once, may
+# sit across a rounding boundary), plus 1e-6 of fp32 arithmetic (4e-6 for fp32 storage).
+# V rows and every untouched slot must match the oracle's append byte for byte.
+
+_MANT = {"bf16": 7, "f16": 10, "f32": 23}
+_EMIN = {"bf16": -126, "f16": -14, "f32": -126}
+
+
+def _ulp(v, dtype):
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** _EMIN[dtype])))
+    return 2.0 ** (e - _MANT[dtype])
+
+
+def _rope_tol(ref, dtype):
+    if dtype == "f32":
+        return 4e-6 * (1.0 + np.abs(ref))
+    return _ulp(ref, dtype) + 1e-6 * (1.0 + np.abs(ref))
+
+
+def _bits(a, dtype):
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint32 if dtype == "f32" else np.uint16)
+
+
+def _check_rope(b, theta, with_q=True, what=""):
+    import torch
+    announce(f"append+rope {what or b.name}: dtype={b.dtype} rows={b.rows} Hq={b.num_qo_heads} "
+             f"Hkv={b.num_kv_heads} D={b.head_dim} P={b.page_size} theta={theta} q={with_q}")
+    st = W.append_step(b)
+    code = W.DTYPE_CODES[b.dtype]
+    pos = oracle.append_positions(b.qo_indptr, b.kv_indptr, b.last_page_len, b.page_size)
+    k_rot = oracle.rope(code, st.k_new, pos, theta)
+    q_rot = oracle.rope(code, b.q, pos, theta)
+    ref_k, ref_v = oracle.kv_append(b, W.to_storage(k_rot.astype(np.float32), b.dtype), st.v_new,
+                                    st.k_before, st.v_before)
+    h = fl.PagedAttention(config_for(b), device=0)
+    h.plan(b.qo_indptr, b.kv_indptr, b.kv_indices, b.last_page_len, b.num_pages,
+           causal=b.causal, sm_scale=b.sm_scale)
+    k, v = to_device(st.k_before, b.dtype), to_device(st.v_before, b.dtype)
+    kn, vn = to_device(st.k_new, b.dtype), to_device(st.v_new, b.dtype)
+    q = to_device(b.q, b.dtype)
+    h.append_rope(q if with_q else None, kn, vn, k, v, theta)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bytes(to_host_bits(v, b.dtype)), _bytes(ref_v)), f"{what}: V pool"
+    got_k = to_host_bits(k, b.dtype)
+    changed = _bits(ref_k, b.dtype) != _bits(st.k_before, b.dtype)
+    assert changed.sum() == k_rot.size, "every new K value lands in a poisoned slot"
+    assert np.array_equal(_bits(got_k, b.dtype)[~changed], _bits(ref_k, b.dtype)[~changed]), \
+        f"{what}: K pool outside the new slots"
+    gk = W.storage_to_f32(got_k, b.dtype).astype(np.float64)[changed]
+    rk = W.storage_to_f32(ref_k, b.dtype).astype(np.float64)[changed]
+    assert (np.abs(gk - rk) <= _rope_tol(rk, b.dtype) + _ulp(rk, b.dtype) * (b.dtype != "f32")).all(), \
+        f"{what}: rotated K, max err {np.abs(gk - rk).max()}"
+    gq = W.storage_to_f32(to_host_bits(q, b.dtype), b.dtype).astype(np.float64)
+    if with_q:
+        err = np.abs(gq - q_rot)
+        assert (err <= _rope_tol(q_rot, b.dtype)).all(), f"{what}: rotated Q, max err {err.max()}"
+    else:
+        assert np.array_equal(_bits(to_host_bits(q, b.dtype), b.dtype), _bits(b.q, b.dtype))
+    return h, q, k, v, ref_k, ref_v, q_rot
+
+
+ROPE_CASES = [
+    dict(kv=[80, 17, 33, 5, 1], qo=[37, 1, 0, 5, 1], Hq=14, Hkv=2, D=64, P=16, dtype="bf16", theta=1e4),
+    dict(kv=[16, 17, 64, 65, 300], Hq=12, Hkv=2, D=128, P=64, dtype="f16", theta=1e6),
+    dict(kv=[50, 20, 256], qo=[50, 1, 256], Hq=8, Hkv=1, D=64, P=256, dtype="f32", theta=500.0),
+    dict(kv=[32773, 40000, 7], Hq=8, Hkv=1, D=128, P=256, dtype="bf16", theta=1e6),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES,
+                         ids=lambda c: f"{c['dtype']}-D{c['D']}-P{c['P']}-theta{c['theta']:g}-{'ragged' if 'qo' in c else 'decode'}")
+def test_append_rope_variants(case):
+    b = W.make_batch(case["kv"], case.get("qo"), num_qo_heads=case["Hq"], num_kv_heads=case["Hkv"],
+                     head_dim=case["D"], page_size=case["P"], dtype=case["dtype"],
+                     num_pages=sum(-(-k // case["P"]) for k in case["kv"]) + 6, seed=37,
+                     keep_dense=True)
+    _check_rope(b, case["theta"], what=str(case))
+
+
+@pytest.mark.parametrize("name", sorted(W.WORKLOADS))
+def test_append_rope_workloads_full_size(name):
+    _check_rope(W.WORKLOADS[name](keep_dense=True), 1e4)
+
+
+def test_append_rope_without_q_leaves_q_alone():
+    b = W.make_batch([40, 3, 300], [4, 1, 1], num_qo_heads=14, num_kv_heads=2, head_dim=64,
+                     page_size=16, dtype="bf16", seed=38, keep_dense=True)
+    _check_rope(b, 1e4, with_q=False, what="q=NULL")
+
+
+def test_attention_after_append_rope_matches_oracle():
+    """The attention call that follows reads the rotated rows: against the oracle's
+    attention over its own rotated (and rounded) queries and pools."""
+    import dataclasses
+    import torch
+    b = W.make_batch([300, 17, 1536, 100], [1, 1, 512, 1], num_qo_heads=14, num_kv_heads=2,
+                     head_dim=64, page_size=16, dtype="bf16", seed=39, num_pages=200, keep_dense=True)
+    h, q, k, v, ref_k, ref_v, q_rot = _check_rope(b, 1e6, what="then attention")
+    out = torch.full(q.shape, float("nan"), dtype=torch_dtype(b.dtype), device="cuda:0")
+    h.run(q, k, v, out)
+    torch.cuda.synchronize()
+    bb = dataclasses.replace(b, q=W.to_storage(q_rot.astype(np.float32), b.dtype), k_pool=ref_k, v_pool=ref_v)
+    ref_out, _ = oracle.attention(bb)
+    compare(bb, out, None, ref_out, None, "attention after append+rope")

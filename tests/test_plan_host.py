@@ -404,6 +404,10 @@ def test_append_on_empty_plan_and_host_handle():
     assert h.append_slots().size == 0
     msg = _expect(fl.FL_ERR_UNSUPPORTED, fl.fl_paged_kv_append, h.handle, 16, 16, 16, 16)
     assert "host-only" in msg
+    msg = _expect(fl.FL_ERR_UNSUPPORTED, fl.fl_paged_kv_append_rope, h.handle, 16, 16, 16, 16, 16, 1e4)
+    assert "host-only" in msg
+    for theta in (0.0, -1.0, float("inf"), float("nan")):
+        _expect(fl.FL_ERR_INVALID_ARG, fl.fl_paged_kv_append_rope, h.handle, 16, 16, 16, 16, 16, theta)
 
 
 def test_neighbouring_shares_share_an_xcd():
