@@ -413,3 +413,49 @@ def test_attention_after_append_rope_matches_oracle():
     bb = dataclasses.replace(b, q=W.to_storage(q_rot.astype(np.float32), b.dtype), k_pool=ref_k, v_pool=ref_v)
     ref_out, _ = oracle.attention(bb)
     compare(bb, out, None, ref_out, None, "attention after append+rope")
+
+
+def test_append_rope_graph_replay_across_replans():
+    """append_rope captured once in a HIP graph; each replay after a new plan (other page ids
+    and lengths of the same shape) rotates by the new positions into the new slots."""
+    import torch
+    b1 = W.make_batch([40, 300, 17, 2], [1, 1, 9, 1], num_qo_heads=14, num_kv_heads=2, head_dim=64,
+                      page_size=16, dtype="bf16", seed=63, num_pages=64, keep_dense=True)
+    b2 = W.relabel_pages(b1, W.rng_for(64, 0, 0).permutation(b1.num_pages))
+    theta = 1e4
+    announce("append+rope graph replay across re-plans")
+    h = fl.PagedAttention(config_for(b1), device=0)
+    h.plan(b1.qo_indptr, b1.kv_indptr, b1.kv_indices, b1.last_page_len, b1.num_pages,
+           causal=True, sm_scale=b1.sm_scale)
+    st1, st2 = W.append_step(b1), W.append_step(b2)
+    k, v = to_device(st1.k_before, "bf16"), to_device(st1.v_before, "bf16")
+    kn, vn = to_device(st1.k_new, "bf16"), to_device(st1.v_new, "bf16")
+    q = to_device(b1.q, "bf16")
+    h.append_rope(q, kn, vn, k, v, theta)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h.append_rope(q, kn, vn, k, v, theta)
+    pos = oracle.append_positions(b1.qo_indptr, b1.kv_indptr, b1.last_page_len, b1.page_size)
+    q_rot = oracle.rope(2, b1.q, pos, theta)
+    k_rot = W.to_storage(oracle.rope(2, st1.k_new, pos, theta).astype(np.float32), "bf16")
+    for rep in range(4):
+        bb, st = (b2, st2) if rep % 2 else (b1, st1)
+        h.plan(bb.qo_indptr, bb.kv_indptr, bb.kv_indices, bb.last_page_len, bb.num_pages,
+               causal=True, sm_scale=bb.sm_scale)
+        k.copy_(to_device(st.k_before, "bf16"))
+        v.copy_(to_device(st.v_before, "bf16"))
+        q.copy_(to_device(bb.q, "bf16"))
+        g.replay()
+        torch.cuda.synchronize()
+        # same lengths, so the same positions; only the slots differ
+        ref_k, ref_v = oracle.kv_append(bb, k_rot, st.v_new, st.k_before, st.v_before)
+        assert np.array_equal(_bytes(to_host_bits(v, "bf16")), _bytes(ref_v)), f"replay {rep}: V"
+        gk = W.storage_to_f32(to_host_bits(k, "bf16"), "bf16").astype(np.float64)
+        rk = W.storage_to_f32(ref_k, "bf16").astype(np.float64)
+        both_nan = np.isnan(gk) & np.isnan(rk)   # unused slots hold the poison in both
+        with np.errstate(invalid="ignore"):
+            ok = np.abs(gk - rk) <= 2 * _ulp(rk, "bf16") + 1e-6 * (1 + np.abs(rk))
+        assert (both_nan | ok).all(), f"replay {rep}: K"
+        gq = W.storage_to_f32(to_host_bits(q, "bf16"), "bf16").astype(np.float64)
+        assert (np.abs(gq - q_rot) <= _rope_tol(q_rot, "bf16")).all(), f"replay {rep}: Q"
