@@ -909,7 +909,7 @@ __device__ __forceinline__ void merge_pieces(const Seg &w, const AttnArgs &a, in
 // output rows: final rows for a whole row block, device-scope fp32 partial rows for a piece.
 // LAST: the workgroup's final fold: no segment follows, so the LDS slots need no release
 // (the merge phase has a barrier of its own before it reads the pending pieces' fields).
-template <class T, int DT, int D, int NW, bool WR, bool LAST = false>
+template <class T, int DT, int D, int NW, bool WR, bool LAST = false, bool HOIST = true>
 __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, const Seg &cs, int k,
                                              float &m_run, float &l_run, f32x4 *o, int &npend,
                                              int wave, int col, int grp) {
@@ -938,6 +938,15 @@ __device__ __forceinline__ void fold_segment(Smem<D> &sm, const AttnArgs &a, con
             lv[v] = sm.l[v][r];
 #pragma unroll
             for (int q = 0; q < RS::NCH; ++q) ov[v][q] = *reinterpret_cast<const f32x4 *>(&sm.o[v][r][RS::col(t, q)]);
+        }
+        // HOIST: every read above in flight before the first use below (no instruction: the
+        // scheduler may not sink a read past its use here). Measured: 0.5% faster on
+        // memory-bound decode, 2% slower where two workgroups share a compute unit.
+        if constexpr (HOIST) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int q = 0; q < RS::NCH; ++q) asm volatile("" : "+v"(ov[v][q]));
         }
         float M = kNegInf;
 #pragma unroll
@@ -1144,7 +1153,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
         if (p0 == seg_end) {  // the same step in every wave: segment k is done
             if constexpr (FUSE)
                 if (app_row >= 0) write_new_rows<D>(new_slot(k), a, cs, app_row, hkv, lane);
-            fold_segment<T, DT, D, NW, WR>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);
+            fold_segment<T, DT, D, NW, WR, false, EARLY>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);
             ++k;
             cs = seg_fields_lds(hdr_slot(k));
             seg_end = k + 1 < seg_e ? lds_int(hdr_slot(k + 1) + 4 * FL_WI_POS_BEGIN) : nsteps;
@@ -1210,7 +1219,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     group(p0, std::false_type{});
     if constexpr (FUSE)
         if (app_row >= 0) write_new_rows<D>(new_slot(k), a, cs, app_row, hkv, lane);
-    fold_segment<T, DT, D, NW, WR, true>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);
+    fold_segment<T, DT, D, NW, WR, true, EARLY>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);
 
     // ---- merge tickets of the partial pieces (at most the first and the last) -----------
     // The partial rows went out as device-scope stores; each wave waits for their
