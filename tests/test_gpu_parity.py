@@ -132,7 +132,7 @@ def _random_case(seed):
     return b, splits
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(40))
 def test_random_configurations(seed):
     b, splits = _random_case(seed)
     _check(b, num_splits=splits, what=f"random-{seed}")
