@@ -4,8 +4,24 @@
  * One plan per scheduling step, one run per layer, following the plan()/run() split of
  * an attention backend (flashlet README, repository layout: backends/base.py) and the
  * practice of keeping per-step metadata in persistent device buffers that are updated
- * in place (flashlet README, design bullets), so that run() always launches with the
- * same arguments.
+ * in place (flashlet README, design bullets: metadata updated in place each step, so the
+ * launches can be captured in a graph; Torchlet README, Implemented Versions: static
+ * buffers, then the decode step captured once and replayed).
+ *
+ * Graph replay. Every plan has a launch class (fl_paged_attn_plan_launch). Two plans of
+ * one class make run() -- and each of the append calls -- enqueue exactly the same
+ * launches (grid, kernel, arguments): everything that differs between them (lengths, page
+ * ids, request count, causal flag, scale, how many workgroups have work) travels in the
+ * handle's device metadata, which plan() rewrites in place. So a HIP graph captured from
+ * run() calls replays correctly after any later plan of the same class, as long as the
+ * captured q / out / lse / new-row buffers hold that plan's rows (size them for
+ * max_qo_rows) and the pools hold its pages. The class depends only on the kind of step:
+ * decode-only steps (every request at most one query row) share one class per handle,
+ * steps with prefill rows another (at head_dim 64 in a 16-bit type they run two
+ * workgroups per compute unit), decode steps in whole-row blocks (fl_config.whole_rows)
+ * a third; a plan with num_splits > 0 has a class of its own grid. A launch replayed
+ * after a plan of another class does not compute: it touches no memory but the handle's
+ * status word, where fl_paged_attn_refused_launches() counts it.
  *
  * Operation (run). For request r with query rows qo_indptr[r] .. qo_indptr[r+1] and
  * pages kv_indices[kv_indptr[r] .. kv_indptr[r+1]) holding
@@ -95,8 +111,10 @@ typedef struct {
                                   request has at most one query row) with num_kv_heads *
                                   head_dim = 128, num_kv_heads > 1, at most 16 query heads
                                   and a 16-bit type. 0: used where they apply and the step
-                                  has at least one query row per compute unit; 1: used
-                                  wherever they apply; -1: never (one block per kv head) */
+                                  has at least one query row per compute unit; 1: used on
+                                  every decode-only step (create returns
+                                  FL_ERR_UNSUPPORTED for a shape that cannot take them);
+                                  -1: never (one block per kv head)                       */
 } fl_config;
 
 /*
@@ -137,16 +155,17 @@ fl_status fl_paged_attn_plan(fl_handle h, int32_t batch, const int32_t *qo_indpt
                              float sm_scale, int32_t num_splits, void *stream);
 
 /*
- * Compute attention for one layer with the current plan: one kernel launch. Row blocks
- * cut into several pieces are merged inside the same launch by the piece that finishes
- * last. Device pointers:
+ * Compute attention for one layer with the current plan: one kernel launch (also for an
+ * empty plan, whose workgroups all exit at once). Row blocks cut into several pieces are
+ * merged inside the same launch by the piece that finishes last. Device pointers:
  *   q       [rows, num_qo_heads, head_dim]
  *   k_pool  [num_pages, page_size, num_kv_heads, head_dim]
  *   v_pool  same layout as k_pool
  *   out     [rows, num_qo_heads, head_dim], written in full
  *   lse     float[rows, num_qo_heads] or NULL
  * All pointers 16-byte aligned. Enqueues on `stream` and returns; never synchronises or
- * allocates, so it may be captured into a HIP graph.
+ * allocates, so it may be captured into a HIP graph (valid for every later plan of the
+ * same launch class; see "Graph replay" above).
  */
 fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, const void *v_pool,
                             void *out, float *lse, void *stream);
@@ -168,12 +187,16 @@ fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, cons
  *   k_new, v_new    [rows, num_kv_heads, head_dim], rows = qo_indptr[batch] of the plan
  *   k_pool, v_pool  [num_pages, page_size, num_kv_heads, head_dim], one layer
  * All pointers 16-byte aligned; the element type is the handle's fl_dtype. Enqueues on
- * `stream` and returns; never synchronises or allocates (graph-capturable).
+ * `stream` and returns; never synchronises or allocates. The launch is the same for every
+ * plan of the handle (its grid covers max_qo_rows rows; the row count and slots come from
+ * the device metadata), so a captured append replays correctly after any later plan; a
+ * replay after a plan without valid append slots writes nothing and is counted by
+ * fl_paged_attn_refused_launches().
  * Errors: FL_ERR_NOT_PLANNED before a successful plan; FL_ERR_INVALID_ARG when a request
  * of the plan has more query rows than cached tokens (possible without the causal mask),
  * when two rows would write the same slot (a new token in a page two requests share), or
  * for NULL or misaligned pointers; FL_ERR_UNSUPPORTED on a host-only handle, or when
- * rows x (token row bytes / 16) reaches 2^31. A plan of zero rows makes this a no-op.
+ * max_qo_rows x (token row bytes / 16) reaches 2^31. A plan of zero rows writes nothing.
  */
 fl_status fl_paged_kv_append(fl_handle h, const void *k_new, const void *v_new, void *k_pool,
                              void *v_pool, void *stream);
@@ -198,7 +221,8 @@ fl_status fl_paged_kv_append(fl_handle h, const void *k_new, const void *v_new, 
  * Device pointers: q [rows, num_qo_heads, head_dim] (read and written; may be NULL),
  * k_new, v_new, k_pool, v_pool as for fl_paged_kv_append, each aligned to the element size.
  * rope_theta: the base (e.g. 1e4, or 1e6 for Qwen2.5). Enqueues on `stream`; never
- * synchronises or allocates (graph-capturable).
+ * synchronises or allocates; one launch for every plan of the handle, as for
+ * fl_paged_kv_append (graph-capturable).
  * Errors: as fl_paged_kv_append, plus FL_ERR_INVALID_ARG for rope_theta <= 0 or not finite
  * and FL_ERR_UNSUPPORTED for an odd head_dim or one above 128.
  */
@@ -217,7 +241,8 @@ fl_status fl_paged_kv_append_rope(fl_handle h, void *q, const void *k_new, const
  * workgroups read; fp32) make the two launches in order.
  * Device pointers as for fl_paged_kv_append and fl_paged_attn_run; all 16-byte aligned.
  * Errors: those of the two calls (FL_ERR_INVALID_ARG when the plan has no valid append
- * slots). Enqueues on `stream`; never synchronises or allocates (graph-capturable).
+ * slots). Enqueues on `stream`; never synchronises or allocates (graph-capturable: the
+ * one-launch form carries the plan's fused class, fl_paged_attn_plan_launch).
  */
 fl_status fl_paged_attn_run_append(fl_handle h, const void *q, const void *k_new, const void *v_new,
                                    void *k_pool, void *v_pool, void *out, float *lse, void *stream);
@@ -238,6 +263,28 @@ fl_status fl_paged_kv_append_slots(fl_handle h, int32_t *slots, int32_t capacity
  */
 fl_status fl_paged_attn_plan_info(fl_handle h, int32_t *num_work_items, int32_t *num_groups,
                                   int32_t *max_splits, int64_t *workspace_bytes);
+
+/*
+ * The launch the current plan needs (works on host-only handles, which plan as the device
+ * would): *launch_class names the kernel variant and grid of fl_paged_attn_run, and
+ * *fused_class those of the one-launch fl_paged_attn_run_append (0 when the plan takes two
+ * launches there: prefill rows, fp32, or no valid append slots); *grid is the number of
+ * workgroups launched and *busy_groups how many of them have work (the rest exit at once).
+ * Plans with equal classes launch identically, so a graph captured under one replays
+ * correctly under the other. Outputs may be NULL. FL_ERR_NOT_PLANNED without a plan.
+ */
+fl_status fl_paged_attn_plan_launch(fl_handle h, int32_t *launch_class, int32_t *fused_class,
+                                    int32_t *grid, int32_t *busy_groups);
+
+/*
+ * Number of launches of this handle refused since the last call (then reset to zero): a
+ * launch refuses when the plan current at its execution has another launch class than
+ * the one it was enqueued for (a graph replayed after a plan of another kind), or, for the
+ * append kernels, when that plan has no valid append slots. A refused launch writes no
+ * output. Waits for all work on the handle's device first (hipDeviceSynchronize).
+ * Host-only handles report 0.
+ */
+fl_status fl_paged_attn_refused_launches(fl_handle h, int32_t *count);
 
 /*
  * Copy the current plan's work items to host memory: FL_WORK_ITEM_INTS int32 per item,

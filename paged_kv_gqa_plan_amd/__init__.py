@@ -50,8 +50,8 @@ class FlError(RuntimeError):
 EXPORTED = ("fl_paged_attn_create", "fl_paged_attn_destroy", "fl_paged_attn_plan",
             "fl_paged_attn_run", "fl_paged_kv_append", "fl_paged_attn_run_append",
             "fl_paged_kv_append_slots", "fl_paged_kv_append_rope",
-            "fl_paged_attn_plan_info",
-            "fl_paged_attn_get_work_items", "fl_page_pool_create", "fl_page_pool_destroy",
+            "fl_paged_attn_plan_info", "fl_paged_attn_plan_launch",
+            "fl_paged_attn_refused_launches", "fl_paged_attn_get_work_items", "fl_page_pool_create", "fl_page_pool_destroy",
             "fl_page_pool_alloc", "fl_page_pool_reserve", "fl_page_pool_retain",
             "fl_page_pool_release", "fl_page_pool_refcounts", "fl_page_pool_info",
             "fl_paged_kv_poison", "fl_last_error")
@@ -79,6 +79,9 @@ def load_library(path: Optional[str] = None):
     lib.fl_paged_kv_append_slots.argtypes = [vp, vp, i32, ctypes.POINTER(i32)]
     lib.fl_paged_attn_plan_info.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                             ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    lib.fl_paged_attn_plan_launch.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                              ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.fl_paged_attn_refused_launches.argtypes = [vp, ctypes.POINTER(i32)]
     lib.fl_paged_attn_get_work_items.argtypes = [vp, vp, i32, ctypes.POINTER(i32)]
     lib.fl_page_pool_create.argtypes = [i64, i32, ctypes.POINTER(vp)]
     lib.fl_page_pool_destroy.argtypes = [vp]
@@ -197,6 +200,24 @@ def fl_paged_attn_plan_info(h) -> Tuple[int, int, int, int]:
     return n.value, g.value, s.value, b.value
 
 
+def fl_paged_attn_plan_launch(h) -> Tuple[int, int, int, int]:
+    """(launch class of run, launch class of the one-launch run_append or 0, grid,
+    workgroups with work)."""
+    c, f, g, b = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(load_library().fl_paged_attn_plan_launch(h, ctypes.byref(c), ctypes.byref(f),
+                                                    ctypes.byref(g), ctypes.byref(b)),
+           "fl_paged_attn_plan_launch")
+    return c.value, f.value, g.value, b.value
+
+
+def fl_paged_attn_refused_launches(h) -> int:
+    """Launches refused since the last call (waits for the device)."""
+    n = ctypes.c_int32()
+    _check(load_library().fl_paged_attn_refused_launches(h, ctypes.byref(n)),
+           "fl_paged_attn_refused_launches")
+    return n.value
+
+
 def fl_paged_attn_get_work_items(h) -> np.ndarray:
     """The current plan's work list as an int32 array [items, FL_WORK_ITEM_INTS]."""
     lib = load_library()
@@ -278,6 +299,12 @@ class PagedAttention:
 
     def work_items(self) -> np.ndarray:
         return fl_paged_attn_get_work_items(self.handle)
+
+    def launch(self):
+        return fl_paged_attn_plan_launch(self.handle)
+
+    def refused_launches(self) -> int:
+        return fl_paged_attn_refused_launches(self.handle)
 
 
 # ---------------------------------------------------------------------------------------

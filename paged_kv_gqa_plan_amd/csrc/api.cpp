@@ -1,9 +1,12 @@
 // C interface of the paged GQA attention library: handles, plan staging and launches.
 //
-// A handle owns persistent device buffers for the per-step metadata (work list, merge
-// list, a copy of the page table) that plan() refreshes in place and run() reads, so every
-// run() launches with the same arguments (flashlet README, design bullets: metadata in
-// persistent device buffers, updated in place each step; pinned-to-device metadata path).
+// A handle owns persistent device buffers for the per-step metadata (plan header, work
+// list, merge tickets, per-wave pool rows, append slots) that plan() refreshes in place and
+// the kernels read (flashlet README, design bullets: metadata in persistent device
+// buffers, updated in place each step; pinned-to-device metadata path). A launch depends
+// only on the handle and the plan's launch class (the kernel variant and a grid fixed per
+// variant); the plan header tells the kernels how many workgroups have work and every
+// per-step scalar, so one captured launch serves every later plan of its class.
 // The host side stages each plan into one of two pinned buffers and copies it with one
 // asynchronous transfer on the caller's stream; an event per staging buffer keeps a new
 // plan from overwriting a buffer whose copy is still in flight.
@@ -45,11 +48,12 @@ struct fl_paged_attn {
     int32_t log2_page = 0;
 
     // device buffers
-    char *d_meta = nullptr;      // [segments | workgroup records | merge tickets | step rows |
-                                 //  append slots]
+    char *d_meta = nullptr;      // [segments | plan header + workgroup records | merge tickets |
+                                 //  step rows | append slots | status word]
     float *d_part_o = nullptr;   // [part_rows_cap, head_dim]
     float *d_part_lse = nullptr; // [part_rows_cap]
-    int64_t off_wg_rec = 0, off_tickets = 0, off_steps = 0, off_append = 0, meta_bytes = 0;
+    int64_t off_wg_rec = 0, off_tickets = 0, off_steps = 0, off_append = 0, off_pos = 0,
+            off_status = 0, meta_bytes = 0;
     int32_t waves = 4;
     int32_t part_width = 64;     // floats per partial row: head_dim, or 128 for whole rows
 
@@ -97,6 +101,19 @@ fl_status check_config(const fl_config *c) {
         return set_err(FL_ERR_UNSUPPORTED, "waves_per_group must be 0 or 4");
     if (c->whole_rows < -1 || c->whole_rows > 1)
         return set_err(FL_ERR_INVALID_ARG, "whole_rows must be -1, 0 or 1");
+    if (c->whole_rows == 1) {
+        // asked for on every decode step: refuse a shape that can never take them
+        const char *why = c->dtype == FL_F32 ? "fp32 (whole-row blocks are 16-bit only)"
+                          : c->num_kv_heads < 2 ? "one kv head (its tiles already read whole rows)"
+                          : c->num_kv_heads * c->head_dim != 128 ? "num_kv_heads * head_dim != 128"
+                          : c->num_qo_heads > fl::kBlockRows ? "more than 16 query heads"
+                          : ((uint64_t)c->max_qo_rows * c->num_qo_heads + 16) * c->num_qo_heads >=
+                                    (1ull << 32)
+                              ? "(max_qo_rows * num_qo_heads + 16) * num_qo_heads >= 2^32"
+                              : nullptr;
+        if (why) return set_err(FL_ERR_UNSUPPORTED, std::string("whole_rows = 1 on a shape that "
+                                                               "cannot take whole-row blocks: ") + why);
+    }
     // the kernels divide flattened rows of a request (below max_qo_rows * G + 16) by G
     // with a 32-bit reciprocal multiply, exact while the dividend stays below 2^32 / G
     const uint64_t g = (uint64_t)(c->num_qo_heads / c->num_kv_heads);
@@ -129,12 +146,12 @@ void release(fl_paged_attn *h) {
 // values shared by every query head).
 fl::AttnArgs attn_args(const fl_paged_attn *h, const void *q, const void *k_pool, const void *v_pool,
                        void *out, float *lse) {
-    const Plan &p = h->plan;
     fl::AttnArgs a{};
     a.segs = (const int32_t *)h->d_meta;
     a.wg_rec = (const int32_t *)(h->d_meta + h->off_wg_rec);
     a.step_rows = (const int32_t *)(h->d_meta + h->off_steps);
     a.tickets = (int32_t *)(h->d_meta + h->off_tickets);
+    a.status = (int32_t *)(h->d_meta + h->off_status);
     a.q = q;
     a.k = k_pool;
     a.v = v_pool;
@@ -143,14 +160,52 @@ fl::AttnArgs attn_args(const fl_paged_attn *h, const void *q, const void *k_pool
     a.part_o = h->d_part_o;
     a.part_lse = h->d_part_lse;
     a.num_qo_heads = h->cfg.num_qo_heads;
-    const int32_t group = p.whole_rows ? h->cfg.num_qo_heads : h->group;
-    a.num_kv_heads = p.whole_rows ? 1 : h->cfg.num_kv_heads;
-    a.group = group;
-    a.group_magic = group > 1 ? (uint32_t)(((1ull << 32) + group - 1) / group) : 0u;
-    a.real_group = h->group;
-    a.causal = h->causal;
-    a.scale_log2 = h->scale_log2;
     return a;
+}
+
+// The launch a plan needs: kernel variant and grid. Every auto plan of one kind (decode
+// only, or with prefill rows; whole-row blocks or not) gets the same grid, num_cus x the
+// workgroups per compute unit of its kind; forced-split plans launch one workgroup per
+// piece. The class stamp names the variant and the grid, so two plans of one class launch
+// identically.
+struct LaunchDesc {
+    int grid = 0;
+    int cls = 0;        // run(): attention alone
+    int fcls = 0;       // run_append in one launch; 0 when the plan cannot take it
+    int head_dim = 0;   // kernel's row width (Hkv * D for whole-row blocks)
+    bool early = false; // refill a ring slot before the tile's arithmetic
+    bool wr = false;
+};
+LaunchDesc launch_desc(const fl_paged_attn *h, const Plan &p) {
+    LaunchDesc d;
+    d.wr = p.whole_rows;
+    d.head_dim = p.whole_rows ? h->cfg.num_kv_heads * h->cfg.head_dim : h->cfg.head_dim;
+    // fp32 keeps a register ring (refilled after the arithmetic); at head_dim 128 the
+    // arithmetic hides the LDS reads, so the refill always goes first; at 64 it goes first
+    // on the memory-bound steps (one workgroup per compute unit)
+    d.early = h->cfg.dtype != FL_F32 && (d.head_dim >= 128 || p.groups_per_cu == 1);
+    d.grid = p.forced ? std::max<int32_t>(1, p.num_groups) : h->lim.num_cus * p.groups_per_cu;
+    d.cls = (d.grid << 3) | (d.early << 2) | (d.wr << 1) | 1;
+    if (p.decode_only && h->cfg.dtype != FL_F32 && p.append_ok)
+        d.fcls = (1 << 30) | (d.grid << 3) | (1 << 2) | (d.wr << 1) | 1;
+    return d;
+}
+
+// The plan header for the current plan (kHdrInts int32).
+void fill_header(const fl_paged_attn *h, const LaunchDesc &d, int32_t *hdr) {
+    const Plan &p = h->plan;
+    std::memset(hdr, 0, fl::kHdrInts * 4);
+    const int32_t group = p.whole_rows ? h->cfg.num_qo_heads : h->group;
+    hdr[fl::HDR_NUM_GROUPS] = p.num_groups;
+    hdr[fl::HDR_CLASS] = d.cls;
+    hdr[fl::HDR_FCLASS] = d.fcls;
+    hdr[fl::HDR_CAUSAL] = h->causal;
+    std::memcpy(&hdr[fl::HDR_SCALE_LOG2], &h->scale_log2, 4);
+    hdr[fl::HDR_HKV] = p.whole_rows ? 1 : h->cfg.num_kv_heads;
+    hdr[fl::HDR_GROUP] = group;
+    hdr[fl::HDR_GROUP_MAGIC] = group > 1 ? (int32_t)(uint32_t)(((1ull << 32) + group - 1) / group) : 0;
+    hdr[fl::HDR_REAL_GROUP] = h->group;
+    hdr[fl::HDR_APPEND_ROWS] = p.append_ok ? (int32_t)p.append_rows.size() : -1;
 }
 
 }  // namespace
@@ -218,6 +273,10 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
     h->part_width = L.whole_rows_ok ? 128 : cfg->head_dim;
     const int64_t blocks = fl::row_block_bound(L);
     L.group_cap = std::max<int64_t>((int64_t)num_cus * std::max(L.groups_per_cu, 2), 16384);
+    if (L.group_cap >= (1 << 26)) {  // the launch class stamp holds the grid in 26 bits
+        release(h);
+        return set_err(FL_ERR_UNSUPPORTED, "num_cus x groups_per_cu too large");
+    }
     L.seg_cap = blocks + L.group_cap;
     // steps: every row block may read at most all of the plan's pages; each work item adds
     // at most one ring group of padding per wave
@@ -233,11 +292,13 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
     }
 
     h->off_wg_rec = align_up(L.seg_cap * FL_WORK_ITEM_INTS * 4, 256);
-    h->off_tickets = align_up(h->off_wg_rec + L.group_cap * fl::kRecInts * 4, 256);
+    h->off_tickets = align_up(h->off_wg_rec + (fl::kHdrInts + L.group_cap * fl::kRecInts) * 4, 256);
     h->off_steps = align_up(h->off_tickets + blocks * 4, 256);
     h->off_append = align_up(h->off_steps + std::max<int64_t>(1, L.max_tiles) * 4, 256);
-    // append region: the rows' token slots, then their positions (rows ints each)
-    h->meta_bytes = align_up(h->off_append + std::max<int64_t>(1, cfg->max_qo_rows) * 8, 256);
+    // append regions: the rows' token slots, then their positions (max_qo_rows ints each)
+    h->off_pos = align_up(h->off_append + std::max<int64_t>(1, cfg->max_qo_rows) * 4, 256);
+    h->off_status = align_up(h->off_pos + std::max<int64_t>(1, cfg->max_qo_rows) * 4, 256);
+    h->meta_bytes = h->off_status + 256;
 
     if (!h->host_only) {
         hipError_t e;
@@ -248,9 +309,11 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
             release(h);
             return hip_err(e, "hipMalloc (handle buffers)");
         }
-        // merge tickets start at zero once; runs keep them there
+        // merge tickets start at zero once; runs keep them there. The status word counts
+        // refused launches.
         if ((e = hipMemset(h->d_meta + h->off_tickets, 0, (size_t)(h->off_steps - h->off_tickets))) !=
                 hipSuccess ||
+            (e = hipMemset(h->d_meta + h->off_status, 0, 256)) != hipSuccess ||
             (e = hipStreamSynchronize(nullptr)) != hipSuccess) {
             release(h);
             return hip_err(e, "hipMemset (merge tickets)");
@@ -294,7 +357,7 @@ fl_status fl_paged_attn_plan(fl_handle h, int32_t batch, const int32_t *qo_indpt
     h->scale_log2 = (float)(scale * 1.4426950408889634);
     h->causal = causal ? 1 : 0;
 
-    if (!h->host_only && batch > 0) {
+    if (!h->host_only) {
         hipError_t e = hipSetDevice(h->device);
         if (e != hipSuccess) return hip_err(e, "hipSetDevice");
         const int slot = h->cur;
@@ -311,17 +374,20 @@ fl_status fl_paged_attn_plan(fl_handle h, int32_t batch, const int32_t *qo_indpt
         // create and every run leaves them at zero (the piece that merges a row block
         // resets its ticket).
         std::memcpy(st_buf, p.segs.data(), p.segs.size() * 4);
-        std::memcpy(st_buf + h->off_wg_rec, p.wg_rec.data(), p.wg_rec.size() * 4);
+        fill_header(h, launch_desc(h, p), (int32_t *)(st_buf + h->off_wg_rec));
+        std::memcpy(st_buf + h->off_wg_rec + fl::kHdrInts * 4, p.wg_rec.data(), p.wg_rec.size() * 4);
         std::memcpy(st_buf + h->off_steps, p.step_rows.data(), p.step_rows.size() * 4);
-        const int64_t append_bytes = p.append_ok ? (int64_t)p.append_rows.size() * 8 : 0;
+        // append slots and positions
+        const int64_t append_bytes = p.append_ok ? (int64_t)p.append_rows.size() * 4 : 0;
+        const int64_t off_pos = h->off_pos;
         if (append_bytes) {
-            std::memcpy(st_buf + h->off_append, p.append_rows.data(), append_bytes / 2);
-            std::memcpy(st_buf + h->off_append + append_bytes / 2, p.append_pos.data(), append_bytes / 2);
+            std::memcpy(st_buf + h->off_append, p.append_rows.data(), append_bytes);
+            std::memcpy(st_buf + off_pos, p.append_pos.data(), append_bytes);
         }
         fl::StageCopy sc{h->d_stage[slot], h->d_meta,
-                         {0, h->off_wg_rec, h->off_steps, h->off_append},
-                         {(int64_t)p.segs.size() * 4, (int64_t)p.wg_rec.size() * 4,
-                          (int64_t)p.step_rows.size() * 4, append_bytes}};
+                         {0, h->off_wg_rec, h->off_steps, h->off_append, off_pos},
+                         {(int64_t)p.segs.size() * 4, (int64_t)(fl::kHdrInts + p.wg_rec.size()) * 4,
+                          (int64_t)p.step_rows.size() * 4, append_bytes, append_bytes}};
         hipStream_t s = (hipStream_t)stream;
         if ((e = (hipError_t)fl::launch_stage_copy(sc, s)) != hipSuccess)
             return hip_err(e, "plan metadata copy");
@@ -340,17 +406,17 @@ fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, cons
     if (h->host_only) return set_err(FL_ERR_UNSUPPORTED, "run() on a host-only handle");
     if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "run() before a successful plan()");
     const Plan &p = h->plan;
-    if (p.num_groups == 0) return FL_OK;
     if (!q || !k_pool || !v_pool || !out)
         return set_err(FL_ERR_INVALID_ARG, "q, k_pool, v_pool and out must not be NULL");
     if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)out) & 15)
         return set_err(FL_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
 
-    const fl::AttnArgs a = attn_args(h, q, k_pool, v_pool, out, lse);
-    const int head_dim = p.whole_rows ? h->cfg.num_kv_heads * h->cfg.head_dim : h->cfg.head_dim;
-    // two workgroups per compute unit are chosen for steps bound by the per-tile arithmetic
-    const int e = fl::launch_attention(h->cfg.dtype, head_dim, h->waves, p.groups_per_cu == 1,
-                                       p.whole_rows, false, p.num_groups, a, stream);
+    // an empty plan launches too (every workgroup idle), so that a captured launch exists
+    fl::AttnArgs a = attn_args(h, q, k_pool, v_pool, out, lse);
+    const LaunchDesc d = launch_desc(h, p);
+    a.launch_class = d.cls;
+    const int e = fl::launch_attention(h->cfg.dtype, d.head_dim, h->waves, d.early, d.wr, false,
+                                       d.grid, a, stream);
     if (e != (int)hipSuccess) return hip_err((hipError_t)e, "attention launch");
     return FL_OK;
 }
@@ -363,8 +429,8 @@ fl_status fl_paged_attn_run_append(fl_handle h, const void *q, const void *k_new
     if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "run_append before a successful plan()");
     const Plan &p = h->plan;
     if (!p.append_ok) return set_err(FL_ERR_INVALID_ARG, "the plan has no append slots: " + p.append_err);
-    if (p.num_groups == 0) return FL_OK;
-    if (!p.decode_only || h->cfg.dtype == FL_F32) {
+    const LaunchDesc d = launch_desc(h, p);
+    if (!d.fcls) {
         // a prefill chunk's new keys are read by many workgroups: append first, then attend
         fl_status st = fl_paged_kv_append(h, k_new, v_new, k_pool, v_pool, stream);
         if (st != FL_OK) return st;
@@ -379,9 +445,9 @@ fl_status fl_paged_attn_run_append(fl_handle h, const void *q, const void *k_new
     a.k_new = k_new;
     a.v_new = v_new;
     a.append_rows = (const int32_t *)(h->d_meta + h->off_append);
-    const int head_dim = p.whole_rows ? h->cfg.num_kv_heads * h->cfg.head_dim : h->cfg.head_dim;
-    const int e = fl::launch_attention(h->cfg.dtype, head_dim, h->waves, true, p.whole_rows, true,
-                                       p.num_groups, a, stream);
+    a.launch_class = d.fcls;
+    const int e = fl::launch_attention(h->cfg.dtype, d.head_dim, h->waves, true, d.wr, true, d.grid, a,
+                                       stream);
     if (e != (int)hipSuccess) return hip_err((hipError_t)e, "attention + append launch");
     return FL_OK;
 }
@@ -394,18 +460,19 @@ fl_status fl_paged_kv_append(fl_handle h, const void *k_new, const void *v_new, 
     if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "append before a successful plan()");
     const Plan &p = h->plan;
     if (!p.append_ok) return set_err(FL_ERR_INVALID_ARG, "the plan has no append slots: " + p.append_err);
-    const int64_t rows = (int64_t)p.append_rows.size();
-    if (rows == 0) return FL_OK;
     if (!k_new || !v_new || !k_pool || !v_pool)
         return set_err(FL_ERR_INVALID_ARG, "k_new, v_new, k_pool and v_pool must not be NULL");
     if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_pool | (uintptr_t)v_pool) & 15)
         return set_err(FL_ERR_INVALID_ARG, "k_new, v_new, k_pool and v_pool must be 16-byte aligned");
     const int64_t elem = h->cfg.dtype == FL_F32 ? 4 : 2;
     const int64_t row_bytes = (int64_t)h->cfg.num_kv_heads * h->cfg.head_dim * elem;
-    if (rows * (row_bytes / 16) >= INT32_MAX)
-        return set_err(FL_ERR_UNSUPPORTED, "rows x 16-byte chunks per token row must stay below 2^31");
-    fl::AppendArgs a{(const int32_t *)(h->d_meta + h->off_append), k_new, v_new, k_pool, v_pool,
-                     (int32_t)rows, (int32_t)row_bytes};
+    const int64_t max_rows = std::max<int64_t>(1, h->cfg.max_qo_rows);
+    if (max_rows * (row_bytes / 16) >= INT32_MAX)
+        return set_err(FL_ERR_UNSUPPORTED, "max_qo_rows x 16-byte chunks per token row must stay below 2^31");
+    // the grid covers max_qo_rows; the kernel reads the plan's row count from its header
+    fl::AppendArgs a{(const int32_t *)(h->d_meta + h->off_wg_rec), (int32_t *)(h->d_meta + h->off_status),
+                     (const int32_t *)(h->d_meta + h->off_append), k_new, v_new, k_pool, v_pool,
+                     (int32_t)max_rows, (int32_t)row_bytes};
     const int le = fl::launch_kv_append(a, stream);
     if (le != (int)hipSuccess) return hip_err((hipError_t)le, "kv append launch");
     return FL_OK;
@@ -423,8 +490,6 @@ fl_status fl_paged_kv_append_rope(fl_handle h, void *q, const void *k_new, const
     if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "append before a successful plan()");
     const Plan &p = h->plan;
     if (!p.append_ok) return set_err(FL_ERR_INVALID_ARG, "the plan has no append slots: " + p.append_err);
-    const int64_t rows = (int64_t)p.append_rows.size();
-    if (rows == 0) return FL_OK;
     if (!k_new || !v_new || !k_pool || !v_pool)
         return set_err(FL_ERR_INVALID_ARG, "k_new, v_new, k_pool and v_pool must not be NULL");
     const int64_t elem = h->cfg.dtype == FL_F32 ? 4 : 2;
@@ -432,14 +497,16 @@ fl_status fl_paged_kv_append_rope(fl_handle h, void *q, const void *k_new, const
         (uintptr_t)(elem - 1))
         return set_err(FL_ERR_INVALID_ARG, "q, k_new, v_new, k_pool and v_pool must be aligned to the element size");
     fl::RopeArgs a{};
+    a.hdr = (const int32_t *)(h->d_meta + h->off_wg_rec);
+    a.status = (int32_t *)(h->d_meta + h->off_status);
     a.dst_rows = (const int32_t *)(h->d_meta + h->off_append);
-    a.pos = a.dst_rows + rows;
+    a.pos = (const int32_t *)(h->d_meta + h->off_pos);
     a.k_new = k_new;
     a.v_new = v_new;
     a.k_pool = k_pool;
     a.v_pool = v_pool;
     a.q = q;
-    a.rows = (int32_t)rows;
+    a.max_rows = std::max<int32_t>(1, h->cfg.max_qo_rows);
     a.num_kv_heads = h->cfg.num_kv_heads;
     a.num_qo_heads = h->cfg.num_qo_heads;
     a.head_dim = h->cfg.head_dim;
@@ -477,6 +544,35 @@ fl_status fl_paged_attn_plan_info(fl_handle h, int32_t *num_work_items, int32_t 
     if (max_splits) *max_splits = h->plan.max_splits;
     const int64_t width = h->plan.whole_rows ? h->part_width : h->cfg.head_dim;
     if (workspace_bytes) *workspace_bytes = h->plan.part_rows * (width + 1) * 4;
+    return FL_OK;
+}
+
+fl_status fl_paged_attn_plan_launch(fl_handle h, int32_t *launch_class, int32_t *fused_class,
+                                    int32_t *grid, int32_t *busy_groups) {
+    g_last_error.clear();
+    if (!h) return set_err(FL_ERR_INVALID_ARG, "handle is NULL");
+    if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "no plan");
+    const LaunchDesc d = launch_desc(h, h->plan);
+    if (launch_class) *launch_class = d.cls;
+    if (fused_class) *fused_class = d.fcls;
+    if (grid) *grid = d.grid;
+    if (busy_groups) *busy_groups = h->plan.num_groups;
+    return FL_OK;
+}
+
+fl_status fl_paged_attn_refused_launches(fl_handle h, int32_t *count) {
+    g_last_error.clear();
+    if (!h || !count) return set_err(FL_ERR_INVALID_ARG, "handle or count is NULL");
+    *count = 0;
+    if (h->host_only) return FL_OK;
+    hipError_t e;
+    if ((e = hipSetDevice(h->device)) != hipSuccess) return hip_err(e, "hipSetDevice");
+    if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_err(e, "hipDeviceSynchronize");
+    if ((e = hipMemcpy(count, h->d_meta + h->off_status, 4, hipMemcpyDeviceToHost)) != hipSuccess)
+        return hip_err(e, "hipMemcpy (status)");
+    if ((e = hipMemset(h->d_meta + h->off_status, 0, 4)) != hipSuccess ||
+        (e = hipDeviceSynchronize()) != hipSuccess)
+        return hip_err(e, "hipMemset (status)");
     return FL_OK;
 }
 

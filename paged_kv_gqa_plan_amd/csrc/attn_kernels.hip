@@ -1048,9 +1048,14 @@ __device__ __forceinline__ void write_new_rows(const lds_char *slot, const AttnA
     }
 }
 
+// Launch-shape independence: the grid is fixed per launch class, and everything a plan
+// changes (how many workgroups have work, causal flag, scale, head grouping) comes from the
+// plan header in front of the records, read in the same batch of scalar loads as the
+// workgroup's record. A launch whose class stamp is not the plan's touches nothing.
 template <class T, int DT, int D, int NW, bool EARLY, bool WR, bool FUSE>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, const void *k_pool,
-                                                      const void *v_pool, int hkv, const AttnArgs a) {
+                                                      const void *v_pool, int launch_class,
+                                                      const AttnArgs a_in) {
     static_assert(NW == 4 && NW <= kMaxWaves, "four waves per workgroup");
     static_assert(REC_HEAD + FL_WORK_ITEM_INTS <= REC_SEG_BEGIN &&
                   REC_ROWS + kMaxWaves * kRingDepth <= kRecInts, "record layout");
@@ -1076,13 +1081,35 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     const int col = lane & 15;
     const int grp = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    // The workgroup record gives the share, the first segment and every wave's first pool
-    // rows: one batch of scalar loads, issued before anything else.
-    const int32_t *rec = wg_rec + (size_t)blockIdx.x * kRecInts;
+    // The plan header and the workgroup record (the share, the first segment and every
+    // wave's first pool rows): one batch of scalar loads, issued before anything else.
+    // Every launch's grid lies within the record region, whatever the plan.
+    const int32_t *rec = wg_rec + kHdrInts + (size_t)blockIdx.x * kRecInts;
+    int hv[HDR_USED];
+#pragma unroll
+    for (int i = 0; i < HDR_USED; ++i) hv[i] = wg_rec[i];
     int rv[REC_ROWS + kMaxWaves * PF];
 #pragma unroll
     for (int i = 0; i < REC_ROWS + kMaxWaves * PF; ++i) rv[i] = rec[i];
+    // the arguments the first loads need, read in the same batch (consumed here, so they
+    // are not sunk below the branch into a second round trip)
+    AttnArgs a = a_in;
+    asm volatile("" ::"s"(a.segs), "s"(a.step_rows), "s"(a.q), "s"(a.num_qo_heads));
     __builtin_amdgcn_sched_barrier(0);
+    if (hv[FUSE ? HDR_FCLASS : HDR_CLASS] != launch_class) {
+        // launched for a plan of another class (a stale captured graph): refuse
+        if (blockIdx.x == 0 && threadIdx.x == 0)
+            __hip_atomic_fetch_add(a_in.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    if ((int)blockIdx.x >= hv[HDR_NUM_GROUPS]) return;  // idle: this plan needs fewer workgroups
+    a.causal = hv[HDR_CAUSAL];
+    a.scale_log2 = __int_as_float(hv[HDR_SCALE_LOG2]);
+    a.num_kv_heads = hv[HDR_HKV];
+    a.group = hv[HDR_GROUP];
+    a.group_magic = (uint32_t)hv[HDR_GROUP_MAGIC];
+    a.real_group = hv[HDR_REAL_GROUP];
+    const int hkv = a.num_kv_heads;
     const int seg_b = rv[REC_SEG_BEGIN], seg_e = rv[REC_SEG_END];
     const int pos0 = rv[REC_POS];
     const int nsteps = rv[REC_STEPS];  // steps per wave (a positive multiple of PF)
@@ -1305,7 +1332,7 @@ template <int DT, int D, int NW, bool EARLY, bool WR = false, bool FUSE = false>
 hipError_t launch_t(int n, const AttnArgs &a, hipStream_t s) {  // n: workgroups
     using T = typename TileFor<DT, D>::type;
     hipLaunchKernelGGL((attn_kernel<T, DT, D, NW, EARLY, WR, FUSE>), dim3(n), dim3(NW * 64), 0, s, a.wg_rec,
-                       a.k, a.v, a.num_kv_heads, a);
+                       a.k, a.v, a.launch_class, a);
     return hipGetLastError();
 }
 

@@ -87,6 +87,28 @@ enum {
     REC_ROWS = 24,   // kMaxWaves * kRingDepth entries
 };
 constexpr int kRecInts = (REC_ROWS + kMaxWaves * kRingDepth + 31) / 32 * 32;
+// Plan header (int32): one 128-byte line in front of the workgroup records, written by
+// every plan. It carries everything about the step that a launch needs besides the
+// buffers, so one launch (grid, kernel, arguments) serves every plan of its launch class
+// and a captured HIP graph replays correctly after any later plan of that class.
+// Workgroups at or past HDR_NUM_GROUPS exit at once; a launch whose class stamp differs
+// from the plan's (a graph captured on a plan of another class) touches nothing, and its
+// first workgroup counts the refusal in the handle's status word.
+enum {
+    HDR_NUM_GROUPS = 0,  // workgroups with work (the rest of the grid is idle)
+    HDR_CLASS = 1,       // launch class of run() (attention alone)
+    HDR_FCLASS = 2,      // launch class of the one-launch run_append (0: none)
+    HDR_CAUSAL = 3,
+    HDR_SCALE_LOG2 = 4,  // float bits: sm_scale * log2(e)
+    HDR_HKV = 5,         // kv heads as the kernel sees them (1 for whole-row blocks)
+    HDR_GROUP = 6,       // query heads per (virtual) kv head
+    HDR_GROUP_MAGIC = 7, // ceil(2^32 / group), 0 when group == 1
+    HDR_REAL_GROUP = 8,  // query heads per real kv head
+    HDR_APPEND_ROWS = 9, // query rows the append kernels write; -1: the plan has no valid
+                         // append slots (the kernels refuse and count it)
+    HDR_USED = 10,
+    kHdrInts = 32,
+};
 
 struct PlanLimits {
     int32_t num_qo_heads, num_kv_heads, head_dim, page_size;
@@ -120,7 +142,8 @@ struct PlanInput {
 
 struct Plan {
     std::vector<int32_t> segs;      // FL_WORK_ITEM_INTS per segment, grouped by workgroup
-    std::vector<int32_t> wg_rec;    // kRecInts per workgroup
+    std::vector<int32_t> wg_rec;    // kRecInts per workgroup (the plan header in front of
+                                    // them is written by the C-ABI layer)
     std::vector<int32_t> step_rows; // per workgroup, per wave, per step: pool row
                                     // (page * P + slot) * Hkv + kv_head of the step's tile's
                                     // first key (padding steps repeat a real tile's row)
@@ -131,6 +154,7 @@ struct Plan {
     bool whole_rows = false;        // blocks hold every query head of a request and read whole
                                     // token rows (one virtual kv head of Hkv * D values)
     bool decode_only = false;       // every request has at most one query row
+    bool forced = false;            // num_splits > 0: one workgroup per piece, grid = num_groups
     int32_t max_splits = 0;
     int64_t part_rows = 0;
     std::vector<int32_t> append_rows;  // per query row: token row page * P + slot of the
@@ -152,9 +176,10 @@ int64_t row_block_bound(const PlanLimits &lim);
 // ---------------------------------------------------------------------------------------
 struct AttnArgs {
     const int32_t *segs;       // FL_WORK_ITEM_INTS per segment
-    const int32_t *wg_rec;     // kRecInts per workgroup
+    const int32_t *wg_rec;     // plan header (kHdrInts), then kRecInts per workgroup
     const int32_t *step_rows;  // per workgroup, wave and step
     int32_t *tickets;          // one per merged row block, zero between runs
+    int32_t *status;           // refused launches are counted here
     const void *q;
     const void *k;
     const void *v;
@@ -163,6 +188,10 @@ struct AttnArgs {
     float *part_o;             // [part_rows, head_dim]
     float *part_lse;           // [part_rows], log2 domain
     int32_t num_qo_heads;
+    int32_t launch_class;      // must equal the plan header's class (HDR_CLASS, or
+                               // HDR_FCLASS for the fused append) or the launch is refused
+    // Per-plan values: the host leaves them zero; the kernel fills them from the plan header
+    // (so a captured launch sees the plan current at replay time).
     int32_t num_kv_heads;
     int32_t group;
     uint32_t group_magic;      // ceil(2^32 / group) (unused when group == 1)
@@ -183,18 +212,22 @@ struct AttnArgs {
 // whole_rows: head_dim is the virtual row width Hkv * D (128) of whole-row blocks.
 // fuse_append: the launch also appends the new K/V rows (a.k_new, a.v_new; decode-only
 // plans, 16-bit types): it writes them to the pools and uses them for the newest key.
+// grid: workgroups of the launch (the launch class's fixed grid).
 int launch_attention(int dtype, int head_dim, int waves, bool early_refill, bool whole_rows,
-                     bool fuse_append, int num_groups, const AttnArgs &a, void *stream);
+                     bool fuse_append, int grid, const AttnArgs &a, void *stream);
 
 // KV append: copy row r of k_new / v_new (row_bytes each, a multiple of 16) to token row
-// dst_rows[r] of k_pool / v_pool (kv_append.hip).
+// dst_rows[r] of k_pool / v_pool (kv_append.hip), for r below the plan header's
+// HDR_APPEND_ROWS. The grid is sized for max_rows rows, so one launch serves every plan.
 struct AppendArgs {
+    const int32_t *hdr;        // plan header
+    int32_t *status;           // refused launches are counted here
     const int32_t *dst_rows;
     const void *k_new;
     const void *v_new;
     void *k_pool;
     void *v_pool;
-    int32_t rows;
+    int32_t max_rows;
     int32_t row_bytes;
 };
 int launch_kv_append(const AppendArgs &a, void *stream);
@@ -205,6 +238,8 @@ int launch_kv_append(const AppendArgs &a, void *stream);
 // (i < head_dim / 2) are the pair frequencies, already rounded to fp32 on the host.
 constexpr int kMaxRopePairs = 64;  // head_dim <= 128
 struct RopeArgs {
+    const int32_t *hdr;        // plan header: HDR_APPEND_ROWS rows (-1: refused)
+    int32_t *status;
     const int32_t *dst_rows;
     const int32_t *pos;
     const void *k_new;
@@ -212,7 +247,7 @@ struct RopeArgs {
     void *k_pool;
     void *v_pool;
     void *q;
-    int32_t rows, num_kv_heads, num_qo_heads, head_dim, dtype;
+    int32_t max_rows, num_kv_heads, num_qo_heads, head_dim, dtype;
     float inv_freq[kMaxRopePairs];
 };
 int launch_kv_append_rope(const RopeArgs &a, void *stream);
@@ -231,7 +266,7 @@ int launch_kv_poison(const PoisonArgs &a, void *stream);
 
 // Copy byte ranges [off, off + bytes) from pinned host memory to the same offsets of a
 // device buffer with one kernel (offsets 16-byte aligned, sizes multiples of 4).
-constexpr int kStageParts = 4;
+constexpr int kStageParts = 5;
 struct StageCopy {
     const char *src;   // pinned host memory, device-accessible
     char *dst;         // device memory

@@ -7,7 +7,8 @@
 // contiguous, so the copy of one row is row_bytes contiguous bytes on both sides (a
 // multiple of 128). Consecutive lanes take consecutive 16-byte chunks of a row, then of the
 // next row, so every wavefront reads and writes whole 128-byte lines. The copy is the same
-// for every element type: it moves bytes.
+// for every element type: it moves bytes. The grid is sized for the handle's largest plan
+// and the row count comes from the plan header, so one launch serves every plan.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,9 +25,16 @@ constexpr int kThreads = 256;
 constexpr int64_t kMaxBlocks = 4096;  // grid-stride beyond this
 
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(
-    const int32_t *__restrict__ dst_rows, const u32x4 *__restrict__ k_new,
-    const u32x4 *__restrict__ v_new, u32x4 *__restrict__ k_pool, u32x4 *__restrict__ v_pool,
-    uint32_t total_chunks, uint32_t row_chunks) {
+    const int32_t *__restrict__ hdr, int32_t *status, const int32_t *__restrict__ dst_rows,
+    const u32x4 *__restrict__ k_new, const u32x4 *__restrict__ v_new, u32x4 *__restrict__ k_pool,
+    u32x4 *__restrict__ v_pool, uint32_t row_chunks) {
+    const int rows = hdr[HDR_APPEND_ROWS];
+    if (rows < 0) {  // the plan has no valid append slots (only a replayed launch gets here)
+        if (blockIdx.x == 0 && threadIdx.x == 0)
+            __hip_atomic_fetch_add(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const uint32_t total_chunks = (uint32_t)rows * row_chunks;  // below 2^31 (checked on the host)
     const uint32_t stride = gridDim.x * kThreads;
     for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < total_chunks; i += stride) {
         const uint32_t row = i / row_chunks;
@@ -42,15 +50,14 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(
 }  // namespace
 
 int launch_kv_append(const AppendArgs &a, void *stream) {
-    if (a.rows <= 0) return (int)hipSuccess;
-    if (a.row_bytes <= 0 || a.row_bytes % 16) return (int)hipErrorInvalidValue;
+    if (a.max_rows <= 0 || a.row_bytes <= 0 || a.row_bytes % 16) return (int)hipErrorInvalidValue;
     const uint32_t row_chunks = (uint32_t)(a.row_bytes / 16);
-    const int64_t total = (int64_t)a.rows * row_chunks;
+    const int64_t total = (int64_t)a.max_rows * row_chunks;
     if (total >= INT32_MAX) return (int)hipErrorInvalidValue;  // 32-bit chunk indices
     const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, kMaxBlocks);
     hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream,
-                       a.dst_rows, (const u32x4 *)a.k_new, (const u32x4 *)a.v_new, (u32x4 *)a.k_pool,
-                       (u32x4 *)a.v_pool, (uint32_t)total, row_chunks);
+                       a.hdr, a.status, a.dst_rows, (const u32x4 *)a.k_new, (const u32x4 *)a.v_new,
+                       (u32x4 *)a.k_pool, (u32x4 *)a.v_pool, row_chunks);
     return (int)hipGetLastError();
 }
 

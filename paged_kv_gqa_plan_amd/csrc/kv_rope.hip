@@ -11,8 +11,9 @@
 // turns by pos * f_i, with f_i = theta^(-2i/D) supplied by the host already rounded to
 // fp32; the angle is the fp32 product of (float)pos and f_i, its sine and cosine come from
 // the device library's sincosf, and the rotated pair is rounded once to the storage type.
-// One workgroup per row: the work per row is a few hundred pairs, memory-light; the launch
-// cost dominates, as for the plain append.
+// One workgroup per row (a grid sized for the handle's largest plan, striding over the
+// plan header's row count): the work per row is a few hundred pairs, memory-light; the
+// launch cost dominates, as for the plain append.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -56,27 +57,37 @@ __device__ __forceinline__ void rotate_heads(const S *src, S *dst, int heads, fl
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void kv_rope_kernel(const RopeArgs a) {
     using S = typename Store<DT>::T;
-    const int r = blockIdx.x;
+    const int rows = a.hdr[HDR_APPEND_ROWS];
+    if (rows < 0) {  // the plan has no valid append slots (only a replayed launch gets here)
+        if (blockIdx.x == 0 && threadIdx.x == 0)
+            __hip_atomic_fetch_add(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     const int hkv = a.num_kv_heads;
-    const float fpos = (float)a.pos[r];
-    const int64_t src = (int64_t)r * hkv * D;
-    const int64_t dst = (int64_t)a.dst_rows[r] * hkv * D;
-    rotate_heads<S, D>((const S *)a.k_new + src, (S *)a.k_pool + dst, hkv, fpos, a.inv_freq);
-    const S *vn = (const S *)a.v_new + src;
-    S *vp = (S *)a.v_pool + dst;
-    for (int j = threadIdx.x; j < hkv * D; j += kThreads) vp[j] = vn[j];
-    if (a.q) {
-        S *q = (S *)a.q + (int64_t)r * a.num_qo_heads * D;
-        rotate_heads<S, D>(q, q, a.num_qo_heads, fpos, a.inv_freq);
+    for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+        const float fpos = (float)a.pos[r];
+        const int64_t src = (int64_t)r * hkv * D;
+        const int64_t dst = (int64_t)a.dst_rows[r] * hkv * D;
+        rotate_heads<S, D>((const S *)a.k_new + src, (S *)a.k_pool + dst, hkv, fpos, a.inv_freq);
+        const S *vn = (const S *)a.v_new + src;
+        S *vp = (S *)a.v_pool + dst;
+        for (int j = threadIdx.x; j < hkv * D; j += kThreads) vp[j] = vn[j];
+        if (a.q) {
+            S *q = (S *)a.q + (int64_t)r * a.num_qo_heads * D;
+            rotate_heads<S, D>(q, q, a.num_qo_heads, fpos, a.inv_freq);
+        }
     }
 }
 
+constexpr int kMaxRopeBlocks = 1024;  // rows beyond this are strided
+
 template <int DT>
 hipError_t launch_d(const RopeArgs &a, hipStream_t s) {
+    const unsigned grid = (unsigned)(a.max_rows < kMaxRopeBlocks ? a.max_rows : kMaxRopeBlocks);
     if (a.head_dim == 64)
-        hipLaunchKernelGGL((kv_rope_kernel<DT, 64>), dim3(a.rows), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((kv_rope_kernel<DT, 64>), dim3(grid), dim3(kThreads), 0, s, a);
     else if (a.head_dim == 128)
-        hipLaunchKernelGGL((kv_rope_kernel<DT, 128>), dim3(a.rows), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((kv_rope_kernel<DT, 128>), dim3(grid), dim3(kThreads), 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -85,7 +96,7 @@ hipError_t launch_d(const RopeArgs &a, hipStream_t s) {
 }  // namespace
 
 int launch_kv_append_rope(const RopeArgs &a, void *stream) {
-    if (a.rows <= 0) return (int)hipSuccess;
+    if (a.max_rows <= 0) return (int)hipErrorInvalidValue;
     hipStream_t s = (hipStream_t)stream;
     switch (a.dtype) {
     case FL_BF16: return (int)launch_d<FL_BF16>(a, s);

@@ -68,8 +68,13 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         return fail(err, FL_ERR_CAPACITY, "batch %lld exceeds max_batch %lld", B, lim.max_batch);
     if (in.num_splits < 0)
         return fail(err, FL_ERR_INVALID_ARG, "num_splits %lld < 0", in.num_splits);
+    out.forced = in.num_splits > 0;
     if (B == 0) {
+        // nothing to do; the plan still has the launch shape of a decode step
         out.append_ok = true;  // nothing to append
+        out.decode_only = true;
+        out.whole_rows = lim.whole_rows_ok && lim.whole_rows_always;
+        out.groups_per_cu = lim.groups_per_cu > 0 ? lim.groups_per_cu : 1;
         return FL_OK;
     }
     if (!in.kv_indptr || !in.last_page_len)
@@ -185,6 +190,16 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
                      (lim.whole_rows_always || decode_rows >= lim.num_cus);
     const int32_t Hkv = out.whole_rows ? 1 : Hkv_real;
     const int32_t G = out.whole_rows ? lim.num_qo_heads : lim.num_qo_heads / Hkv_real;
+    // Workgroups per compute unit: a step with prefill rows is bound by the per-tile
+    // arithmetic, which two workgroups per unit overlap better, where their LDS fits
+    // (head_dim 64, 16-bit: measured 23 vs 33 us on the ragged mixed step); decode-only
+    // steps are bound by memory latency and do best with one (saturated decode 7.1 vs
+    // 10.5 us, the extra split's merge dominates). The choice depends only on the step's
+    // kind, so every step of one kind launches the same grid.
+    const bool prefill = !decode_only;
+    const int gpc = lim.groups_per_cu > 0 ? lim.groups_per_cu
+                                          : (prefill && lim.head_dim <= 64 && lim.dtype != FL_F32 ? 2 : 1);
+    out.groups_per_cu = gpc;
 
     // ---- row blocks -------------------------------------------------------------------
     // per kv head: the share of its row slice in odd 256-byte halves, in percent; 50 (no
@@ -245,19 +260,8 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         // share is cut at a multiple of a step group, so only a block's last piece carries
         // padding. The smallest per-share budget that needs at most G shares is found by
         // bisection.
-        // Workgroups per compute unit: a step with prefill rows is bound by the per-tile
-        // arithmetic, which two workgroups per unit overlap better, where their LDS fits
-        // (head_dim 64, 16-bit: measured 23 vs 33 us on the ragged mixed step); decode-only
-        // steps are bound by memory latency and do best with one (saturated decode 7.1 vs
-        // 10.5 us, the extra split's merge dominates).
-        bool prefill = false;
-        for (int32_t r = 0; r < B && !prefill; ++r)
-            prefill = in.qo_indptr && in.qo_indptr[r + 1] - in.qo_indptr[r] > 1;
-        int gpc = lim.groups_per_cu;
-        if (gpc <= 0) gpc = prefill && lim.head_dim <= 64 && lim.dtype != FL_F32 ? 2 : 1;
         const int64_t kFoldCost = prefill ? kFoldCostMixed : out.whole_rows ? kFoldCostWhole : kFoldCostDecode;
         const int64_t kCutCost = prefill ? kCutCostMixed : out.whole_rows ? kCutCostWhole : kCutCostDecode;
-        out.groups_per_cu = gpc;
         const int64_t want = (int64_t)lim.num_cus * gpc;
         const int64_t G_max = std::min(std::max<int64_t>(1, std::min(want, ceil_div(T, lim.min_group_tiles))), T);
         const int64_t U = (int64_t)lim.waves * kRingDepth;

@@ -138,10 +138,13 @@ def test_random_configurations(seed):
     _check(b, num_splits=splits, what=f"random-{seed}")
 
 
-def test_fp32_long_context_skew_reduced():
-    b = W.make_batch(W.long_context_lengths(0, long_len=8192), num_qo_heads=12, num_kv_heads=2,
-                     head_dim=128, page_size=256, dtype="f32", seed=0)
-    _check(b, what="f32-long-context-skew-8192")
+def test_fp32_long_context_skew_full():
+    """The long-context skew batch at full size in fp32 (8 x 32768 + 56 x 512 cached tokens,
+    12/2 heads, d 128, 256-slot pages): the most pieces per row block and the deepest
+    log-sum-exp merge, against the 1e-5 bar."""
+    b = W.long_context_skew(dtype="f32")
+    d, _ = _check(b, what="f32-long-context-skew")
+    assert d.h.info()[2] >= 8  # the long histories are cut into many pieces and merged
 
 
 def test_fp32_saturated_decode():
@@ -196,13 +199,12 @@ def _plant(b, r, t, rows=None):
     b.q[sel, :, 0] = W.to_storage(np.array([32.0], np.float32), b.dtype)[0]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+# whole-row blocks are 16-bit only (create refuses whole_rows = 1 for fp32)
+@pytest.mark.parametrize("dtype,whole_rows", [("bf16", 1), ("bf16", -1), ("f16", 1), ("f16", -1),
+                                              ("f32", -1)])
 @pytest.mark.parametrize("P", [16, 64, 256])
 @pytest.mark.parametrize("splits", [0, 1, 4])
-@pytest.mark.parametrize("whole_rows", [1, -1])
-def test_needles_bit_exact(dtype, P, splits, whole_rows):
-    if dtype == "f32" and whole_rows == 1:
-        pytest.skip("whole-row blocks are 16-bit only; fp32 runs one block per kv head")
+def test_needles_bit_exact(dtype, whole_rows, P, splits):
     kv = [1, P, P + 1, 3 * P - 1, 300, 1000]
     spots = [0, P - 1, P, 3 * P - 2, 299, 517]
     b = _needle_batch(kv, None, P, dtype)

@@ -249,18 +249,35 @@ def test_whole_rows_only_where_they_apply():
     r = W.make_batch([40, 300, 17], [5, 1, 1], num_qo_heads=14, num_kv_heads=2, head_dim=64,
                      page_size=16)
     assert (plan_batch(host_handle(whole_rows=1), r)[:, idx["kv_head"]] >= 0).all()  # prefill rows
+    # the default and -1 plan such shapes per kv head
     for kw, shape in ((dict(dtype="f32"), dict(dtype="f32")),                    # fp32
                       (dict(D=128), dict(head_dim=128)),                         # 2 x 128 wide
                       (dict(Hq=32), dict(num_qo_heads=32))):                     # 32 heads
         bb = W.make_batch([40, 300, 17], **{**dict(num_qo_heads=14, num_kv_heads=2, head_dim=64,
                                                    page_size=16), **shape})
-        it = plan_batch(host_handle(whole_rows=1, **kw), bb)
-        assert (it[:, idx["kv_head"]] >= 0).all(), kw
-        check_coverage(it, bb)
-    # one kv head of 128 already reads whole rows: no change there either
+        for wr in (0, -1):
+            it = plan_batch(host_handle(whole_rows=wr, num_cus=2, **kw), bb)
+            assert (it[:, idx["kv_head"]] >= 0).all(), kw
+            check_coverage(it, bb)
     bb = W.make_batch([40, 300], num_qo_heads=8, num_kv_heads=1, head_dim=128, page_size=16)
-    assert (plan_batch(host_handle(Hq=8, Hkv=1, D=128, whole_rows=1), bb)[:, idx["kv_head"]] == 0).all()
+    assert (plan_batch(host_handle(Hq=8, Hkv=1, D=128, num_cus=2), bb)[:, idx["kv_head"]] == 0).all()
     _expect(fl.FL_ERR_INVALID_ARG, host_handle, whole_rows=2)
+
+
+@pytest.mark.parametrize("kw,why", [
+    (dict(dtype="f32"), "fp32"),
+    (dict(D=128), "head_dim"),
+    (dict(Hq=32), "16 query heads"),
+    (dict(Hq=8, Hkv=1, D=128), "one kv head"),
+    (dict(Hq=16, Hkv=4, D=64), "head_dim"),
+])
+def test_whole_rows_forced_on_a_shape_that_cannot_take_them_is_refused(kw, why):
+    """whole_rows = 1 asks for whole-row blocks on every decode step: a shape that can never
+    take them is refused at create instead of silently planned per kv head."""
+    msg = _expect(fl.FL_ERR_UNSUPPORTED, host_handle, whole_rows=1, **kw)
+    assert "whole_rows" in msg and why in msg, msg
+    host_handle(whole_rows=0, **kw)
+    host_handle(whole_rows=-1, **kw)
 
 
 def test_forced_splits_are_capped_by_tiles():
@@ -425,3 +442,108 @@ def test_neighbouring_shares_share_an_xcd():
     assert (np.diff(xcd) >= 0).all()                  # XCD 0's run, then XCD 1's, ...
     counts = np.bincount(xcd, minlength=8)
     assert counts.max() - counts.min() <= 1
+
+
+# ---- launch shape: one launch per kind of step -----------------------------------------------
+def _meta(kv_lens, qo_lens, P, rng):
+    """Page-table metadata for the given lengths, pages drawn at random from a large pool."""
+    kv_lens = np.asarray(kv_lens, np.int64)
+    pages = -(-kv_lens // P)
+    kv_indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int32)
+    pool = int(kv_indptr[-1]) + 64
+    kv_indices = rng.permutation(pool)[:kv_indptr[-1]].astype(np.int32)
+    last = (kv_lens - (pages - 1) * P).astype(np.int32)
+    qo_indptr = np.concatenate([[0], np.cumsum(qo_lens)]).astype(np.int32)
+    return qo_indptr, kv_indptr, kv_indices, last, pool
+
+
+def _serving_lengths(steps, seed, start=96, cap=160, max_prompt=4096):
+    """Decode steps of a serving loop: every request grows by one token per step, some
+    finish, new ones join with prompts of assorted lengths."""
+    rng = np.random.default_rng(seed)
+    live = list(rng.integers(1, max_prompt, size=start))
+    for _ in range(steps):
+        yield list(live)
+        live = [k + 1 for k in live]
+        for _ in range(int(rng.integers(0, 4))):           # finish
+            if live:
+                live.pop(int(rng.integers(len(live))))
+        for _ in range(int(rng.integers(0, 5))):           # join
+            if len(live) < cap:
+                live.insert(int(rng.integers(len(live) + 1)), int(rng.integers(1, max_prompt)))
+
+
+@pytest.mark.parametrize("shape", [
+    dict(Hq=14, Hkv=2, D=64, P=16, dtype="bf16"),
+    dict(Hq=12, Hkv=2, D=128, P=256, dtype="f16"),
+    dict(Hq=14, Hkv=2, D=64, P=16, dtype="bf16", whole_rows=1),
+    dict(Hq=12, Hkv=2, D=128, P=64, dtype="f32"),
+])
+def test_every_plan_of_a_kind_launches_the_same(shape):
+    """64 decode steps of a serving loop (histories grow, requests finish and join) give one
+    launch class and one grid; the workgroups past each plan's busy count are idle (no work
+    item names them). A step with a prefill chunk has its own class where its launch differs
+    (two workgroups per compute unit at head_dim 64 in a 16-bit type) and never the
+    one-launch append class."""
+    P = shape["P"]
+    wr = shape.get("whole_rows", 0)
+    h = host_handle(Hq=shape["Hq"], Hkv=shape["Hkv"], D=shape["D"], P=P, dtype=shape["dtype"],
+                    max_batch=256, max_rows=2048, max_pages=1 << 20, num_cus=256, whole_rows=wr)
+    rng = np.random.default_rng(5)
+    idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
+    seen = set()
+    batches = 0
+    for kv in _serving_lengths(64, seed=11):
+        qo, kp, ki, last, pool = _meta(kv, [1] * len(kv), P, rng)
+        h.plan(qo, kp, ki, last, pool)
+        cls, fcls, grid, busy = h.launch()
+        seen.add((cls, fcls, grid))
+        assert grid == 256 and 1 <= busy <= grid
+        groups = h.work_items()[:, idx["group"]]
+        assert set(groups.tolist()) == set(range(busy))      # the rest of the grid is idle
+        batches += 1
+    assert batches == 64 and len(seen) == 1, seen
+    (cls, fcls, grid), = seen
+    assert (fcls != 0) == (shape["dtype"] != "f32")
+    # an empty step launches the same way (every workgroup idle)
+    h.plan(np.zeros(1, np.int32), np.zeros(1, np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32), 1)
+    if not wr:
+        assert h.launch()[:3] == (cls, fcls, grid) and h.launch()[3] == 0
+    # mixed steps: chunks of 2..600 rows on top of the decodes
+    mixed = set()
+    for s, kv in enumerate(_serving_lengths(8, seed=12)):
+        ql = [1] * len(kv)
+        for j in range(1 + s % 3):
+            ql[j] = min(kv[j], 2 + 73 * (s + j))
+        qo, kp, ki, last, pool = _meta(kv, ql, P, rng)
+        h.plan(qo, kp, ki, last, pool)
+        c, f, g, b = h.launch()
+        mixed.add((c, f, g))
+        assert f == 0 and 1 <= b <= g
+    assert len(mixed) == 1
+    (c, f, g), = mixed
+    two_per_cu = shape["D"] == 64 and shape["dtype"] != "f32"
+    assert g == (512 if two_per_cu else 256)
+    assert (c == cls) == (not two_per_cu and not wr)
+
+
+def test_decode_class_changes_only_where_whole_rows_switch_on():
+    """With the default whole_rows = 0 a decode step takes whole-row blocks from one query row
+    per compute unit on: the class switches there and nowhere else."""
+    h = host_handle(max_batch=512, max_rows=512, num_cus=256)
+    rng = np.random.default_rng(6)
+    classes = {}
+    for n in (1, 100, 255, 256, 300, 512):
+        qo, kp, ki, last, pool = _meta([300] * n, [1] * n, 16, rng)
+        h.plan(qo, kp, ki, last, pool)
+        classes[n] = h.launch()[0]
+    assert classes[1] == classes[100] == classes[255]
+    assert classes[256] == classes[300] == classes[512] != classes[255]
+
+
+def test_forced_splits_launch_one_workgroup_per_piece():
+    b = W.tiny_decode()
+    h = host_handle()
+    plan_batch(h, b, num_splits=3)
+    cls, fcls, grid, busy = h.launch()
+    assert grid == busy == h.info()[1] == len(h.work_items())
