@@ -171,6 +171,25 @@ fl_status fl_paged_attn_run(fl_handle h, const void *q, const void *k_pool, cons
                             void *out, float *lse, void *stream);
 
 /*
+ * fl_paged_attn_run without any device allocation, for callers that cannot allocate
+ * device memory (code that may not call hipMalloc: tight serving loops, harnesses that
+ * forbid it). The same attention as fl_paged_attn_run on the handle's current plan, with
+ * the same kernel and launch (so the same bits), but every device buffer beyond q, the
+ * pools, out and lse -- the plan's metadata, the merge tickets and the fp32 partial rows
+ * -- lives in one fixed device array of the library (16 MiB per GPU, held by each GPU the
+ * library runs on until the process ends). The handle may be host-only (device -1:
+ * created and planned without any HIP call); the call then runs on the current device.
+ * Each call copies the plan's metadata from the handle's host memory (pageable; the copies
+ * have read their source when the call returns) and clears the merge tickets with a small
+ * kernel, on `stream`. Calls on one GPU share the array: calls that overlap on one GPU
+ * (different streams or threads) race; calls ordered on one stream do not.
+ * Pointers and layouts as for fl_paged_attn_run. Errors: those of fl_paged_attn_run, and
+ * FL_ERR_CAPACITY (with the sizes) when the plan needs more than the array holds.
+ */
+fl_status fl_paged_attn_run_noalloc(fl_handle h, const void *q, const void *k_pool,
+                                    const void *v_pool, void *out, float *lse, void *stream);
+
+/*
  * Append one layer's new K and V rows to the paged pools with the current plan, before
  * that layer's run() reads them (flashlet README, design bullets: set_kv writes the new
  * tokens into the NHD pool in place with one indexed copy; the pool keeps every layer's

@@ -48,7 +48,7 @@ class FlError(RuntimeError):
 
 
 EXPORTED = ("fl_paged_attn_create", "fl_paged_attn_destroy", "fl_paged_attn_plan",
-            "fl_paged_attn_run", "fl_paged_kv_append", "fl_paged_attn_run_append",
+            "fl_paged_attn_run", "fl_paged_attn_run_noalloc", "fl_paged_kv_append", "fl_paged_attn_run_append",
             "fl_paged_kv_append_slots", "fl_paged_kv_append_rope",
             "fl_paged_attn_plan_info", "fl_paged_attn_plan_launch",
             "fl_paged_attn_refused_launches", "fl_paged_attn_get_work_items", "fl_page_pool_create", "fl_page_pool_destroy",
@@ -74,6 +74,7 @@ def load_library(path: Optional[str] = None):
     lib.fl_paged_attn_destroy.argtypes = [vp]
     lib.fl_paged_attn_plan.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, ctypes.c_float, i32, vp]
     lib.fl_paged_attn_run.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.fl_paged_attn_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.fl_paged_kv_append.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.fl_paged_attn_run_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fl_paged_kv_append_slots.argtypes = [vp, vp, i32, ctypes.POINTER(i32)]
@@ -148,6 +149,15 @@ def fl_paged_attn_run(h, q: int, k_pool: int, v_pool: int, out: int, lse: Option
                                             ctypes.c_void_p(v_pool), ctypes.c_void_p(out),
                                             ctypes.c_void_p(lse or 0), ctypes.c_void_p(int(stream))),
            "fl_paged_attn_run")
+
+
+def fl_paged_attn_run_noalloc(h, q: int, k_pool: int, v_pool: int, out: int,
+                              lse: Optional[int] = None, stream: int = 0) -> None:
+    """fl_paged_attn_run without device allocation (the library's fixed scratch array);
+    the handle may be host-only."""
+    _check(load_library().fl_paged_attn_run_noalloc(
+        h, ctypes.c_void_p(q), ctypes.c_void_p(k_pool), ctypes.c_void_p(v_pool), ctypes.c_void_p(out),
+        ctypes.c_void_p(lse or 0), ctypes.c_void_p(int(stream))), "fl_paged_attn_run_noalloc")
 
 
 def fl_paged_kv_append(h, k_new: int, v_new: int, k_pool: int, v_pool: int,
@@ -276,6 +286,14 @@ class PagedAttention:
         fl_paged_attn_run(self.handle, q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                           out.data_ptr(), None if lse is None else lse.data_ptr(),
                           self._stream(stream))
+
+    def run_noalloc(self, q, k_pool, v_pool, out, lse=None, stream=None):
+        if stream is None and self.device < 0:
+            import torch
+            stream = torch.cuda.current_stream().cuda_stream
+        fl_paged_attn_run_noalloc(self.handle, q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                  out.data_ptr(), None if lse is None else lse.data_ptr(),
+                                  self._stream(stream))
 
     def append(self, k_new, v_new, k_pool, v_pool, stream=None):
         fl_paged_kv_append(self.handle, k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfl_paged_attn.so")
 SOURCES = ["plan.cpp", "api.cpp", "page_pool.cpp", "attn_kernels.hip", "stage_copy.hip",
-           "kv_append.hip", "kv_poison.hip", "kv_rope.hip"]
+           "kv_append.hip", "kv_poison.hip", "kv_rope.hip", "noalloc.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of every kernel; MFMA accumulators live in ordinary
 # VGPRs (the accumulator-register form costs a copy each time the VALU touches them); the

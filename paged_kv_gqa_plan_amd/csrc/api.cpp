@@ -67,6 +67,7 @@ struct fl_paged_attn {
     // current plan
     bool planned = false;
     Plan plan;
+    int32_t hdr_host[fl::kHdrInts] = {};  // its plan header (as staged to the device)
     int32_t causal = 1;
     float scale_log2 = 0.f;
 };
@@ -209,6 +210,33 @@ void fill_header(const fl_paged_attn *h, const LaunchDesc &d, int32_t *hdr) {
 }
 
 }  // namespace
+
+fl_status fl::noalloc_view(fl_handle h, NoallocView *v) {
+    if (!h) return set_err(FL_ERR_INVALID_ARG, "handle is NULL");
+    if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "run before a successful plan()");
+    const Plan &p = h->plan;
+    const LaunchDesc d = launch_desc(h, p);
+    v->device = h->host_only ? -1 : h->device;
+    v->hdr = h->hdr_host;
+    v->recs = p.wg_rec.data();
+    v->rec_bytes = (int64_t)p.wg_rec.size() * 4;
+    v->segs = p.segs.data();
+    v->seg_bytes = (int64_t)p.segs.size() * 4;
+    v->steps = p.step_rows.data();
+    v->step_bytes = (int64_t)p.step_rows.size() * 4;
+    v->num_merges = p.num_merges;
+    v->part_rows = p.part_rows;
+    v->part_width = d.head_dim;  // the kernel's row width for this plan
+    v->dtype = h->cfg.dtype;
+    v->head_dim = d.head_dim;
+    v->waves = h->waves;
+    v->grid = d.grid;
+    v->launch_class = d.cls;
+    v->num_qo_heads = h->cfg.num_qo_heads;
+    v->early = d.early;
+    v->whole_rows = d.wr;
+    return FL_OK;
+}
 
 extern "C" {
 
@@ -356,6 +384,7 @@ fl_status fl_paged_attn_plan(fl_handle h, int32_t batch, const int32_t *qo_indpt
     const double scale = sm_scale > 0.f ? (double)sm_scale : 1.0 / std::sqrt((double)h->cfg.head_dim);
     h->scale_log2 = (float)(scale * 1.4426950408889634);
     h->causal = causal ? 1 : 0;
+    fill_header(h, launch_desc(h, h->plan), h->hdr_host);
 
     if (!h->host_only) {
         hipError_t e = hipSetDevice(h->device);
@@ -374,7 +403,7 @@ fl_status fl_paged_attn_plan(fl_handle h, int32_t batch, const int32_t *qo_indpt
         // create and every run leaves them at zero (the piece that merges a row block
         // resets its ticket).
         std::memcpy(st_buf, p.segs.data(), p.segs.size() * 4);
-        fill_header(h, launch_desc(h, p), (int32_t *)(st_buf + h->off_wg_rec));
+        std::memcpy(st_buf + h->off_wg_rec, h->hdr_host, fl::kHdrInts * 4);
         std::memcpy(st_buf + h->off_wg_rec + fl::kHdrInts * 4, p.wg_rec.data(), p.wg_rec.size() * 4);
         std::memcpy(st_buf + h->off_steps, p.step_rows.data(), p.step_rows.size() * 4);
         // append slots and positions

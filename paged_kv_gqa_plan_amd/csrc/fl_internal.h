@@ -264,6 +264,25 @@ struct PoisonArgs {
 };
 int launch_kv_poison(const PoisonArgs &a, void *stream);
 
+// What the allocation-free run (noalloc.hip) needs from a planned handle: the host copy of
+// the plan's device metadata, its partial-row needs and its launch (api.cpp).
+struct NoallocView {
+    int device;                    // the handle's device, -1 for a host-only handle
+    const int32_t *hdr;            // kHdrInts
+    const int32_t *recs;           // kRecInts per busy workgroup
+    int64_t rec_bytes;
+    const int32_t *segs;
+    int64_t seg_bytes;
+    const int32_t *steps;
+    int64_t step_bytes;
+    int32_t num_merges;            // merge tickets the plan uses (must start at zero)
+    int64_t part_rows;             // fp32 partial rows of part_width floats (+ one lse each)
+    int32_t part_width;
+    int32_t dtype, head_dim, waves, grid, launch_class, num_qo_heads;
+    bool early, whole_rows;
+};
+fl_status noalloc_view(fl_handle h, NoallocView *v);
+
 // Copy byte ranges [off, off + bytes) from pinned host memory to the same offsets of a
 // device buffer with one kernel (offsets 16-byte aligned, sizes multiples of 4).
 constexpr int kStageParts = 5;

@@ -547,3 +547,22 @@ def test_forced_splits_launch_one_workgroup_per_piece():
     plan_batch(h, b, num_splits=3)
     cls, fcls, grid, busy = h.launch()
     assert grid == busy == h.info()[1] == len(h.work_items())
+
+
+def test_allocation_free_run_refuses_plans_beyond_its_array():
+    """The allocation-free run checks the plan's needs against its fixed device array before
+    any HIP call: 16384 forced pieces of 6 rows need ~50 MB of partial rows."""
+    lens = [8192] * 16
+    b = W.make_batch(lens, num_qo_heads=12, num_kv_heads=2, head_dim=128, page_size=256, dtype="f16",
+                     num_pages=16 * 32, seed=1)
+    h = host_handle(Hq=12, Hkv=2, D=128, P=256, dtype="f16", max_batch=16, max_rows=16,
+                    max_pages=1 << 12, num_cus=256)
+    plan_batch(h, b, num_splits=512)
+    assert h.info()[1] == 16384
+    msg = _expect(fl.FL_ERR_CAPACITY, fl.fl_paged_attn_run_noalloc, h.handle, 256, 256, 256, 256)
+    assert "scratch" in msg and "16777216" in msg, msg
+    # NULL and misaligned pointers are refused first, also without a GPU
+    _expect(fl.FL_ERR_INVALID_ARG, fl.fl_paged_attn_run_noalloc, h.handle, 0, 256, 256, 256)
+    _expect(fl.FL_ERR_INVALID_ARG, fl.fl_paged_attn_run_noalloc, h.handle, 258, 256, 256, 256)
+    h2 = host_handle()
+    _expect(fl.FL_ERR_NOT_PLANNED, fl.fl_paged_attn_run_noalloc, h2.handle, 256, 256, 256, 256)
