@@ -14,6 +14,11 @@ Reported (one JSON line):
   us_per_call  HIP-event time of the step's layer runs on the launch stream, divided by
                the number of layers
   roofline     the attention kernel against the 8 TB/s HBM peak
+  floors       the same launch pattern's floors: a plain read of exactly the call's K/V tiles
+               with the loads in flight at once, and an empty kernel (read_probe.hip)
+  workloads    the other workloads (mixed-length decode, long-context skew, the ragged step
+               with one prefill chunk, several chunks in one call), each timed the same way
+               with its own floors
   cpu_baseline the CPU oracle on the host's cores, on the same batch
 
 Usage: python bench.py [--workload saturated_decode] [--steps 20] [--warmup 3]
@@ -33,7 +38,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged GQA decode: µs/call and KV GB/s (% HBM peak), 128 seqs×300 ctx"
 LAYERS = {"tiny_decode": 24, "saturated_decode": 24, "ragged_mixed_step": 24,
-          "mixed_length_decode": 28, "long_context_skew": 28}
+          "mixed_length_decode": 28, "long_context_skew": 28, "multi_chunk_step": 24}
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "csrc", "attn_kernels.hip")
 PLAN_SRC = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "csrc", "plan.cpp")
 
@@ -100,7 +105,8 @@ def cpu_baseline(b, gpu_out0, budget_s: float):
     got = gpu_out0.to(torch.float64).cpu().numpy()
     err = float(np.abs(got - ref).max())
     return {"value": round(b.kv_bytes() / per_call / 1e9, 3), "unit": "GB/s",
-            "cores": oracle.max_threads(), "kind": "oracle",
+            "cores": oracle.max_threads(), "kind": "oracle", "cpu_model": cpu_model(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"the full {b.name} batch (one layer call), {calls} repeats over "
                       f"{el:.1f} s, {per_call * 1e3:.2f} ms per call (first call {first * 1e3:.1f} ms)",
             "ms_per_call": round(per_call * 1e3, 4),
@@ -388,6 +394,223 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4}), flush=True)
 
 
+def tile_rows(b):
+    """Pool row (page * P + slot) * Hkv + kv_head of the first key of every 16-key tile of
+    every (request, kv head): the tiles a decode call must read, each once."""
+    import numpy as np
+    P, Hkv = b.page_size, b.num_kv_heads
+    out = []
+    for r in range(b.batch_size):
+        kl = int(b.kv_lens[r])
+        t = np.arange(0, kl, 16)
+        pages = b.kv_indices[b.kv_indptr[r] + t // P].astype(np.int64)
+        slot_rows = pages * P + t % P
+        for h in range(Hkv):
+            out.append(slot_rows * Hkv + h)
+    return np.concatenate(out).astype(np.int32)
+
+
+def graph_us(body, stream, L: int, replays: int = 20):
+    """Median time per layer of `body` (L launches) captured in one HIP graph."""
+    import torch
+    body()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(replays)]
+    for a, e in ev:
+        a.record(stream)
+        g.replay()
+        e.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(e) / L * 1e3 for a, e in ev)
+    return us[len(us) // 2]
+
+
+def floors(b, ks, vs, L: int, stream, grid: int = 256):
+    """The read floor of the workload's access pattern and the launch floor, each as a graph
+    of L launches over the same per-layer pools the attention reads (the probe kernels of
+    paged_kv_gqa_plan_amd/csrc/read_probe.hip): a plain read of exactly the tiles the call
+    needs (each (request, kv head)'s keys once, the kv head's slice of every token row),
+    every load of a wave's tiles in flight at once where they fit (8 tiles of 128-byte
+    slices, 4 of 256-byte ones), and an empty kernel of `grid` workgroups."""
+    import ctypes
+
+    import torch
+
+    from paged_kv_gqa_plan_amd._build import PROBE_LIB
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.fl_probe_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_void_p]
+    lib.fl_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    rows = torch.from_numpy(tile_rows(b)).to("cuda:0")
+    sink = torch.zeros(grid * 4, dtype=torch.int32, device="cuda:0")
+    slice_bytes = b.head_dim * b.elem_bytes
+    nb = 8 if slice_bytes == 128 else 4
+
+    def reads():
+        s = torch.cuda.current_stream().cuda_stream  # the capture stream while capturing
+        for l in range(L):
+            assert lib.fl_probe_read_tiles(rows.data_ptr(), rows.numel(), ks[l].data_ptr(), vs[l].data_ptr(),
+                                           b.num_kv_heads, slice_bytes, nb, sink.data_ptr(), grid, s) == 0
+
+    def empties():
+        s = torch.cuda.current_stream().cuda_stream
+        for _ in range(L):
+            assert lib.fl_probe_empty(grid, s) == 0
+    read_us, empty_us = graph_us(reads, stream, L), graph_us(empties, stream, L)
+    tile_bytes = rows.numel() * 16 * slice_bytes * 2
+    tiles_per_wave = -(-rows.numel() // (grid * 4))
+    return {"read_floor_us": round(read_us, 3),
+            "read_floor_GB_per_s": round(b.kv_bytes() / (read_us * 1e-6) / 1e9, 1),
+            "read_floor_kind": f"plain read of the call's {rows.numel()} tiles ({tile_bytes} bytes, "
+                               f"the kv head's slice of 16 token rows of K and V each), {grid} "
+                               f"workgroups, up to {nb} tiles in flight per wave "
+                               f"({'all of them' if tiles_per_wave <= nb else f'of {tiles_per_wave}'}), "
+                               f"graph of {L} launches",
+            "launch_floor_us": round(empty_us, 3),
+            "launch_floor_kind": f"empty kernel of {grid} workgroups, graph of {L} launches"}
+
+
+def prefill_flops(b) -> int:
+    """Algorithmic flops of the requests with more than one query row (unmasked pairs)."""
+    pairs = 0
+    for ql, kl in zip(b.qo_lens.tolist(), b.kv_lens.tolist()):
+        if ql > 1:
+            pairs += sum(kl - ql + i + 1 for i in range(ql)) if b.causal else ql * kl
+    return pairs * b.num_qo_heads * 4 * b.head_dim
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+class Leg:
+    """One workload on the device: per-layer pools, a handle, the layer runs captured in a
+    HIP graph (or eager), timed over `steps` steps of plan + L runs."""
+
+    def __init__(self, name, args, L: int = 0):
+        import torch
+
+        import paged_kv_gqa_plan_amd as fl
+        import workloads as W
+        self.b = b = W.WORKLOADS[name](seed=args.seed)
+        self.L = L or args.layers or LAYERS[name]
+        self.q = device_tensor(b.q, b.dtype)
+        k0, v0 = device_tensor(b.k_pool, b.dtype), device_tensor(b.v_pool, b.dtype)
+        gen = torch.Generator(device="cuda:0")
+        gen.manual_seed(1000 + args.seed)
+        self.ks, self.vs = [k0], [v0]
+        for _ in range(1, self.L):
+            self.ks.append(torch.randn(k0.shape, dtype=k0.dtype, device="cuda:0", generator=gen))
+            self.vs.append(torch.randn(v0.shape, dtype=k0.dtype, device="cuda:0", generator=gen))
+        self.outs = [torch.empty(self.q.shape, dtype=k0.dtype, device="cuda:0") for _ in range(self.L)]
+        cfg = fl.make_config(b.num_qo_heads, b.num_kv_heads, b.head_dim, b.page_size, b.dtype,
+                             b.batch_size, b.rows, int(b.kv_indptr[-1]),
+                             groups_per_cu=args.groups_per_cu, min_group_tokens=args.min_group_tokens,
+                             waves_per_group=args.waves, whole_rows=args.whole_rows)
+        self.h = fl.PagedAttention(cfg, device=0)
+        self.stream = torch.cuda.current_stream()
+        self.args = args
+
+    def plan(self):
+        b = self.b
+        self.h.plan(b.qo_indptr, b.kv_indptr, b.kv_indices, b.last_page_len, b.num_pages,
+                    causal=b.causal, sm_scale=b.sm_scale, num_splits=self.args.splits)
+
+    def layers(self):
+        for l in range(self.L):
+            self.h.run(self.q, self.ks[l], self.vs[l], self.outs[l])
+
+    def time(self, steps: int, warmup: int, eager: bool = False):
+        import numpy as np
+        import torch
+        graph = None
+        if not eager:
+            self.plan()
+            self.layers()  # first launches outside the capture
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                self.layers()
+
+        def step(ev=None):
+            self.plan()
+            if ev is not None:
+                ev[0].record(self.stream)
+            if graph is not None:
+                graph.replay()
+            else:
+                self.layers()
+            if ev is not None:
+                ev[1].record(self.stream)
+
+        for _ in range(max(warmup, 1)):
+            step()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s_ in range(steps):
+            step(evs[s_])
+        torch.cuda.synchronize()
+        self.wall = time.perf_counter() - t0
+        call_ms = [a.elapsed_time(e) / self.L for (a, e) in evs]
+        plan_s = 0.0
+        for _ in range(10):
+            t1 = time.perf_counter()
+            self.plan()
+            plan_s += time.perf_counter() - t1
+        torch.cuda.synchronize()
+        self.us_call = float(np.mean(call_ms)) * 1e3
+        self.us_call_med = float(np.median(call_ms)) * 1e3
+        self.plan_us = plan_s / 10 * 1e6
+        n_items, n_groups, max_splits, ws_bytes = self.h.info()
+        b = self.b
+        achieved = b.kv_bytes() / (self.us_call * 1e-6) / 1e9
+        d = {"batch": b.batch_size, "query_rows": b.rows, "kv_tokens": int(b.kv_lens.sum()),
+             "num_qo_heads": b.num_qo_heads, "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
+             "dtype": b.dtype, "page_size": b.page_size, "layers": self.L,
+             "us_per_call": round(self.us_call, 3), "us_per_call_median": round(self.us_call_med, 3),
+             "kv_bytes_per_call": b.kv_bytes(), "kv_GB_per_s": round(achieved, 1),
+             "hbm_peak_frac": round(achieved / HBM_PEAK_GBS, 4),
+             "plan_host_us": round(self.plan_us, 2), "work_items": n_items, "workgroups": n_groups,
+             "max_splits": max_splits, "workspace_bytes": ws_bytes,
+             "launch": "eager" if eager else "hip_graph"}
+        pf = prefill_flops(b)
+        if pf:
+            # the prefill part's algorithmic flops over the whole call's time: a lower bound
+            # of its rate (the decode rows share the call)
+            d["prefill_flops_per_call"] = pf
+            d["prefill_mfma_frac_lower_bound"] = round(pf / (self.us_call * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4)
+        self.achieved = achieved
+        return d
+
+    def close(self):
+        import torch
+        self.h.close()
+        del self.q, self.ks, self.vs, self.outs
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16
+EXTRA_WORKLOADS = ("mixed_length_decode", "long_context_skew", "ragged_mixed_step", "multi_chunk_step")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,9 +628,12 @@ def main(argv=None):
                          "apply, -1 never (one block per kv head)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra-workloads", default=",".join(EXTRA_WORKLOADS),
+                    help="comma-separated workloads timed after the headline one ('' for none)")
     ap.add_argument("--attention-only", action="store_true",
-                    help="time the attention runs only (no cold call, probe, append legs or CPU "
-                         "baseline): for profiler runs, whose summaries pick the attention kernel")
+                    help="time the attention runs of the chosen workload only (no floors, cold "
+                         "call, probe, append legs, other workloads or CPU baseline): for "
+                         "profiler runs, whose summaries pick the attention kernel")
     ap.add_argument("--eager", action="store_true", help="launch layer runs without a HIP graph")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
@@ -437,91 +663,17 @@ def main(argv=None):
         copy_calibration(args.copy_calibration_mib)
         return 0
 
-    import numpy as np
-    import torch
+    # torch first: its HIP runtime is the one the library then binds to
+    import torch  # noqa: F401
 
     import paged_kv_gqa_plan_amd as fl
-    import workloads as W
 
     fl.load_library()
-    b = W.WORKLOADS[args.workload](seed=args.seed)
-    L = args.layers or LAYERS[args.workload]
+    leg = Leg(args.workload, args)
+    b, L = leg.b, leg.L
+    d = leg.time(args.steps, args.warmup, eager=args.eager)
     kv_bytes = b.kv_bytes()
-
-    q = device_tensor(b.q, b.dtype)
-    k0 = device_tensor(b.k_pool, b.dtype)
-    v0 = device_tensor(b.v_pool, b.dtype)
-    tdt = k0.dtype
-    gen = torch.Generator(device="cuda:0")
-    gen.manual_seed(1000 + args.seed)
-    ks, vs = [k0], [v0]
-    for _ in range(1, L):
-        ks.append(torch.randn(k0.shape, dtype=tdt, device="cuda:0", generator=gen))
-        vs.append(torch.randn(v0.shape, dtype=tdt, device="cuda:0", generator=gen))
-    outs = [torch.empty(q.shape, dtype=tdt, device="cuda:0") for _ in range(L)]
-
-    cfg = fl.make_config(b.num_qo_heads, b.num_kv_heads, b.head_dim, b.page_size, b.dtype,
-                         b.batch_size, b.rows, int(b.kv_indptr[-1]),
-                         groups_per_cu=args.groups_per_cu, min_group_tokens=args.min_group_tokens,
-                         waves_per_group=args.waves, whole_rows=args.whole_rows)
-    h = fl.PagedAttention(cfg, device=0)
-    stream = torch.cuda.current_stream()
-
-    def plan():
-        h.plan(b.qo_indptr, b.kv_indptr, b.kv_indices, b.last_page_len, b.num_pages,
-               causal=b.causal, sm_scale=b.sm_scale, num_splits=args.splits)
-
-    def layers():
-        for l in range(L):
-            h.run(q, ks[l], vs[l], outs[l])
-
-    graph = None
-    if not args.eager:
-        plan()
-        layers()  # first launches outside the capture
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            layers()
-
-    def step(ev=None):
-        plan()
-        if ev is not None:
-            ev[0].record(stream)
-        if graph is not None:
-            graph.replay()
-        else:
-            layers()
-        if ev is not None:
-            ev[1].record(stream)
-
-    for _ in range(max(args.warmup, 1)):
-        step()
-    torch.cuda.synchronize()
-    n_items, n_groups, max_splits, ws_bytes = h.info()
-
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    plan_s = 0.0
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s_ in range(args.steps):
-        step(evs[s_])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    call_ms = [a.elapsed_time(e) / L for (a, e) in evs]
-    # plan host time, measured on its own after the timed region
-    for _ in range(10):
-        t1 = time.perf_counter()
-        plan()
-        plan_s += time.perf_counter() - t1
-    torch.cuda.synchronize()
-    plan_us = plan_s / 10 * 1e6
-
-    us_call = float(np.mean(call_ms)) * 1e3
-    us_call_med = float(np.median(call_ms)) * 1e3
-    value = kv_bytes * L * args.steps / wall / 1e9
-    achieved = kv_bytes / (us_call * 1e-6) / 1e9
+    value = kv_bytes * L * args.steps / leg.wall / 1e9
     traffic = traffic_from_profile(args.workload)
     res = {
         "metric": METRIC,
@@ -530,7 +682,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": round(leg.wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -543,36 +695,53 @@ def main(argv=None):
                    "seed": args.seed, "splits": args.splits, "waves": args.waves,
                    "whole_rows": args.whole_rows,
                    "parallelism": "single GPU"},
-        "us_per_call": round(us_call, 3),
-        "us_per_call_median": round(us_call_med, 3),
+        "us_per_call": d["us_per_call"],
+        "us_per_call_median": d["us_per_call_median"],
         "kv_bytes_per_call": kv_bytes,
-        "hbm_peak_frac_per_call": round(achieved / HBM_PEAK_GBS, 4),
-        "attention_us_per_step": round(us_call * L, 2),
-        "launch": "eager" if args.eager else "hip_graph",
-        "plan_host_us": round(plan_us, 2),
-        "work_items": n_items,
-        "workgroups": n_groups,
-        "max_splits": max_splits,
-        "workspace_bytes": ws_bytes,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "hbm_peak_frac_per_call": d["hbm_peak_frac"],
+        "attention_us_per_step": round(leg.us_call * L, 2),
+        "launch": d["launch"],
+        "plan_host_us": d["plan_host_us"],
+        "work_items": d["work_items"],
+        "workgroups": d["workgroups"],
+        "max_splits": d["max_splits"],
+        "workspace_bytes": d["workspace_bytes"],
+        "roofline": {"bound": "hbm", "achieved": round(leg.achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(leg.achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
     }
-    out0 = outs[0].clone()  # layer 0's result, before the extra legs below overwrite it
+    out0 = leg.outs[0].clone()  # layer 0's result, before the extra legs below overwrite it
     if not args.attention_only:
-        cold = cold_call_us(h, q, ks[0], vs[0], outs[0], stream)
+        fl_ = floors(b, leg.ks, leg.vs, L, leg.stream)
+        fl_["achieved_frac_of_read_floor"] = round(fl_["read_floor_us"] / leg.us_call, 4)
+        res["floors"] = fl_
+        cold = cold_call_us(leg.h, leg.q, leg.ks[0], leg.vs[0], leg.outs[0], leg.stream)
         probe = stream_probe_gbs()
         res["cold_call_us"] = round(cold, 3)
         res["stream_probe"] = {"GB_per_s": round(probe, 1),
                                "kind": "device copy of 1 GiB, bytes read + written per second",
-                               "achieved_frac_of_probe": round(achieved / probe, 4)}
-        res["kv_append"] = time_kv_append(h, b, ks, vs, L, stream)
-        res["kv_append_rope"] = time_kv_append(h, b, ks, vs, L, stream, rope_theta=1e4)
-        res["append_attention"] = time_append_attention(h, b, q, ks, vs, outs, L, stream)
+                               "achieved_frac_of_probe": round(leg.achieved / probe, 4)}
+        res["kv_append"] = time_kv_append(leg.h, b, leg.ks, leg.vs, L, leg.stream)
+        res["kv_append_rope"] = time_kv_append(leg.h, b, leg.ks, leg.vs, L, leg.stream, rope_theta=1e4)
+        res["append_attention"] = time_append_attention(leg.h, b, leg.q, leg.ks, leg.vs, leg.outs, L,
+                                                        leg.stream)
+    leg.close()
+    if not args.attention_only and args.extra_workloads:
+        # the other workloads, each with its own floors, timed the same way
+        res["workloads"] = {}
+        for name in [w for w in args.extra_workloads.split(",") if w and w != args.workload]:
+            x = Leg(name, args)
+            e = x.time(args.steps, args.warmup, eager=args.eager)
+            f = floors(x.b, x.ks, x.vs, x.L, x.stream)
+            f["achieved_frac_of_read_floor"] = round(f["read_floor_us"] / x.us_call, 4)
+            e.update(f)
+            res["workloads"][name] = e
+            x.close()
+            print(f"# {name}: {e['us_per_call']} us per call, {e['hbm_peak_frac']:.3f} of HBM peak, "
+                  f"read floor {f['read_floor_us']} us", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline and not args.attention_only:
         res["cpu_baseline"] = cpu_baseline(b, out0, args.cpu_budget)
     print(json.dumps(res), flush=True)
-    h.close()
     return 0
 
 

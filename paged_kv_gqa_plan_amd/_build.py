@@ -10,6 +10,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfl_paged_attn.so")
+# benchmark-only measurement kernels (read floor, empty launch), a library of their own
+PROBE_LIB = os.path.join(PKG, "libfl_read_probe.so")
+PROBE_SOURCES = ["read_probe.hip"]
 SOURCES = ["plan.cpp", "api.cpp", "page_pool.cpp", "attn_kernels.hip", "stage_copy.hip",
            "kv_append.hip", "kv_poison.hip", "kv_rope.hip", "noalloc.hip"]
 ARCH = "gfx950"
@@ -28,11 +31,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build_library(verbose: bool = False, out: str = LIB, defines=()) -> str:
+def build_library(verbose: bool = False, out: str = LIB, defines=(), sources=None) -> str:
     tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-function", *DEVICE_FLAGS, *[f"-D{d}" for d in defines],
-           "-I", INCLUDE, "-I", CSRC, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           "-I", INCLUDE, "-I", CSRC, *[os.path.join(CSRC, s) for s in (sources or SOURCES)], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,5 +49,10 @@ def build_library(verbose: bool = False, out: str = LIB, defines=()) -> str:
     return out
 
 
+def build_probe(verbose: bool = False) -> str:
+    return build_library(verbose, out=PROBE_LIB, sources=PROBE_SOURCES)
+
+
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_probe(verbose=True))

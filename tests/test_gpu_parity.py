@@ -64,6 +64,14 @@ def test_ragged_mixed_step_full():
     _check(W.ragged_mixed_step())
 
 
+def test_multi_chunk_step_full():
+    """Four 128-row prefill chunks on 256..2048 cached tokens plus 124 decode rows in one call
+    (the shape bench.py times)."""
+    b = W.multi_chunk_step()
+    assert (b.qo_lens[:4] == 128).all() and (b.qo_lens[4:] == 1).all() and b.batch_size == 128
+    _check(b)
+
+
 # ---- forced slice counts: the merge path ------------------------------------------------
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 1000])
 def test_split_counts(splits):

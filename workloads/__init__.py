@@ -341,10 +341,32 @@ def ragged_mixed_step(seed: int = 0, dtype: str = "bf16", keep_dense: bool = Fal
                       keep_dense=keep_dense)
 
 
+def multi_chunk_lengths(seed: int = 0, chunks: int = 4, chunk_rows: int = 128, decodes: int = 124):
+    """Several prefill chunks sharing one 512-token budget with decode rows: 4 chunks of 128
+    rows, each on top of 256..2048 cached tokens, plus 124 decode rows with contexts uniform
+    in [32, 768]; chunk requests first."""
+    rng = rng_for(seed, 6, STREAM_LENGTHS)
+    cached = rng.integers(256, 2048, size=chunks, endpoint=True).astype(np.int32)
+    dec = rng.integers(32, 768, size=decodes, endpoint=True).astype(np.int32)
+    kv = np.concatenate([cached + chunk_rows, dec]).astype(np.int32)
+    qo = np.concatenate([np.full(chunks, chunk_rows), np.ones(decodes)]).astype(np.int32)
+    return kv, qo
+
+
+def multi_chunk_step(seed: int = 0, dtype: str = "bf16", keep_dense: bool = False) -> Batch:
+    """Four 128-row causal prefill chunks (on 256..2048 cached tokens each) plus 124 decode rows
+    in one ragged call; 14 q / 2 kv heads, d 64, 16-slot pages, 8192-page pool."""
+    kv, qo = multi_chunk_lengths(seed)
+    return make_batch(kv, qo, num_qo_heads=14, num_kv_heads=2, head_dim=64, page_size=16,
+                      dtype=dtype, num_pages=8192, seed=seed, cfg_id=6, name="multi_chunk_step",
+                      keep_dense=keep_dense)
+
+
 WORKLOADS = {
     "tiny_decode": tiny_decode,
     "saturated_decode": saturated_decode,
     "mixed_length_decode": mixed_length_decode,
     "long_context_skew": long_context_skew,
     "ragged_mixed_step": ragged_mixed_step,
+    "multi_chunk_step": multi_chunk_step,
 }
