@@ -305,7 +305,7 @@ fl_status fl_paged_attn_create(const fl_config *cfg, int device, fl_handle *out)
         release(h);
         return set_err(FL_ERR_UNSUPPORTED, "num_cus x groups_per_cu too large");
     }
-    L.seg_cap = blocks + L.group_cap;
+    L.seg_cap = blocks + fl::kQuadBlocks * L.group_cap;  // quad pieces take kQuadBlocks slots
     // steps: every row block may read at most all of the plan's pages; each work item adds
     // at most one ring group of padding per wave
     const int64_t tiles_bound = blocks * ((L.max_kv_pages * L.page_size + 15) / 16 + 1) +
@@ -612,11 +612,18 @@ fl_status fl_paged_attn_get_work_items(fl_handle h, int32_t *items, int32_t capa
     if (!h->planned) return set_err(FL_ERR_NOT_PLANNED, "no plan");
     if (capacity < 0 || (capacity > 0 && !items))
         return set_err(FL_ERR_INVALID_ARG, "items is NULL or capacity < 0");
-    const int32_t n = std::min(capacity, h->plan.num_segs);
-    if (n > 0) std::memcpy(items, h->plan.segs.data(), (size_t)n * FL_WORK_ITEM_INTS * 4);
-    if (h->plan.whole_rows)  // the kernel's virtual kv head 0 is every real kv head
-        for (int32_t i = 0; i < n; ++i) items[(size_t)i * FL_WORK_ITEM_INTS + FL_WI_KV_HEAD] = -1;
-    if (num_items) *num_items = h->plan.num_segs;
+    // the plan's segment slots without the empty ones of quads with fewer than four blocks
+    const Plan &p = h->plan;
+    int32_t n = 0;
+    for (int32_t i = 0; i < p.num_seg_slots && n < capacity; ++i) {
+        const int32_t *it = &p.segs[(size_t)i * FL_WORK_ITEM_INTS];
+        if (it[FL_WI_NUM_ROWS] == 0) continue;
+        std::memcpy(items + (size_t)n * FL_WORK_ITEM_INTS, it, FL_WORK_ITEM_INTS * 4);
+        if (p.whole_rows)  // the kernel's virtual kv head 0 is every real kv head
+            items[(size_t)n * FL_WORK_ITEM_INTS + FL_WI_KV_HEAD] = -1;
+        ++n;
+    }
+    if (num_items) *num_items = p.num_segs;
     return FL_OK;
 }
 

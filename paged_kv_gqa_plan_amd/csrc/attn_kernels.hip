@@ -197,8 +197,15 @@ struct Seg {  // wave-uniform fields of the segment being computed
     int q_start, qo_len, kv_len, kv_head, row_begin, num_rows, tok_begin, tok_end, part_row,
         split, num_splits, merge, pos_begin;
 };
+// Plan metadata is never written while a kernel runs: read through the constant address
+// space, wave-uniform reads are scalar loads even after the kernel's own stores (which
+// would otherwise make the compiler fall back to vector loads and full vmcnt drains).
+typedef __attribute__((address_space(4))) const int32_t cint32;
+__device__ __forceinline__ const cint32 *cptr(const int32_t *p) { return (const cint32 *)p; }
+
 // the same fields read from memory with wave-uniform (scalar) loads
-__device__ __forceinline__ Seg seg_fields_mem(const int32_t *h) {
+template <typename P>
+__device__ __forceinline__ Seg seg_fields_mem(P h) {
     Seg s;
     s.q_start = h[FL_WI_Q_START];
     s.qo_len = h[FL_WI_QO_LEN];
@@ -1015,6 +1022,352 @@ __device__ __forceinline__ void stage_rows(const lds_char *dst, const int32_t *r
 }
 
 // ---------------------------------------------------------------------------------------
+// prefill units (16-bit types): the rows of a prefill chunk in units of up to eight 16-row
+// blocks of one request and kv head, two blocks per wave, over 64-key steps. The four
+// waves load a step's four 16-key tiles (one each, the HalfTile ring format) into one LDS
+// buffer and all read all four, so a unit streams its keys once for 128 flattened rows and
+// each wave reads each K piece and V column once for both of its blocks; a ring of
+// kQuadBufs buffers keeps the next two steps' loads in flight during a step's arithmetic.
+// Per step and block: S^T = K Q^T over the four tiles (MFMA 16x16x32), one online-softmax
+// update for all 64 keys, and O^T += V^T P^T as two 32-key contractions (16x16x32): the
+// contraction runs over keys in any order, so 32-key operand k index 8g + j takes key
+// 4g + j of the pair's first tile (j < 4) or 4g + j - 4 of its second, which is exactly how
+// the S^T accumulators of the two tiles hold P and how the transpose reads return V.
+// ---------------------------------------------------------------------------------------
+constexpr int kQuadBufs = 3;
+constexpr int kWaveBlocks = kQuadBlocks / kMaxWaves;  // row blocks each wave computes (2)
+
+template <int D>
+struct QuadLds {
+    static constexpr int kSub = 2 * kTileTokens * 2 * D;  // one 16-key tile: K then V
+    static constexpr int kStep = kQuadStepTiles * kSub;
+    static constexpr int kQ = kTileTokens * 2 * D;        // one block's 16 Q rows
+    // step buffers, then per wave two parities of its blocks' Q rows
+    static constexpr int bytes = kQuadBufs * kStep + kMaxWaves * 2 * kWaveBlocks * kQ;
+};
+
+// One row block's state in a prefill wave.
+template <int DT, int D>
+struct UnitBlock {
+    Seg w;
+    RowInfo ri;
+    typename HalfTile<DT, D>::QOp qc;
+    int first_limit, last_limit;
+    float m_run;
+    f32x4 o[D / 16 + 1];  // the output blocks, then the row sums of p (PV against ones)
+};
+
+// One 64-key step for the wave's blocks that see some of its keys (act[b]); full[b]: no
+// mask needed. K pieces and V columns are read from LDS once and serve every block.
+template <int DT, int D>
+__device__ __forceinline__ void unit_step(const lds_char *buf, const uint32_t *roff, const uint32_t *toff,
+                                          UnitBlock<DT, D> *bs, const bool *act, const bool *full, int t0,
+                                          int grp, int tok_end, float scale_log2) {
+    using H = Half<DT>;
+    constexpr int NC = D / 32, NJ = D / 16, NB = kWaveBlocks;
+    f32x4 s[NB][kQuadStepTiles];
+#pragma unroll
+    for (int u = 0; u < kQuadStepTiles; ++u) {
+        const lds_char *src = buf + u * QuadLds<D>::kSub;
+        u32x4 kk[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kk[c] = *(const __attribute__((address_space(3))) u32x4 *)(src + roff[c]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            s[b][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (act[b]) {
+#pragma unroll
+                for (int c = 0; c < NC; ++c) s[b][u] = H::mma_k32(kk[c], bs[b].qc.q[c], s[b][u]);
+            }
+        }
+    }
+    float p[NB][kQuadStepTiles][4];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        if (!act[b]) continue;
+        if (!full[b]) {
+#pragma unroll
+            for (int u = 0; u < kQuadStepTiles; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = t0 + kTileTokens * u + 4 * grp + e;
+                    s[b][u][e] = (t < tok_end) && (t <= bs[b].ri.limit) ? s[b][u][e] : kNegInf;
+                }
+        }
+        // one running-max update for the 64 keys (lazy: moves only by more than kSlack)
+        float mt = kNegInf;
+#pragma unroll
+        for (int u = 0; u < kQuadStepTiles; ++u)
+            mt = fmaxf(mt, fmaxf(fmaxf(s[b][u][0], s[b][u][1]), fmaxf(s[b][u][2], s[b][u][3])));
+        mt = max_xor32(max_xor16(mt)) * scale_log2;
+        float &m_run = bs[b].m_run;
+        const bool move = mt > m_run + kSlack;  // false while both are -inf
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+            const float m_new = move ? mt : m_run;
+            const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;  // 0 while m_run is -inf
+            m_run = m_new;
+#pragma unroll
+            for (int j = 0; j <= NJ; ++j) bs[b].o[j] = bs[b].o[j] * alpha;
+        }
+        const float base = (full[b] || m_run != kNegInf) ? m_run : 0.f;
+#pragma unroll
+        for (int u = 0; u < kQuadStepTiles; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[b][u][e] = fast_exp2(__builtin_fmaf(s[b][u][e], scale_log2, -base));
+    }
+    // keys at or past tok_end may hold anything (NaN included): their V becomes 0
+    const bool tail = t0 + kQuadStepTokens > tok_end;
+    constexpr uint32_t kOnes = H::kOne | H::kOne << 16;
+    const u32x4 ones = {kOnes, kOnes, kOnes, kOnes};
+#pragma unroll
+    for (int v = 0; v < kQuadStepTiles / 2; ++v) {
+        const int u0 = 2 * v, u1 = 2 * v + 1;
+        const lds_char *b0 = buf + u0 * QuadLds<D>::kSub, *b1 = buf + u1 * QuadLds<D>::kSub;
+        u32x4 vt[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const u32x2 x0 = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(b0 + toff[j])));
+            const u32x2 x1 = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(b1 + toff[j])));
+            vt[j] = u32x4{x0[0], x0[1], x1[0], x1[1]};
+        }
+        if (tail) {  // wave-uniform: only a piece's last step can reach past tok_end
+            const int k0 = t0 + kTileTokens * u0 + 4 * grp, k1 = t0 + kTileTokens * u1 + 4 * grp;
+            const u32x4 m = {(k0 < tok_end ? 0xFFFFu : 0u) | (k0 + 1 < tok_end ? 0xFFFF0000u : 0u),
+                             (k0 + 2 < tok_end ? 0xFFFFu : 0u) | (k0 + 3 < tok_end ? 0xFFFF0000u : 0u),
+                             (k1 < tok_end ? 0xFFFFu : 0u) | (k1 + 1 < tok_end ? 0xFFFF0000u : 0u),
+                             (k1 + 2 < tok_end ? 0xFFFFu : 0u) | (k1 + 3 < tok_end ? 0xFFFF0000u : 0u)};
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) vt[j] &= m;
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (!act[b]) continue;
+            // P = P_hi + P_lo in the 16-bit type (as for the decode tiles); 32-key operand k
+            // index 8g + j is key 4g + j of tile u0 (j < 4) or 4g + j - 4 of tile u1
+            const float *p0 = p[b][u0], *p1 = p[b][u1];
+            uint32_t h[4] = {H::pack(p0[0], p0[1]), H::pack(p0[2], p0[3]), H::pack(p1[0], p1[1]),
+                             H::pack(p1[2], p1[3])};
+            asm("" : "+v"(h[0]), "+v"(h[1]), "+v"(h[2]), "+v"(h[3]));
+            const u32x4 ph = {h[0], h[1], h[2], h[3]};
+            const u32x4 pl = {H::pack(p0[0] - H::lo_f(h[0]), p0[1] - H::hi_f(h[0])),
+                              H::pack(p0[2] - H::lo_f(h[1]), p0[3] - H::hi_f(h[1])),
+                              H::pack(p1[0] - H::lo_f(h[2]), p1[1] - H::hi_f(h[2])),
+                              H::pack(p1[2] - H::lo_f(h[3]), p1[3] - H::hi_f(h[3]))};
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                bs[b].o[j] = H::mma_k32(vt[j], ph, bs[b].o[j]);
+                bs[b].o[j] = H::mma_k32(vt[j], pl, bs[b].o[j]);
+            }
+            bs[b].o[NJ] = H::mma_k32(ones, ph, bs[b].o[NJ]);
+            bs[b].o[NJ] = H::mma_k32(ones, pl, bs[b].o[NJ]);
+        }
+    }
+}
+
+// One wave's finish of one block of a unit piece: the final rows (or, for a piece of a
+// block cut by a share boundary, device-scope fp32 partial rows and their log2-domain lse).
+template <int DT, int D>
+__device__ __forceinline__ void unit_finish(const AttnArgs &a, const UnitBlock<DT, D> &bl, int col, int grp) {
+    constexpr int NJ = D / 16;
+    const Seg &w = bl.w;
+    const float l = bl.o[NJ][0];  // the row's sum of p, in every element of the sum block
+    if (!bl.ri.ok) return;
+    const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;  // exact for powers of two
+    const float lse2 = l > 0.f ? bl.m_run + fast_log2(l) : kNegInf;
+    if (w.part_row < 0) {
+        const int64_t row = (int64_t)(w.q_start + bl.ri.qi) * a.num_qo_heads + w.kv_head * a.group + bl.ri.qh;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const float res[4] = {bl.o[j][0] * inv, bl.o[j][1] * inv, bl.o[j][2] * inv, bl.o[j][3] * inv};
+            store_out<DT, 4>(a.out, row * D + 32 * (j >> 1) + 8 * grp + 4 * (j & 1), res);
+        }
+        if (a.lse && grp == 0) a.lse[row] = lse2 * kLn2;
+    } else {
+        const __amdgpu_buffer_rsrc_t rs = part_rsrc(a.part_o);
+        const int pr = w.part_row + col;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const float res[4] = {bl.o[j][0] * inv, bl.o[j][1] * inv, bl.o[j][2] * inv, bl.o[j][3] * inv};
+            part_store<4>(rs, (pr * D + 32 * (j >> 1) + 8 * grp + 4 * (j & 1)) * 4, res);
+        }
+        if (grp == 0) part_store1(part_rsrc(a.part_lse), pr * 4, lse2);
+    }
+}
+
+// A prefill workgroup: its share of unit pieces, step by step. Wave w computes blocks 2w
+// and 2w + 1 of each unit; every wave loads tile w of each step.
+template <int DT, int D>
+__device__ __forceinline__ void quad_path(const int *rv, const AttnArgs &a, const void *k_pool, const void *v_pool,
+                                          int hkv, const lds_char *lds, int wv, int lane) {
+    using T = HalfTile<DT, D>;
+    using UB = UnitBlock<DT, D>;
+    constexpr int NJ = D / 16, NC = D / 32, NB = kWaveBlocks;
+    constexpr int kL = T::kLoads;           // loads of one wave's tile of a step (K and V)
+    constexpr int kQL = NB * NC;            // loads of one wave's Q rows (its blocks)
+    static_assert(kQuadStepTiles == kMaxWaves, "one tile of a step per wave");
+    const int col = lane & 15, grp = lane >> 4;
+    const int seg_b = rv[REC_SEG_BEGIN];
+    const int nsteps = rv[REC_STEPS];
+    const cint32 *rows = cptr(a.step_rows) + rv[REC_POS];
+    // Q rows of block b of this wave, parity par: NB * 2 buffers per wave
+    auto qbuf = [&](int par, int b) {
+        return lds + kQuadBufs * QuadLds<D>::kStep + ((wv * 2 + par) * NB + b) * QuadLds<D>::kQ;
+    };
+    typename T::template Ring<1> ring;      // lane offsets of the tile loads and operand reads
+    T::ring_init(ring, lds, lane, hkv);
+    auto unit_steps = [](const Seg &s) { return (s.tok_end - s.tok_begin + kQuadStepTokens - 1) / kQuadStepTokens; };
+    auto seg_of = [&](int unit, int b) {
+        return seg_fields_mem(cptr(a.segs) + (size_t)(seg_b + kQuadBlocks * unit + NB * wv + b) * FL_WORK_ITEM_INTS);
+    };
+
+    // issue cursor: the unit whose steps are being loaded, and its end step
+    int iq = 0;
+    Seg iw[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) iw[b] = seg_of(0, b);
+    int i_end = unit_steps(iw[0]);
+    auto stage_q = [&](int par) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) T::template q_stage<false>(qbuf(par, b), a, iw[b], lane);
+    };
+    // step g's tile of this wave into buffer g % kQuadBufs; at a unit's first step, its Q
+    // rows go out first (into the wave's Q buffers of that unit's parity). The tile's pool
+    // row was read one step earlier (next_row), so no scalar load waits in front of it.
+    int next_row = 0;
+    auto issue = [&](int g, auto buf) {  // buf: g % kQuadBufs, a compile-time constant
+        constexpr int B = decltype(buf)::value;
+        if (g == i_end) {
+            ++iq;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) iw[b] = seg_of(iq, b);
+            i_end += unit_steps(iw[0]);
+            stage_q(iq & 1);
+        }
+        T::ring_issue(ring, B * kQuadStepTiles + wv, k_pool, v_pool, next_row);
+        if (g + 1 < nsteps) next_row = rows[kQuadStepTiles * (g + 1) + wv];
+    };
+    // compute cursor (taken before issue(1), which moves the issue cursor on when the
+    // first piece has a single step)
+    int k = 0, q_first = 0;
+    UB bs[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) bs[b].w = iw[b];
+    int q_end = unit_steps(bs[0].w);
+    stage_q(0);
+    T::ring_issue(ring, wv, k_pool, v_pool, rows[wv]);
+    if (nsteps > 1) {
+        next_row = rows[kQuadStepTiles + wv];
+        issue(1, std::integral_constant<int, 1>{});
+    }
+
+    int npend = 0;
+    Seg pend[2][NB];  // the wave's cut blocks (first and last piece of the share)
+    // one step; B = g % kQuadBufs is a compile-time constant, so every LDS address of the
+    // step is a lane's fixed offset plus an immediate
+    auto step = [&](int g, auto buf) {
+        constexpr int B = decltype(buf)::value;
+        // this wave's tile of step g (and the Q rows of a unit starting there) have landed
+        // when at most the next step's loads are outstanding
+        if (g + 1 < nsteps) {
+            if (g + 1 == q_end)  // step g + 1 starts the next unit: its Q rows went out first
+                wait_vm<kL + kQL>();
+            else
+                wait_vm<kL>();
+        } else {
+            wait_vm<0>();
+        }
+        __syncthreads();  // every wave's tile of step g is in LDS; step g - 1's buffer is free
+        if (g == q_first) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                UB &x = bs[b];
+                x.ri = row_info(x.w, a, col);
+                x.qc = T::q_fetch(qbuf(k & 1, b), x.ri, col, grp);
+                const int f_last = x.w.row_begin + max(x.w.num_rows, 1) - 1;
+                x.first_limit = a.causal ? x.w.kv_len - x.w.qo_len + div_group(x.w.row_begin, a) : x.w.kv_len - 1;
+                x.last_limit = a.causal ? x.w.kv_len - x.w.qo_len + div_group(f_last, a) : x.w.kv_len - 1;
+                x.m_run = kNegInf;
+#pragma unroll
+                for (int j = 0; j <= NJ; ++j) x.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            wait_lds();  // the Q buffers may be refilled from here on
+        }
+        if (g + 2 < nsteps) issue(g + 2, std::integral_constant<int, (B + 2) % kQuadBufs>{});
+        const int t0 = bs[0].w.tok_begin + kQuadStepTokens * (g - q_first);
+        const int tok_end = bs[0].w.tok_end;
+        bool act[NB], full[NB];
+        bool any = false;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            act[b] = bs[b].w.num_rows > 0 && t0 <= bs[b].last_limit;
+            full[b] = t0 + kQuadStepTokens <= tok_end && t0 + kQuadStepTokens - 1 <= bs[b].first_limit;
+            any = any || act[b];
+        }
+        if (any)
+            unit_step<DT, D>(lds + B * QuadLds<D>::kStep, ring.roff, ring.toff, bs, act, full, t0, grp, tok_end,
+                             a.scale_log2);
+        if (g + 1 == q_end) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                if (bs[b].w.num_rows > 0) unit_finish<DT, D>(a, bs[b], col, grp);
+            if (bs[0].w.part_row >= 0 && npend < 2) {  // a cut unit: first and last piece only
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (npend == 0)
+                        pend[0][b] = bs[b].w;
+                    else
+                        pend[1][b] = bs[b].w;
+                }
+                ++npend;
+            }
+            if (g + 1 < nsteps) {
+                ++k;
+                q_first = q_end;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) bs[b].w = seg_of(k, b);
+                q_end += unit_steps(bs[0].w);
+            }
+        }
+    };
+    static_assert(kQuadBufs == 3, "the step loop is unrolled by the three buffers");
+    for (int g = 0; g < nsteps; g += kQuadBufs) {
+        step(g, std::integral_constant<int, 0>{});
+        if (g + 1 < nsteps) step(g + 1, std::integral_constant<int, 1>{});
+        if (g + 2 < nsteps) step(g + 2, std::integral_constant<int, 2>{});
+    }
+    // merge tickets of this wave's cut blocks: each wave draws its own blocks' tickets once
+    // its partial rows are acknowledged; the piece that draws a block's last ticket merges it
+    if (npend > 0) {
+        __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (i >= npend) break;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const Seg &ps = i == 0 ? pend[0][b] : pend[1][b];
+                if (ps.num_rows == 0) continue;  // an empty slot of the unit
+                int last = 0;
+                if (lane == 0) {
+                    const int done = __hip_atomic_fetch_add(a.tickets + ps.merge, 1, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+                    if (done == ps.num_splits - 1) {
+                        __hip_atomic_store(a.tickets + ps.merge, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        last = 1;
+                    }
+                }
+                last = __builtin_amdgcn_readfirstlane(last);
+                if (last) {
+                    const int r = lane >> 2;
+                    if (r < ps.num_rows) merge_pieces<DT, D, 4, (D > 64 ? 4 : 8), false>(ps, a, r, lane & 3);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // the kernel: one workgroup per equal share of the plan's tiles
 // ---------------------------------------------------------------------------------------
 // The record and the pools come as separate leading arguments as well: those arrive in
@@ -1073,8 +1426,15 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     static_assert(!FUSE || DT != FL_F32, "the fused append runs with 16-bit types");
     constexpr int kNewB = FUSE ? 2 * 512 : 0;  // two slots of new K and V rows
     constexpr int kWaveB = kRingB + kQB + 4 * kHdrSlot + 2 * 256 + kNewB;
-    __shared__ Smem<D> sm;
-    __shared__ __attribute__((aligned(16))) char wave_lds[NW * kWaveB];
+    // one LDS area: the decode path's fold state and per-wave rings, or the prefill path's
+    // step buffers and Q rows
+    constexpr bool kQuads = !WR && !FUSE && DT != FL_F32;
+    constexpr int kSmemB = (int)((sizeof(Smem<D>) + 15) / 16 * 16);
+    constexpr int kDecodeB = kSmemB + NW * kWaveB;
+    constexpr int kQuadB = kQuads ? QuadLds<D>::bytes : 0;
+    __shared__ __attribute__((aligned(16))) char lds_raw[kDecodeB > kQuadB ? kDecodeB : kQuadB];
+    Smem<D> &sm = *reinterpret_cast<Smem<D> *>(lds_raw);
+    char *const wave_lds = lds_raw + kSmemB;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -1110,6 +1470,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     a.group_magic = (uint32_t)hv[HDR_GROUP_MAGIC];
     a.real_group = hv[HDR_REAL_GROUP];
     const int hkv = a.num_kv_heads;
+    if constexpr (kQuads) {
+        if (rv[REC_KIND] == 1) {  // a prefill workgroup
+            quad_path<DT, D>(rv, a, k_pool, v_pool, hkv, (const lds_char *)lds_raw, wv, lane);
+            return;
+        }
+    }
     const int seg_b = rv[REC_SEG_BEGIN], seg_e = rv[REC_SEG_END];
     const int pos0 = rv[REC_POS];
     const int nsteps = rv[REC_STEPS];  // steps per wave (a positive multiple of PF)

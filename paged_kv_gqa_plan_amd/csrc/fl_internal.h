@@ -69,6 +69,33 @@ constexpr int kFoldCostDecode = kStreamTileCost * FL_FOLD_TILES_DECODE;
 constexpr int kCutCostDecode = kStreamTileCost * FL_CUT_TILES_DECODE;
 constexpr int kFoldCostMixed = kStreamTileCost * FL_FOLD_TILES_MIXED;
 constexpr int kCutCostMixed = kStreamTileCost * FL_CUT_TILES_MIXED;
+// Prefill units: up to kQuadBlocks consecutive row blocks of one request and kv head (one
+// per wave: 64 flattened rows) over 64-key steps of four 16-key tiles (one loaded by each
+// wave). Two blocks per wave (128 rows) measured slower on the ragged mixed step (29.6 vs
+// 16.8 us for the chunk alone): half the units to spread, as many merges, and the two
+// blocks' arithmetic did not overlap. Planner's estimate of a unit step and of a unit
+// piece's fixed costs, in the same hundredths of a streamed decode tile as above.
+#ifndef FL_QUAD_BLOCKS
+#define FL_QUAD_BLOCKS 4
+#endif
+constexpr int kQuadBlocks = FL_QUAD_BLOCKS;
+constexpr int kQuadStepTiles = 4;
+constexpr int kQuadStepTokens = kQuadStepTiles * 16;
+#ifndef FL_QUAD_STEP_COST
+#define FL_QUAD_STEP_COST 500
+#endif
+#ifndef FL_QUAD_SEG_COST
+#define FL_QUAD_SEG_COST 400
+#endif
+// A unit cut by a share boundary costs its pieces a round trip each for the partial rows
+// and the ticket, and one more for the merge: charged 1500 (ragged mixed step 17.7-18.1 us
+// against 19.7-20.4 at 200-600 and 19.4-22 at 2500-4000; four-chunk step 17.0-17.1 us).
+#ifndef FL_QUAD_CUT_COST
+#define FL_QUAD_CUT_COST 1500
+#endif
+constexpr int64_t kQuadStepCost = FL_QUAD_STEP_COST;
+constexpr int64_t kQuadSegCost = FL_QUAD_SEG_COST;
+constexpr int64_t kQuadCutCost = FL_QUAD_CUT_COST;
 // XCDs of the GPU (MI355X: 8 of 32 compute units), which take a launch's workgroups in
 // turn; the plan places runs of neighbouring shares on one XCD (one L2).
 constexpr int kXcds = 8;
@@ -81,9 +108,13 @@ constexpr bool kXcdAwareLayout = FL_XCD_AWARE != 0;
 // steps, so every load a workgroup issues first (Q, K/V, step rows) depends on this record
 // alone. With two ring slots it is one 128-byte line, read by one batch of scalar loads.
 constexpr int kMaxWaves = 4;
+// A prefill workgroup's record (REC_KIND 1) uses the segment range (kQuadBlocks slots per
+// quad piece), REC_POS (its first step row: kQuadBlocks per 64-key step) and REC_STEPS
+// (its 64-key steps).
 enum {
     REC_HEAD = 0,    // FL_WORK_ITEM_INTS entries
     REC_SEG_BEGIN = 16, REC_SEG_END = 17, REC_POS = 18, REC_STEPS = 19, REC_FIRST_END = 20,
+    REC_KIND = 21,   // 0: decode blocks, 1: prefill quads
     REC_ROWS = 24,   // kMaxWaves * kRingDepth entries
 };
 constexpr int kRecInts = (REC_ROWS + kMaxWaves * kRingDepth + 31) / 32 * 32;
@@ -148,8 +179,10 @@ struct Plan {
                                     // (page * P + slot) * Hkv + kv_head of the step's tile's
                                     // first key (padding steps repeat a real tile's row)
     int32_t num_groups = 0;
+    int32_t num_prefill_groups = 0; // workgroups 0 .. this - 1 run prefill quads
     int32_t groups_per_cu = 1;      // workgroups per compute unit the shares were cut for
-    int32_t num_segs = 0;
+    int32_t num_segs = 0;           // work items (empty quad slots not counted)
+    int32_t num_seg_slots = 0;      // segment slots in segs
     int32_t num_merges = 0;
     bool whole_rows = false;        // blocks hold every query head of a request and read whole
                                     // token rows (one virtual kv head of Hkv * D values)

@@ -213,14 +213,27 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
             for (int64_t x = h * slice; x < (h + 1) * slice; x += 16) odd += (x / 256) & 1;
             odd_pct[h] = 100 * odd / (slice / 16);
         }
+    // Prefill units: in a 16-bit type, a request with more than one row block per kv head (a
+    // prefill chunk) runs in units of up to kQuadBlocks consecutive blocks (two per wave)
+    // over 64-key steps whose K/V the waves share through LDS. Every block of a unit spans
+    // the unit's keys (the keys of its last row); the kernel masks each row at its own
+    // causal limit.
+    const bool quads_ok = lim.dtype != FL_F32 && !out.whole_rows;
     std::vector<Block> blocks;
+    struct Quad {
+        int64_t block0;
+        int32_t nblocks, kv_end;
+    };
+    std::vector<Quad> quads;
     for (int32_t r = 0; r < B; ++r) {
         const int32_t np = in.kv_indptr[r + 1] - in.kv_indptr[r];
         const int32_t kv_len = (np - 1) * P + in.last_page_len[r];
         const int32_t ql = in.qo_indptr ? in.qo_indptr[r + 1] - in.qo_indptr[r] : 1;
         const int32_t nflat = ql * G;
         const int32_t base_cost = nflat > kBlockRows ? kSharedTileCost : kStreamTileCost;
-        for (int32_t h = 0; h < Hkv; ++h)
+        const bool quad = quads_ok && nflat > kBlockRows;
+        for (int32_t h = 0; h < Hkv; ++h) {
+            const int64_t first = (int64_t)blocks.size();
             for (int32_t f0 = 0; f0 < nflat; f0 += kBlockRows) {
                 const int32_t tile_cost =
                     (int32_t)(base_cost * (10000 + kOddHalfPercent * (odd_pct[h] - 50)) / 10000);
@@ -229,64 +242,115 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
                 const int32_t kv_end = in.causal ? kv_len - ql + i_last + 1 : kv_len;
                 blocks.push_back({r, h, f0, nr, kv_end, tile_cost});
             }
+            if (!quad) continue;
+            for (int64_t b0 = first; b0 < (int64_t)blocks.size(); b0 += kQuadBlocks) {
+                const int32_t n = (int32_t)std::min<int64_t>(kQuadBlocks, (int64_t)blocks.size() - b0);
+                const int32_t kv_end = blocks[b0 + n - 1].kv_end;
+                for (int32_t w = 0; w < n; ++w) blocks[b0 + w].kv_end = kv_end;
+                quads.push_back({b0, n, kv_end});
+            }
+        }
     }
     const int64_t nblocks = (int64_t)blocks.size();
-    std::vector<int64_t> tiles(nblocks), first_tile(nblocks + 1, 0);
+    std::vector<char> in_quad(nblocks, 0);
+    for (const Quad &qd : quads)
+        for (int32_t w = 0; w < qd.nblocks; ++w) in_quad[qd.block0 + w] = 1;
+    std::vector<int64_t> dblocks;  // blocks of the decode path
+    std::vector<int64_t> tiles(nblocks, 0);
+    int64_t T = 0;
     for (int64_t b = 0; b < nblocks; ++b) {
+        if (in_quad[b]) continue;
+        dblocks.push_back(b);
         tiles[b] = ceil_div(blocks[b].kv_end, kTileTokens);
-        first_tile[b + 1] = first_tile[b] + tiles[b];
+        T += tiles[b];
     }
-    const int64_t T = first_tile[nblocks];
+    const int64_t nquads = (int64_t)quads.size();
+    std::vector<int64_t> qsteps(nquads);
+    int64_t QS = 0;
+    for (int64_t q = 0; q < nquads; ++q) {
+        qsteps[q] = ceil_div(quads[q].kv_end, kQuadStepTokens);
+        QS += qsteps[q];
+    }
 
-    // ---- pieces: (block, tile range), grouped by workgroup -----------------------------
+    // ---- pieces: (block or quad, tile or step range), grouped by workgroup --------------
+    // Workgroups 0 .. Gp-1 run the quads' pieces (the prefill path), the rest the decode
+    // blocks' pieces.
     struct Piece {
-        int64_t block, lo, hi, group;
+        bool quad;
+        int64_t idx, lo, hi, group;
     };
     std::vector<Piece> pieces;
-    int64_t G_wg = 0;
+    int64_t Gp = 0, G_wg = 0;
     if (in.num_splits > 0) {
-        // every block in num_splits balanced pieces (fewer for short blocks), one workgroup each
-        for (int64_t b = 0; b < nblocks; ++b) {
-            int64_t s = std::max<int64_t>(1, std::min<int64_t>(in.num_splits, tiles[b]));
-            const int64_t per = ceil_div(tiles[b], s);
-            s = ceil_div(tiles[b], per);
+        // every block or quad in num_splits balanced pieces (fewer for short ones), one
+        // workgroup each
+        auto cut = [&](bool is_quad, int64_t idx, int64_t n) {
+            int64_t s = std::max<int64_t>(1, std::min<int64_t>(in.num_splits, n));
+            const int64_t per = ceil_div(n, s);
+            s = ceil_div(n, per);
             for (int64_t j = 0; j < s; ++j)
-                pieces.push_back({b, j * per, std::min<int64_t>((j + 1) * per, tiles[b]), G_wg++});
-        }
+                pieces.push_back({is_quad, idx, j * per, std::min<int64_t>((j + 1) * per, n), G_wg++});
+        };
+        for (int64_t q = 0; q < nquads; ++q) cut(true, q, qsteps[q]);
+        Gp = G_wg;
+        for (int64_t b : dblocks) cut(false, b, tiles[b]);
     } else {
-        // Contiguous shares of the tile sequence with equal estimated time. A piece of n tiles
-        // costs the ring steps it occupies in all waves (n rounded up to whole step groups,
-        // at its block's tile cost) plus a fixed charge for its fold; a block cut inside a
-        // share is cut at a multiple of a step group, so only a block's last piece carries
-        // padding. The smallest per-share budget that needs at most G shares is found by
-        // bisection.
+        // Contiguous shares of each sequence (quad steps; decode tiles) with equal estimated
+        // time. A decode piece of n tiles costs the ring steps it occupies in all waves (n
+        // rounded up to whole step groups, at its block's tile cost) plus a fixed charge for
+        // its fold; a block cut inside a share is cut at a multiple of a step group, so only
+        // a block's last piece carries padding. A quad piece of n steps costs n steps plus
+        // its finish. The smallest per-share budget that needs at most the given number of
+        // shares is found by bisection. The grid's workgroups are divided between the two
+        // paths in proportion to their estimated totals.
         const int64_t kFoldCost = prefill ? kFoldCostMixed : out.whole_rows ? kFoldCostWhole : kFoldCostDecode;
         const int64_t kCutCost = prefill ? kCutCostMixed : out.whole_rows ? kCutCostWhole : kCutCostDecode;
         const int64_t want = (int64_t)lim.num_cus * gpc;
-        const int64_t G_max = std::min(std::max<int64_t>(1, std::min(want, ceil_div(T, lim.min_group_tiles))), T);
         const int64_t U = (int64_t)lim.waves * kRingDepth;
-        auto cost = [&](int64_t b, int64_t n, bool cut) {
+        auto dcost = [&](int64_t b, int64_t n, bool cut) {
             return blocks[b].tile_cost * U * ceil_div(n, U) + kFoldCost + (cut ? kCutCost : 0);
         };
-        // walk the blocks filling shares of budget C; emit pieces when `out` is set
-        auto fill = [&](int64_t C, bool out) {
-            int64_t shares = 0, b = 0, pos = 0;
-            while (b < nblocks) {
+        auto qcost = [&](int64_t, int64_t n, bool cut) {
+            return kQuadStepCost * n + kQuadSegCost + (cut ? kQuadCutCost : 0);
+        };
+        int64_t Cd = 0, Cp = 0;
+        for (int64_t b : dblocks) Cd += dcost(b, tiles[b], false);
+        for (int64_t q = 0; q < nquads; ++q) Cp += qcost(q, qsteps[q], false);
+        int64_t Gp_max = 0, Gd_max = 0;
+        if (nquads == 0) {
+            Gd_max = want;
+        } else if (dblocks.empty()) {
+            Gp_max = want;
+        } else {
+            Gp_max = std::min<int64_t>(want - 1, std::max<int64_t>(1, (want * Cp + (Cp + Cd) / 2) / (Cp + Cd)));
+            Gd_max = want - Gp_max;
+        }
+        Gp_max = std::min(Gp_max, QS);
+        Gd_max = std::min(std::max<int64_t>(dblocks.empty() ? 0 : 1, std::min(Gd_max, ceil_div(T, lim.min_group_tiles))), T);
+        // walk the units filling shares of budget C; emit pieces (group = first_group +
+        // share) when `emit` is set. cost(u, n, cut); unit sizes n_of(u); step granularity.
+        auto fill = [&](const std::vector<int64_t> &units, auto n_of, auto cost, int64_t gran, bool is_quad,
+                        int64_t C, int64_t first_group, bool emit) {
+            int64_t shares = 0, i = 0, pos = 0;
+            const int64_t nu = (int64_t)units.size();
+            while (i < nu) {
                 int64_t budget = C;
-                while (b < nblocks) {
-                    const int64_t r = tiles[b] - pos;
-                    if (cost(b, r, pos > 0) <= budget) {
-                        if (out) pieces.push_back({b, pos, tiles[b], shares});
-                        budget -= cost(b, r, pos > 0);
-                        ++b;
+                while (i < nu) {
+                    const int64_t u = units[i];
+                    const int64_t r = n_of(u) - pos;
+                    if (cost(u, r, pos > 0) <= budget) {
+                        if (emit) pieces.push_back({is_quad, u, pos, n_of(u), first_group + shares});
+                        budget -= cost(u, r, pos > 0);
+                        ++i;
                         pos = 0;
                         continue;
                     }
-                    const int64_t step_cost = blocks[b].tile_cost * U;
-                    const int64_t fixed = kFoldCost + kCutCost;
-                    const int64_t n = budget >= fixed + step_cost ? U * ((budget - fixed) / step_cost) : 0;
+                    // the largest whole number of step groups that fits the remaining budget
+                    const int64_t step_cost = cost(u, gran, true) - cost(u, 0, true);
+                    const int64_t fixed = cost(u, 0, true);
+                    const int64_t n = budget >= fixed + step_cost ? gran * ((budget - fixed) / step_cost) : 0;
                     if (n > 0) {
-                        if (out) pieces.push_back({b, pos, pos + n, shares});
+                        if (emit) pieces.push_back({is_quad, u, pos, pos + n, first_group + shares});
                         pos += n;
                     }
                     break;
@@ -295,28 +359,45 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
             }
             return shares;
         };
-        int64_t total = 0;
-        for (int64_t b = 0; b < nblocks; ++b) total += cost(b, tiles[b], false);
+        auto balance = [&](const std::vector<int64_t> &units, auto n_of, auto cost, int64_t gran, bool is_quad,
+                           int64_t G_max, int64_t least, int64_t first_group) {
+            if (units.empty() || G_max <= 0) return (int64_t)0;
+            int64_t total = 0;
+            for (int64_t u : units) total += cost(u, n_of(u), false);
+            int64_t lo = std::max<int64_t>(least, ceil_div(total, G_max)), hi = std::max(total, least);
+            while (lo < hi) {  // every budget >= least makes progress
+                const int64_t mid = lo + (hi - lo) / 2;
+                if (fill(units, n_of, cost, gran, is_quad, mid, first_group, false) <= G_max)
+                    hi = mid;
+                else
+                    lo = mid + 1;
+            }
+            return fill(units, n_of, cost, gran, is_quad, lo, first_group, true);
+        };
+        std::vector<int64_t> qunits(nquads);
+        std::iota(qunits.begin(), qunits.end(), 0);
+        auto q_n = [&](int64_t q) { return qsteps[q]; };
+        auto d_n = [&](int64_t b) { return tiles[b]; };
+        Gp = balance(qunits, q_n, qcost, 1, true, Gp_max, qcost(0, 1, true), 0);
         int64_t max_tile_cost = 0;
-        for (const Block &bl : blocks) max_tile_cost = std::max<int64_t>(max_tile_cost, bl.tile_cost);
-        const int64_t least = kFoldCost + kCutCost + max_tile_cost * U;
-        int64_t lo = std::max<int64_t>(least, ceil_div(total, G_max)), hi = std::max(total, least);
-        while (lo < hi) {  // every budget >= least makes progress
-            const int64_t mid = lo + (hi - lo) / 2;
-            if (fill(mid, false) <= G_max)
-                hi = mid;
-            else
-                lo = mid + 1;
-        }
-        G_wg = fill(lo, true);
+        for (int64_t b : dblocks) max_tile_cost = std::max<int64_t>(max_tile_cost, blocks[b].tile_cost);
+        G_wg = Gp + balance(dblocks, d_n, dcost, U, false, Gd_max, kFoldCost + kCutCost + max_tile_cost * U, Gp);
     }
-    if ((int64_t)pieces.size() > lim.seg_cap || G_wg > lim.group_cap)
+    int64_t nslots = 0;  // segment slots: one per decode piece, kQuadBlocks per quad piece
+    for (const Piece &pc : pieces) nslots += pc.quad ? kQuadBlocks : 1;
+    if (nslots > lim.seg_cap || G_wg > lim.group_cap)
         return fail(err, FL_ERR_CAPACITY, "%lld work items / %lld workgroups exceed the handle's "
-                    "capacity (%lld); lower num_splits", (long long)pieces.size(), G_wg, lim.seg_cap);
+                    "capacity (%lld); lower num_splits", nslots, G_wg, lim.seg_cap);
 
-    // pieces per block, partial rows and merge tickets
+    // pieces per block, partial rows and merge tickets (a quad's blocks are cut alike)
     std::vector<int32_t> npieces(nblocks, 0), piece_idx(pieces.size());
-    for (size_t k = 0; k < pieces.size(); ++k) piece_idx[k] = npieces[pieces[k].block]++;
+    for (size_t k = 0; k < pieces.size(); ++k) {
+        const Piece &pc = pieces[k];
+        const int64_t b0 = pc.quad ? quads[pc.idx].block0 : pc.idx;
+        const int32_t nb = pc.quad ? quads[pc.idx].nblocks : 1;
+        piece_idx[k] = npieces[b0];
+        for (int32_t w = 0; w < nb; ++w) ++npieces[b0 + w];
+    }
     std::vector<int64_t> part_base(nblocks, -1);
     std::vector<int32_t> merge_of(nblocks, -1);
     int64_t part_next = 0;
@@ -333,102 +414,149 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         return fail(err, FL_ERR_CAPACITY, "%lld partial rows exceed the workspace (%lld rows)",
                     part_next, lim.part_rows_cap);
 
-    // ---- emit segments, workgroup tables and per-wave step rows --------------------------
-    // Within a segment, tile j goes to wave j % NW as that wave's step j / NW; every
-    // segment's per-wave step count is rounded up to a multiple of the ring depth, the
-    // same in all waves. Padding steps repeat a real tile of the segment (never scored).
+    // ---- emit segments, workgroup tables and step rows ----------------------------------
+    // Decode pieces: one segment each; within it tile j goes to wave j % NW as that wave's
+    // step j / NW; every segment's per-wave step count is rounded up to a multiple of the
+    // ring depth, the same in all waves. Padding steps repeat a real tile of the segment
+    // (never scored). Quad pieces: kQuadBlocks segment slots each (slots past the quad's
+    // blocks hold num_rows 0), and per 64-key step the pool rows of its four 16-key tiles.
     const int NW = lim.waves;
-    out.segs.assign(pieces.size() * FL_WORK_ITEM_INTS, 0);
-    out.wg_rec.assign(G_wg * kRecInts, 0);
-    out.step_rows.clear();
-    std::vector<int64_t> seg_steps(pieces.size());
     int64_t total = 0;
+    std::vector<int64_t> seg_steps(pieces.size());
     for (size_t k = 0; k < pieces.size(); ++k) {
-        const int64_t nt = pieces[k].hi - pieces[k].lo;
-        seg_steps[k] = ceil_div(ceil_div(nt, NW), kRingDepth) * kRingDepth;
-        total += seg_steps[k] * NW;
+        const int64_t n = pieces[k].hi - pieces[k].lo;
+        if (pieces[k].quad) {
+            seg_steps[k] = n;
+            total += n * kQuadStepTiles;
+        } else {
+            seg_steps[k] = ceil_div(ceil_div(n, NW), kRingDepth) * kRingDepth;
+            total += seg_steps[k] * NW;
+        }
     }
     if (total > lim.max_tiles)
         return fail(err, FL_ERR_CAPACITY, "%lld tile steps exceed max_tiles %lld", total,
                     lim.max_tiles);
+    out.segs.assign((size_t)nslots * FL_WORK_ITEM_INTS, 0);
+    out.wg_rec.assign(G_wg * kRecInts, 0);
     out.step_rows.assign((size_t)total, 0);
-    size_t k = 0;
-    int64_t off = 0;
     // Workgroup b runs on XCD b % kXcds (workgroups are handed to the XCDs in turn), and
-    // each XCD has its own L2. Shares next to each other in the tile sequence hold
-    // neighbouring row blocks, which for a prefill chunk read the same K/V, so share s goes
-    // to the workgroup that puts runs of consecutive shares on one XCD: the first
-    // ceil(G / kXcds) shares on XCD 0, the next on XCD 1, and so on.
-    const auto workgroup_of = [&](int64_t share) -> int64_t {
-        if (!kXcdAwareLayout) return share;
-        int64_t first = 0;
+    // each XCD has its own L2. Shares next to each other in a sequence hold neighbouring row
+    // blocks, which for a prefill chunk read the same K/V, so share s of a path with n shares
+    // (starting at workgroup `first`) goes to the workgroup that puts runs of consecutive
+    // shares on one XCD: the first ceil(n / kXcds) shares on one XCD, the next on the next.
+    const auto workgroup_of = [&](int64_t share, int64_t n, int64_t first) -> int64_t {
+        if (!kXcdAwareLayout) return first + share;
+        int64_t lo = 0;
         for (int64_t x = 0; x < kXcds; ++x) {
-            const int64_t n_x = (G_wg - x + kXcds - 1) / kXcds;  // workgroups on XCD x
-            if (share < first + n_x) return (share - first) * kXcds + x;
-            first += n_x;
+            const int64_t n_x = (n - x + kXcds - 1) / kXcds;  // shares on this XCD
+            if (share < lo + n_x) return first + (share - lo) * kXcds + x;
+            lo += n_x;
         }
-        return share;  // not reached
+        return first + share;  // not reached
     };
+    auto fill_item = [&](int32_t *it, const Block &bl, int64_t t0, int64_t t1, int64_t b, int32_t pidx,
+                         int64_t wg, int64_t pos) {
+        const int32_t np = in.kv_indptr[bl.req + 1] - in.kv_indptr[bl.req];
+        it[FL_WI_Q_START] = in.qo_indptr ? in.qo_indptr[bl.req] : bl.req;
+        it[FL_WI_QO_LEN] = in.qo_indptr ? in.qo_indptr[bl.req + 1] - in.qo_indptr[bl.req] : 1;
+        it[FL_WI_KV_LEN] = (np - 1) * P + in.last_page_len[bl.req];
+        it[FL_WI_PAGE_BASE] = in.kv_indptr[bl.req];
+        it[FL_WI_KV_HEAD] = bl.kvh;
+        it[FL_WI_ROW_BEGIN] = bl.row_begin;
+        it[FL_WI_NUM_ROWS] = bl.nrows;
+        it[FL_WI_TOK_BEGIN] = (int32_t)t0;
+        it[FL_WI_TOK_END] = (int32_t)t1;
+        it[FL_WI_PART_ROW] = npieces[b] > 1 ? (int32_t)(part_base[b] + (int64_t)pidx * bl.nrows) : -1;
+        it[FL_WI_REQUEST] = bl.req;
+        it[FL_WI_SPLIT] = pidx;
+        it[FL_WI_NUM_SPLITS] = npieces[b];
+        it[FL_WI_MERGE] = merge_of[b];
+        it[FL_WI_GROUP] = (int32_t)wg;
+        it[FL_WI_POS_BEGIN] = (int32_t)pos;
+    };
+    auto pool_row = [&](const Block &bl, int64_t t) {
+        const int32_t *pages = in.kv_indices + in.kv_indptr[bl.req];
+        return (int32_t)(((int64_t)pages[t / P] * P + t % P) * Hkv + bl.kvh);
+    };
+    size_t k = 0;
+    int64_t slot = 0, off = 0;
+    int32_t real_segs = 0;
     for (int64_t g = 0; g < G_wg; ++g) {
-        const int64_t wg = workgroup_of(g);
+        const bool pg = g < Gp;
+        const int64_t wg = pg ? workgroup_of(g, Gp, 0) : workgroup_of(g - Gp, G_wg - Gp, Gp);
         int32_t *rec = &out.wg_rec[wg * kRecInts];
         size_t k_end = k;
-        int64_t steps = 0;
-        while (k_end < pieces.size() && pieces[k_end].group == g) steps += seg_steps[k_end++];
-        rec[REC_SEG_BEGIN] = (int32_t)k;
-        rec[REC_SEG_END] = (int32_t)k_end;
+        int64_t steps = 0, slots = 0;
+        while (k_end < pieces.size() && pieces[k_end].group == g) {
+            steps += seg_steps[k_end];
+            slots += pieces[k_end].quad ? kQuadBlocks : 1;
+            ++k_end;
+        }
+        rec[REC_KIND] = pg ? 1 : 0;
+        rec[REC_SEG_BEGIN] = (int32_t)slot;
+        rec[REC_SEG_END] = (int32_t)(slot + slots);
         rec[REC_POS] = (int32_t)off;
         rec[REC_STEPS] = (int32_t)steps;
         rec[REC_FIRST_END] = (int32_t)seg_steps[k];
-        const size_t k_first = k;
+        const int64_t slot_first = slot;
         int64_t pos = 0;
         for (; k < k_end; ++k) {
             const Piece &pc = pieces[k];
-            const Block &bl = blocks[pc.block];
-            const int32_t np = in.kv_indptr[bl.req + 1] - in.kv_indptr[bl.req];
-            const int32_t kv_len = (np - 1) * P + in.last_page_len[bl.req];
-            const int64_t t0 = pc.lo * kTileTokens;
-            const int64_t t1 = std::min<int64_t>(pc.hi * kTileTokens, bl.kv_end);
-            int32_t *it = &out.segs[k * FL_WORK_ITEM_INTS];
-            it[FL_WI_Q_START] = in.qo_indptr ? in.qo_indptr[bl.req] : bl.req;
-            it[FL_WI_QO_LEN] = in.qo_indptr ? in.qo_indptr[bl.req + 1] - in.qo_indptr[bl.req] : 1;
-            it[FL_WI_KV_LEN] = kv_len;
-            it[FL_WI_PAGE_BASE] = in.kv_indptr[bl.req];
-            it[FL_WI_KV_HEAD] = bl.kvh;
-            it[FL_WI_ROW_BEGIN] = bl.row_begin;
-            it[FL_WI_NUM_ROWS] = bl.nrows;
-            it[FL_WI_TOK_BEGIN] = (int32_t)t0;
-            it[FL_WI_TOK_END] = (int32_t)t1;
-            it[FL_WI_PART_ROW] =
-                npieces[pc.block] > 1
-                    ? (int32_t)(part_base[pc.block] + (int64_t)piece_idx[k] * bl.nrows)
-                    : -1;
-            it[FL_WI_REQUEST] = bl.req;
-            it[FL_WI_SPLIT] = piece_idx[k];
-            it[FL_WI_NUM_SPLITS] = npieces[pc.block];
-            it[FL_WI_MERGE] = merge_of[pc.block];
-            it[FL_WI_GROUP] = (int32_t)wg;
-            it[FL_WI_POS_BEGIN] = (int32_t)pos;
-            const int32_t *pages = in.kv_indices + in.kv_indptr[bl.req];
-            const int64_t nt = pc.hi - pc.lo;
-            for (int64_t q = 0; q < seg_steps[k]; ++q)
-                for (int w = 0; w < NW; ++w) {
-                    int64_t j = q * NW + w;
-                    if (j >= nt) j = (nt - 1 - w >= 0) ? nt - 1 - ((nt - 1 - w) % NW) : 0;
-                    const int64_t t = t0 + j * kTileTokens;
-                    const int64_t slot = (int64_t)pages[t / P] * P + t % P;
-                    out.step_rows[off + w * steps + pos + q] = (int32_t)(slot * Hkv + bl.kvh);
+            if (pc.quad) {
+                const Quad &qd = quads[pc.idx];
+                const Block &b0 = blocks[qd.block0];
+                const int64_t t0 = pc.lo * kQuadStepTokens;
+                const int64_t t1 = std::min<int64_t>(pc.hi * kQuadStepTokens, qd.kv_end);
+                for (int32_t w = 0; w < kQuadBlocks; ++w, ++slot) {
+                    int32_t *it = &out.segs[slot * FL_WORK_ITEM_INTS];
+                    if (w < qd.nblocks) {
+                        fill_item(it, blocks[qd.block0 + w], t0, t1, qd.block0 + w, piece_idx[k], wg, pos);
+                        ++real_segs;
+                    } else {  // an empty slot: the same request and keys, no rows
+                        fill_item(it, b0, t0, t1, qd.block0, piece_idx[k], wg, pos);
+                        it[FL_WI_NUM_ROWS] = 0;
+                        it[FL_WI_MERGE] = -1;
+                        it[FL_WI_PART_ROW] = -1;
+                    }
                 }
+                // per step, the pool rows of its four 16-key tiles (tiles past the keys
+                // repeat the last real one; their keys are never scored)
+                const int64_t last_tile = (qd.kv_end - 1) / kTileTokens * kTileTokens;
+                for (int64_t s = pc.lo; s < pc.hi; ++s)
+                    for (int32_t u = 0; u < kQuadStepTiles; ++u) {
+                        const int64_t t = std::min<int64_t>(s * kQuadStepTokens + u * kTileTokens, last_tile);
+                        out.step_rows[off + (s - pc.lo) * kQuadStepTiles + u] = pool_row(b0, t);
+                    }
+                off += (pc.hi - pc.lo) * kQuadStepTiles;
+            } else {
+                const Block &bl = blocks[pc.idx];
+                const int64_t t0 = pc.lo * kTileTokens;
+                const int64_t t1 = std::min<int64_t>(pc.hi * kTileTokens, bl.kv_end);
+                fill_item(&out.segs[slot * FL_WORK_ITEM_INTS], bl, t0, t1, pc.idx, piece_idx[k], wg, pos);
+                ++slot;
+                ++real_segs;
+                const int64_t nt = pc.hi - pc.lo;
+                for (int64_t q = 0; q < seg_steps[k]; ++q)
+                    for (int w = 0; w < NW; ++w) {
+                        int64_t j = q * NW + w;
+                        if (j >= nt) j = (nt - 1 - w >= 0) ? nt - 1 - ((nt - 1 - w) % NW) : 0;
+                        out.step_rows[off + w * steps + pos + q] = pool_row(bl, t0 + j * kTileTokens);
+                    }
+            }
             pos += seg_steps[k];
         }
-        std::copy_n(&out.segs[k_first * FL_WORK_ITEM_INTS], FL_WORK_ITEM_INTS, rec + REC_HEAD);
-        for (int w = 0; w < NW; ++w)  // every share has >= kRingDepth steps per wave
-            for (int q = 0; q < kRingDepth; ++q)
-                rec[REC_ROWS + w * kRingDepth + q] = out.step_rows[off + w * steps + q];
-        off += steps * NW;
+        if (!pg) {
+            std::copy_n(&out.segs[slot_first * FL_WORK_ITEM_INTS], FL_WORK_ITEM_INTS, rec + REC_HEAD);
+            for (int w = 0; w < NW; ++w)  // every share has >= kRingDepth steps per wave
+                for (int q = 0; q < kRingDepth; ++q)
+                    rec[REC_ROWS + w * kRingDepth + q] = out.step_rows[off + w * steps + q];
+            off += steps * NW;
+        }
     }
     out.num_groups = (int32_t)G_wg;
-    out.num_segs = (int32_t)pieces.size();
+    out.num_prefill_groups = (int32_t)Gp;
+    out.num_segs = real_segs;
+    out.num_seg_slots = (int32_t)nslots;
     out.num_merges = merges;
     out.part_rows = part_next;
     return FL_OK;

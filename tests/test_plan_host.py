@@ -38,10 +38,19 @@ def plan_batch(h, b, num_splits=0, causal=None):
     return h.work_items()
 
 
+def quad_rows(b, r, whole=False):
+    """Flattened rows per prefill unit of request r: 64 for a chunk of more than one 16-row
+    block in a 16-bit type (the prefill path), else 0 (blocks of the decode path)."""
+    G = b.num_qo_heads if whole else b.group
+    return 64 if (b.dtype != "f32" and not whole and int(b.qo_lens[r]) * G > 16) else 0
+
+
 def check_coverage(items, b, causal=True):
     """Every (request, kv head, flattened row) sees exactly its causal key range, once, in
     16-aligned non-empty slices; split items own disjoint partial rows. Whole-row items
-    (kv_head -1) cover every kv head at once, their rows flattened over all query heads."""
+    (kv_head -1) cover every kv head at once, their rows flattened over all query heads.
+    Blocks of a prefill unit (64 flattened rows) span the keys of the unit's last row; the
+    kernel masks each row at its own limit."""
     idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
     col = lambda n: items[:, idx[n]]
     whole = bool((col("kv_head") == -1).any())
@@ -60,8 +69,9 @@ def check_coverage(items, b, causal=True):
     part_used = set()
     for (r, h, f0, nr), sl in cover.items():
         kl, ql = int(b.kv_lens[r]), int(b.qo_lens[r])
-        i_last = (f0 + nr - 1) // G
-        kv_end = kl - ql + i_last + 1 if causal else kl
+        qr = quad_rows(b, r, whole)
+        f_last = min(f0 // qr * qr + qr, ql * G) - 1 if qr else f0 + nr - 1
+        kv_end = kl - ql + f_last // G + 1 if causal else kl
         sl.sort()
         assert sl[0][0] == 0 and sl[-1][1] == kv_end
         for a, c in zip(sl, sl[1:]):
@@ -81,13 +91,24 @@ def check_coverage(items, b, causal=True):
         for h in kv_heads:
             for f in range(int(b.qo_lens[r]) * G):
                 assert seen_rows.get((r, h, f)) == 1, (r, h, f)
-    # a workgroup holds at most two cut pieces, its first and its last segment (the kernel
-    # keeps the fields of two pending pieces for the merge tickets)
+    # a workgroup holds at most two cut pieces, its first and its last (the kernel keeps the
+    # fields of two pending pieces for the merge tickets); the blocks of a quad piece are
+    # one piece
     groups = col("group")
     for g in np.unique(groups):
         mine = np.nonzero(groups == g)[0]
-        cut = [j for j, i in enumerate(mine) if items[i, idx["part_row"]] >= 0]
-        assert len(cut) <= 2 and all(j in (0, len(mine) - 1) for j in cut), (g, cut)
+        pieces, cut = [], set()
+        for i in mine:
+            it = items[i]
+            r = it[idx["request"]]
+            qr = quad_rows(b, r, whole)
+            key = (r, it[idx["kv_head"]], it[idx["tok_begin"]],
+                   it[idx["row_begin"]] // qr if qr else (-1, it[idx["row_begin"]]))
+            if not pieces or pieces[-1] != key:
+                pieces.append(key)
+            if it[idx["part_row"]] >= 0:
+                cut.add(len(pieces) - 1)
+        assert len(cut) <= 2 and all(j in (0, len(pieces) - 1) for j in cut), (g, cut, len(pieces))
     # the items carry the right request facts
     for it in items:
         r = it[idx["request"]]
@@ -113,9 +134,10 @@ def test_plan_covers_every_row_and_key_once(name, splits):
     b = SHAPES[name]()
     h = host_handle(Hq=b.num_qo_heads, Hkv=b.num_kv_heads, D=64, P=b.page_size, dtype=b.dtype)
     if name == "ragged_mixed_step" and splits == 1000:
-        # every 16-key tile its own slice: beyond the handle's item capacity, reported as such
-        assert "work items" in _expect(fl.FL_ERR_CAPACITY, plan_batch, h, b, num_splits=splits)
-        return
+        # in fp32 (no prefill quads) every 16-key tile of the chunk's 448 row blocks its own
+        # slice: beyond the handle's item capacity, reported as such
+        hf = host_handle(Hq=b.num_qo_heads, Hkv=b.num_kv_heads, D=64, P=b.page_size, dtype="f32")
+        assert "work items" in _expect(fl.FL_ERR_CAPACITY, plan_batch, hf, b, num_splits=splits)
     items = plan_batch(h, b, num_splits=splits)
     check_coverage(items, b)
     n, ng, ms, ws = h.info()
@@ -430,18 +452,27 @@ def test_append_on_empty_plan_and_host_handle():
 def test_neighbouring_shares_share_an_xcd():
     """Workgroup b runs on XCD b % 8: the plan hands runs of consecutive shares (neighbouring
     row blocks, which for a prefill chunk read the same K/V) to one XCD, in equal numbers."""
-    b = W.ragged_mixed_step()
-    h = host_handle(num_cus=256)
-    items = plan_batch(h, b)
-    idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
-    g = items[:, idx["group"]]
-    order = g[np.r_[True, g[1:] != g[:-1]]]          # workgroups in share order
-    n = h.info()[1]
-    assert sorted(order.tolist()) == list(range(n))   # a permutation of the workgroups
-    xcd = order % 8
-    assert (np.diff(xcd) >= 0).all()                  # XCD 0's run, then XCD 1's, ...
-    counts = np.bincount(xcd, minlength=8)
-    assert counts.max() - counts.min() <= 1
+    for b, dtype in ((W.ragged_mixed_step(), "bf16"), (W.ragged_mixed_step(), "f32")):
+        # bf16: the chunk in prefill quads (workgroups 0 .. Gp-1) and the decode blocks (the
+        # rest), each path in its own runs; fp32: one sequence of 16-row blocks
+        h = host_handle(num_cus=256, dtype=dtype)
+        items = plan_batch(h, b)
+        idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
+        g = items[:, idx["group"]]
+        first = np.r_[True, g[1:] != g[:-1]]
+        order = g[first]                                  # workgroups in share order
+        n = h.info()[1]
+        assert sorted(order.tolist()) == list(range(n))   # a permutation of the workgroups
+        prefill = (b.qo_lens[items[first, idx["request"]]] > 1) & (dtype != "f32")
+        gp = int(prefill.sum())
+        assert (order[prefill] < gp).all() and (order[~prefill] >= gp).all()
+        for part in (order[prefill], order[~prefill]):
+            if part.size == 0:
+                continue
+            xcd = part % 8
+            assert (np.diff(xcd) != 0).sum() <= 7        # one contiguous run per XCD
+            counts = np.bincount(xcd, minlength=8)
+            assert counts.max() - counts.min() <= 1
 
 
 # ---- launch shape: one launch per kind of step -----------------------------------------------
