@@ -1339,6 +1339,8 @@ __device__ __forceinline__ void quad_path(const int *rv, const AttnArgs &a, cons
     }
     // merge tickets of this wave's cut blocks: each wave draws its own blocks' tickets once
     // its partial rows are acknowledged; the piece that draws a block's last ticket merges it
+    // (the same ordering as the decode path's tickets; a wave writes and merges only its
+    // own blocks' rows, so its own wait suffices and no barrier is needed)
     if (npend > 0) {
         __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
@@ -1619,6 +1621,21 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     // acknowledgement before the workgroup draws its tickets with device-scope atomics (one
     // lane per piece, both in one instruction), so the piece that draws a row block's last
     // ticket finds every other piece complete.
+    // Ordering, in the terms of the CDNA3/CDNA4 ISA's scope bits (SC1 set, SC0 clear:
+    // device scope) and of LLVM's AMDGPU memory model for gfx942/gfx950:
+    //   1. a device-scope store writes through this XCD's L2 to the coherence point all
+    //      XCDs share, and is acknowledged (vmcnt, which counts stores on this target) only
+    //      once it is there; s_waitcnt(0) then the barrier: every wave's rows are there;
+    //   2. the ticket is an agent-scope atomic, performed at that same point; atomics on one
+    //      address are totally ordered, so the last ticket is drawn after every other
+    //      piece's increment, each made after that piece's acknowledged stores;
+    //   3. the merging piece reads the partial rows with device-scope loads, which do not
+    //      take lines from its own L2, and issues them only after its atomic returned (the
+    //      loads depend on the returned value).
+    // This is the agent-scope release/acquire code sequence of that memory model without
+    // its L2 write-back and invalidate steps, which only order non-device-scope accesses:
+    // every access another workgroup reads here is device scope. A whole-cache write-back
+    // and invalidate (the fence form) measured 5-7x slower on split workloads.
     if (npend > 0) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
