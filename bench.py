@@ -43,10 +43,38 @@ KERNEL_SRC = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "csrc", "attn_kernels.h
 PLAN_SRC = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "csrc", "plan.cpp")
 
 
+def code_text(path: str) -> str:
+    """The source's code without its comments and blank lines (C and C++ comments; string
+    and character literals kept as written), so that a comment edit leaves the hash of the
+    kernel and planner sources unchanged."""
+    src = open(path, encoding="utf-8").read()
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":  # a literal: copy through its closing quote
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (l.rstrip() for l in "".join(out).splitlines())
+    return "\n".join(l for l in lines if l)
+
+
 def source_hash() -> str:
+    """Hash of the attention kernel's and the planner's code (comments excluded)."""
     h = hashlib.sha256()
     for p in (KERNEL_SRC, PLAN_SRC):
-        h.update(open(p, "rb").read())
+        h.update(code_text(p).encode())
     return h.hexdigest()[:16]
 
 

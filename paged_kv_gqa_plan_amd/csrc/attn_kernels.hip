@@ -1022,12 +1022,12 @@ __device__ __forceinline__ void stage_rows(const lds_char *dst, const int32_t *r
 }
 
 // ---------------------------------------------------------------------------------------
-// prefill units (16-bit types): the rows of a prefill chunk in units of up to eight 16-row
-// blocks of one request and kv head, two blocks per wave, over 64-key steps. The four
-// waves load a step's four 16-key tiles (one each, the HalfTile ring format) into one LDS
-// buffer and all read all four, so a unit streams its keys once for 128 flattened rows and
-// each wave reads each K piece and V column once for both of its blocks; a ring of
-// kQuadBufs buffers keeps the next two steps' loads in flight during a step's arithmetic.
+// prefill units (16-bit types): the rows of a prefill chunk in units of up to kQuadBlocks
+// (four) 16-row blocks of one request and kv head, kWaveBlocks (one) per wave, over 64-key
+// steps. The four waves load a step's four 16-key tiles (one each, the HalfTile ring
+// format) into one LDS buffer and all read all four, so a unit streams its keys once for
+// its 64 flattened rows; a ring of kQuadBufs buffers keeps the next two steps' loads in
+// flight during a step's arithmetic.
 // Per step and block: S^T = K Q^T over the four tiles (MFMA 16x16x32), one online-softmax
 // update for all 64 keys, and O^T += V^T P^T as two 32-key contractions (16x16x32): the
 // contraction runs over keys in any order, so 32-key operand k index 8g + j takes key
@@ -1035,7 +1035,7 @@ __device__ __forceinline__ void stage_rows(const lds_char *dst, const int32_t *r
 // the S^T accumulators of the two tiles hold P and how the transpose reads return V.
 // ---------------------------------------------------------------------------------------
 constexpr int kQuadBufs = 3;
-constexpr int kWaveBlocks = kQuadBlocks / kMaxWaves;  // row blocks each wave computes (2)
+constexpr int kWaveBlocks = kQuadBlocks / kMaxWaves;  // row blocks each wave computes (1)
 
 template <int D>
 struct QuadLds {
