@@ -41,6 +41,7 @@ LAYERS = {"tiny_decode": 24, "saturated_decode": 24, "ragged_mixed_step": 24,
           "mixed_length_decode": 28, "long_context_skew": 28, "multi_chunk_step": 24}
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "csrc", "attn_kernels.hip")
 PLAN_SRC = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "csrc", "plan.cpp")
+INTERNAL_H = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "csrc", "fl_internal.h")  # planner costs, layouts
 
 
 def code_text(path: str) -> str:
@@ -71,9 +72,10 @@ def code_text(path: str) -> str:
 
 
 def source_hash() -> str:
-    """Hash of the attention kernel's and the planner's code (comments excluded)."""
+    """Hash of the attention kernel's and the planner's code and of their shared header
+    (comments excluded)."""
     h = hashlib.sha256()
-    for p in (KERNEL_SRC, PLAN_SRC):
+    for p in (KERNEL_SRC, PLAN_SRC, INTERNAL_H):
         h.update(code_text(p).encode())
     return h.hexdigest()[:16]
 

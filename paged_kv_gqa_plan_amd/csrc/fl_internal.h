@@ -82,16 +82,18 @@ constexpr int kQuadBlocks = FL_QUAD_BLOCKS;
 constexpr int kQuadStepTiles = 4;
 constexpr int kQuadStepTokens = kQuadStepTiles * 16;
 #ifndef FL_QUAD_STEP_COST
-#define FL_QUAD_STEP_COST 500
+#define FL_QUAD_STEP_COST 450
 #endif
 #ifndef FL_QUAD_SEG_COST
 #define FL_QUAD_SEG_COST 400
 #endif
 // A unit cut by a share boundary costs its pieces a round trip each for the partial rows
-// and the ticket, and one more for the merge: charged 1500 (ragged mixed step 17.7-18.1 us
-// against 19.7-20.4 at 200-600 and 19.4-22 at 2500-4000; four-chunk step 17.0-17.1 us).
+// and the ticket, and one more for the merge. Step 450 and cut 1100, chosen by a sweep of
+// both (four runs on two boxes): ragged mixed step 17.3-17.6 us and four-chunk step
+// 16.4-16.6 us, against 17.6-19.0 and 16.7-16.9 at 500 and 1500; cuts of 200-600 or
+// 2500-4000 measured 19.4-22 us.
 #ifndef FL_QUAD_CUT_COST
-#define FL_QUAD_CUT_COST 1500
+#define FL_QUAD_CUT_COST 1100
 #endif
 constexpr int64_t kQuadStepCost = FL_QUAD_STEP_COST;
 constexpr int64_t kQuadSegCost = FL_QUAD_SEG_COST;
