@@ -1669,6 +1669,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
         };
         const bool both = npend == 2 && lds_int((const lds_char *)&sm.last[0]) &&
                           lds_int((const lds_char *)&sm.last[1]);
+        // A block's merge takes its pieces kMbWide (more than eight rows) or kMbNarrow (up to
+        // eight) at a time whichever way the workgroup's threads are split over its rows: the
+        // batches fix the order of the arithmetic, so a block's rows come out bit for bit
+        // the same whichever workgroup merges it. (fp32 rows take half as many per batch:
+        // twice the registers per piece.)
+        constexpr int kMbWide = DT == FL_F32 ? 4 : 8, kMbNarrow = 2 * kMbWide;
         if (both) {
             // both pieces merge here: each half of the workgroup (two waves) takes one, so
             // the two merges' loads are in flight together instead of one after the other
@@ -1679,10 +1685,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
             if (ps.num_rows > kBlockRows / 2) {
                 constexpr int TPRH = TPR / 2;
                 const int r = u / TPRH;
-                if (r < ps.num_rows) merge_pieces<DT, D, TPRH, 4, WR>(ps, a, r, u % TPRH);
+                if (r < ps.num_rows) merge_pieces<DT, D, TPRH, kMbWide, WR>(ps, a, r, u % TPRH);
             } else {
                 const int r = u / TPR;
-                if (r < ps.num_rows) merge_pieces<DT, D, TPR, 8, WR>(ps, a, r, u % TPR);
+                if (r < ps.num_rows) merge_pieces<DT, D, TPR, kMbNarrow, WR>(ps, a, r, u % TPR);
             }
         } else {
 #pragma unroll
@@ -1691,11 +1697,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
                 const Seg ps = pend_seg(i);
                 if (ps.num_rows > kBlockRows / 2) {
                     const int r = threadIdx.x / TPR;
-                    if (r < ps.num_rows) merge_pieces<DT, D, TPR, 8, WR>(ps, a, r, threadIdx.x % TPR);
-                } else {  // up to 8 rows: twice the threads per row, up to 16 pieces per batch
+                    if (r < ps.num_rows) merge_pieces<DT, D, TPR, kMbWide, WR>(ps, a, r, threadIdx.x % TPR);
+                } else {  // up to 8 rows: twice the threads per row, twice the pieces per batch
                     constexpr int TPR2 = 2 * TPR;
                     const int r2 = threadIdx.x / TPR2;
-                    if (r2 < ps.num_rows) merge_pieces<DT, D, TPR2, 16, WR>(ps, a, r2, threadIdx.x % TPR2);
+                    if (r2 < ps.num_rows)
+                        merge_pieces<DT, D, TPR2, kMbNarrow, WR>(ps, a, r2, threadIdx.x % TPR2);
                 }
             }
         }
