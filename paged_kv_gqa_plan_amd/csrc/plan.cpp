@@ -439,8 +439,9 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
     out.segs.assign((size_t)nslots * FL_WORK_ITEM_INTS, 0);
     out.wg_rec.assign(G_wg * kRecInts, 0);
     out.step_rows.assign((size_t)total, 0);
-    // Workgroup b runs on XCD b % kXcds (workgroups are handed to the XCDs in turn), and
-    // each XCD has its own L2. Shares next to each other in a sequence hold neighbouring row
+    // Workgroups b and b + kXcds run on one XCD (the XCDs take a launch's workgroups in turn:
+    // XCD (b + c) % kXcds, c fixed within a launch), and each XCD has its own L2. Shares next
+    // to each other in a sequence hold neighbouring row
     // blocks, which for a prefill chunk read the same K/V, so share s of a path with n shares
     // (starting at workgroup `first`) goes to the workgroup that puts runs of consecutive
     // shares on one XCD: the first ceil(n / kXcds) shares on one XCD, the next on the next.

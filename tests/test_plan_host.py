@@ -450,7 +450,7 @@ def test_append_on_empty_plan_and_host_handle():
 
 
 def test_neighbouring_shares_share_an_xcd():
-    """Workgroup b runs on XCD b % 8: the plan hands runs of consecutive shares (neighbouring
+    """Workgroups b and b + 8 run on one XCD: the plan hands runs of consecutive shares (neighbouring
     row blocks, which for a prefill chunk read the same K/V) to one XCD, in equal numbers."""
     for b, dtype in ((W.ragged_mixed_step(), "bf16"), (W.ragged_mixed_step(), "f32")):
         # bf16: the chunk in prefill quads (workgroups 0 .. Gp-1) and the decode blocks (the
