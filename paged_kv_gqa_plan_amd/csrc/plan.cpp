@@ -59,7 +59,18 @@ int64_t row_block_bound(const PlanLimits &lim) {
 }
 
 fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std::string *err) {
-    out = Plan();
+    {  // a fresh plan that keeps the previous one's vector storage (a plan per step)
+        Plan fresh;
+        std::vector<int32_t> *keep[] = {&out.segs, &out.wg_rec, &out.step_rows, &out.append_rows,
+                                        &out.append_pos};
+        std::vector<int32_t> *into[] = {&fresh.segs, &fresh.wg_rec, &fresh.step_rows, &fresh.append_rows,
+                                        &fresh.append_pos};
+        for (int i = 0; i < 5; ++i) {
+            keep[i]->clear();
+            into[i]->swap(*keep[i]);
+        }
+        out = std::move(fresh);
+    }
     const int32_t B = in.batch;
     const int32_t P = lim.page_size;
     const int32_t Hkv_real = lim.num_kv_heads;
@@ -214,7 +225,7 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
             odd_pct[h] = 100 * odd / (slice / 16);
         }
     // Prefill units: in a 16-bit type, a request with more than one row block per kv head (a
-    // prefill chunk) runs in units of up to kQuadBlocks consecutive blocks (two per wave)
+    // prefill chunk) runs in units of up to kQuadBlocks consecutive blocks (one per wave)
     // over 64-key steps whose K/V the waves share through LDS. Every block of a unit spans
     // the unit's keys (the keys of its last row); the kernel masks each row at its own
     // causal limit.
@@ -306,7 +317,7 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         const int64_t kFoldCost = prefill ? kFoldCostMixed : out.whole_rows ? kFoldCostWhole : kFoldCostDecode;
         const int64_t kCutCost = prefill ? kCutCostMixed : out.whole_rows ? kCutCostWhole : kCutCostDecode;
         const int64_t want = (int64_t)lim.num_cus * gpc;
-        const int64_t U = (int64_t)lim.waves * kRingDepth;
+        constexpr int64_t U = (int64_t)kMaxWaves * kRingDepth;  // tiles of one ring group
         auto dcost = [&](int64_t b, int64_t n, bool cut) {
             return blocks[b].tile_cost * U * ceil_div(n, U) + kFoldCost + (cut ? kCutCost : 0);
         };
@@ -328,7 +339,9 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         Gp_max = std::min(Gp_max, QS);
         Gd_max = std::min(std::max<int64_t>(dblocks.empty() ? 0 : 1, std::min(Gd_max, ceil_div(T, lim.min_group_tiles))), T);
         // walk the units filling shares of budget C; emit pieces (group = first_group +
-        // share) when `emit` is set. cost(u, n, cut); unit sizes n_of(u); step granularity.
+        // share) when `emit` is set. cost(u, n, cut); unit sizes n_of(u); step granularity;
+        // whole[i]: cost of the whole of units[i] (the common case, computed once).
+        std::vector<int64_t> whole;
         auto fill = [&](const std::vector<int64_t> &units, auto n_of, auto cost, int64_t gran, bool is_quad,
                         int64_t C, int64_t first_group, bool emit) {
             int64_t shares = 0, i = 0, pos = 0;
@@ -338,9 +351,10 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
                 while (i < nu) {
                     const int64_t u = units[i];
                     const int64_t r = n_of(u) - pos;
-                    if (cost(u, r, pos > 0) <= budget) {
+                    const int64_t c = pos == 0 ? whole[i] : cost(u, r, true);
+                    if (c <= budget) {
                         if (emit) pieces.push_back({is_quad, u, pos, n_of(u), first_group + shares});
-                        budget -= cost(u, r, pos > 0);
+                        budget -= c;
                         ++i;
                         pos = 0;
                         continue;
@@ -363,8 +377,19 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
                            int64_t G_max, int64_t least, int64_t first_group) {
             if (units.empty() || G_max <= 0) return (int64_t)0;
             int64_t total = 0;
-            for (int64_t u : units) total += cost(u, n_of(u), false);
+            whole.resize(units.size());
+            for (size_t i = 0; i < units.size(); ++i) total += whole[i] = cost(units[i], n_of(units[i]), false);
+            // The share count only falls as the budget grows. The smallest budget that fits
+            // lies within a few fixed charges of the even split: bracket it by doubling a step
+            // from there (a budget of `total` always fits), then bisect.
             int64_t lo = std::max<int64_t>(least, ceil_div(total, G_max)), hi = std::max(total, least);
+            for (int64_t d = least; lo + d < hi; d *= 2) {
+                if (fill(units, n_of, cost, gran, is_quad, lo + d, first_group, false) <= G_max) {
+                    hi = lo + d;
+                    break;
+                }
+                lo = lo + d + 1;  // lo + d does not fit, nor does anything below it
+            }
             while (lo < hi) {  // every budget >= least makes progress
                 const int64_t mid = lo + (hi - lo) / 2;
                 if (fill(units, n_of, cost, gran, is_quad, mid, first_group, false) <= G_max)
@@ -420,7 +445,7 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
     // ring depth, the same in all waves. Padding steps repeat a real tile of the segment
     // (never scored). Quad pieces: kQuadBlocks segment slots each (slots past the quad's
     // blocks hold num_rows 0), and per 64-key step the pool rows of its four 16-key tiles.
-    const int NW = lim.waves;
+    constexpr int NW = kMaxWaves;
     int64_t total = 0;
     std::vector<int64_t> seg_steps(pieces.size());
     for (size_t k = 0; k < pieces.size(); ++k) {
@@ -475,9 +500,10 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         it[FL_WI_GROUP] = (int32_t)wg;
         it[FL_WI_POS_BEGIN] = (int32_t)pos;
     };
+    const int lp = __builtin_ctz((unsigned)P);  // the page size is a power of two
     auto pool_row = [&](const Block &bl, int64_t t) {
         const int32_t *pages = in.kv_indices + in.kv_indptr[bl.req];
-        return (int32_t)(((int64_t)pages[t / P] * P + t % P) * Hkv + bl.kvh);
+        return (int32_t)((((int64_t)pages[t >> lp] << lp) + (t & (P - 1))) * Hkv + bl.kvh);
     };
     size_t k = 0;
     int64_t slot = 0, off = 0;
