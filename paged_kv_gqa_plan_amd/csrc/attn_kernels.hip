@@ -150,6 +150,20 @@ __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// The same for a wave-uniform count n in [LO, HI] known only at run time (a binary search
+// over the immediate forms).
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_in(int n) {
+    if constexpr (LO == HI) {
+        wait_vm<LO>();
+    } else {
+        constexpr int MID = (LO + HI) / 2;
+        if (n <= MID)
+            wait_vm_in<LO, MID>(n);
+        else
+            wait_vm_in<MID + 1, HI>(n);
+    }
+}
 // Wait until this wave's LDS reads have returned (before a slot is refilled).
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -1480,7 +1494,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
     }
     const int seg_b = rv[REC_SEG_BEGIN], seg_e = rv[REC_SEG_END];
     const int pos0 = rv[REC_POS];
-    const int nsteps = rv[REC_STEPS];  // steps per wave (a positive multiple of PF)
+    const int nsteps = rv[REC_STEPS];  // steps per wave (at least PF)
     int seg_end = rv[REC_FIRST_END];
     int row_first[PF];  // this wave's (a select over the waves' entries, all in SGPRs)
 #pragma unroll
@@ -1536,15 +1550,23 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
 
     // ---- the step stream: PF tiles of K and V in flight per wave -------------------------
     // Every slot of the ring is in flight until its step (padding steps re-read a real tile
-    // and are never scored). Loads complete in issue order, so at slot s at most PF - 1
-    // later tiles are outstanding behind it, and at a group's top everything issued before
-    // the previous group's refills has landed (headers, Q, row windows included).
+    // and are never scored). Segments start on multiples of PF steps; only the last one may
+    // end between them, so the last group holds e = nsteps - p0 <= PF steps and the one
+    // before it refills only those e slots. Loads complete in issue order, so at slot s of a
+    // group at most PF - 1 later tiles are outstanding behind it (fewer in those two groups:
+    // PF - 1 - s + min(s, e) in the one before the last, e - 1 - s in the last), and at a
+    // group's top everything issued before the previous group's refills has landed
+    // (headers, Q, row windows included).
     int win = 0;  // window of the last refill
-    // One group of PF steps. The last group issues no refills, so nothing is in flight when
-    // the final fold starts.
-    auto group = [&](int p0, auto refill) {
+    // One group of PF steps (e of them real in the last group, e refills in the one before
+    // it, PF elsewhere). The last group issues no refills, so nothing is in flight when the
+    // final fold starts.
+    auto group = [&](int p0, auto refill, int e) {
         constexpr bool kRefill = decltype(refill)::value;
-        wait_vm<PF * kLoads>();
+        if (kRefill || e == PF)
+            wait_vm<PF * kLoads>();
+        else
+            wait_vm_in<kLoads, PF * kLoads>(e * kLoads);
         if (p0 == seg_end) {  // the same step in every wave: segment k is done
             if constexpr (FUSE)
                 if (app_row >= 0) write_new_rows<D>(new_slot(k), a, cs, app_row, hkv, lane);
@@ -1568,22 +1590,29 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
             T::template q_stage<WR>(q_b, a, ns, lane);
             if constexpr (FUSE) stage_new_rows<D>(new_slot(k + 1), a, ns, hkv, lane);
         }
-        int nrow[PF];  // pool rows of this group's refills
+        int nrow[PF];  // pool rows of this group's refills (entries past nsteps unused)
         if constexpr (kRefill) {
 #pragma unroll
             for (int s = 0; s < PF; ++s) {
-                const int q = p0 + PF + s;  // < nsteps
+                const int q = p0 + PF + s;
                 nrow[s] = lds_int(rows_b + 256 * ((q >> 6) & 1) + 4 * (q & 63));
             }
         }
         static_for<0, PF>([&](auto si) {
             constexpr int s = decltype(si)::value;
+            if (!kRefill && s > 0 && s >= e) return;  // past the share's last step
             const int p = p0 + s;
             const int j = (p - cs.pos_begin) * NW + wv;  // tile of the segment (wave-uniform)
-            T::template ring_arrive<kRefill ? PF - 1 : PF - 1 - s>(ring, s);
+            constexpr int kLater = kRefill ? PF - 1 : PF - 1 - s;
+            if ((!kRefill || s > 0) && e != PF) {  // fewer tiles behind: wait for the exact count
+                const int later = kRefill ? PF - 1 - s + min(s, e) : e - 1 - s;
+                wait_vm_in<0, kLater * kLoads>(later * kLoads);
+            }
+            T::template ring_arrive<kLater>(ring, s);
             auto refill = [&] {
                 if constexpr (kRefill) {
                     const int q = p + PF;
+                    if (s > 0 && s >= e) return;  // past the share's last step
                     T::ring_release();
                     if ((q >> 6) != win) {  // first refill in window q/64: fetch the next window
                         win = q >> 6;
@@ -1610,8 +1639,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const int32_t *wg_rec, co
         });
     };
     int p0 = 0;
-    for (; p0 + PF < nsteps; p0 += PF) group(p0, std::true_type{});
-    group(p0, std::false_type{});
+    for (; p0 + PF < nsteps; p0 += PF) group(p0, std::true_type{}, min(PF, nsteps - p0 - PF));
+    group(p0, std::false_type{}, nsteps - p0);
     if constexpr (FUSE)
         if (app_row >= 0) write_new_rows<D>(new_slot(k), a, cs, app_row, hkv, lane);
     fold_segment<T, DT, D, NW, WR, true, EARLY>(sm, a, cs, k, m_run, l_run, o, npend, wave, col, grp);

@@ -310,7 +310,8 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         // time. A decode piece of n tiles costs the ring steps it occupies in all waves (n
         // rounded up to whole step groups, at its block's tile cost) plus a fixed charge for
         // its fold; a block cut inside a share is cut at a multiple of a step group, so only
-        // a block's last piece carries padding. A quad piece of n steps costs n steps plus
+        // a block's last piece carries padding (a share's last piece is emitted with whole
+        // steps only, which the estimate does not count on). A quad piece of n steps costs n steps plus
         // its finish. The smallest per-share budget that needs at most the given number of
         // shares is found by bisection. The grid's workgroups are divided between the two
         // paths in proportion to their estimated totals.
@@ -441,10 +442,11 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
 
     // ---- emit segments, workgroup tables and step rows ----------------------------------
     // Decode pieces: one segment each; within it tile j goes to wave j % NW as that wave's
-    // step j / NW; every segment's per-wave step count is rounded up to a multiple of the
-    // ring depth, the same in all waves. Padding steps repeat a real tile of the segment
-    // (never scored). Quad pieces: kQuadBlocks segment slots each (slots past the quad's
-    // blocks hold num_rows 0), and per 64-key step the pool rows of its four 16-key tiles.
+    // step j / NW; every segment's per-wave step count but a share's last is rounded up to a
+    // multiple of the ring depth, the same in all waves (every share has at least one
+    // ring group of steps). Padding steps repeat a real tile of the segment (never scored).
+    // Quad pieces: kQuadBlocks segment slots each (slots past the quad's blocks hold
+    // num_rows 0), and per 64-key step the pool rows of its four 16-key tiles.
     constexpr int NW = kMaxWaves;
     int64_t total = 0;
     std::vector<int64_t> seg_steps(pieces.size());
@@ -454,7 +456,12 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
             seg_steps[k] = n;
             total += n * kQuadStepTiles;
         } else {
-            seg_steps[k] = ceil_div(ceil_div(n, NW), kRingDepth) * kRingDepth;
+            // a share's last segment needs no padding to whole ring groups (the kernel's
+            // last group may be short), only every share at least one group in all
+            const bool last = k + 1 == pieces.size() || pieces[k + 1].group != pieces[k].group;
+            const bool first = k == 0 || pieces[k - 1].group != pieces[k].group;
+            seg_steps[k] = last ? std::max<int64_t>(ceil_div(n, NW), first ? kRingDepth : 1)
+                                : ceil_div(ceil_div(n, NW), kRingDepth) * kRingDepth;
             total += seg_steps[k] * NW;
         }
     }
