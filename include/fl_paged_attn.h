@@ -252,12 +252,14 @@ fl_status fl_paged_kv_append_rope(fl_handle h, void *q, const void *k_new, const
  * Append one layer's new K/V rows and compute that layer's attention in one call: the
  * result equals fl_paged_kv_append followed by fl_paged_attn_run (same pointers, same
  * plan), up to the floating-point summation order. On decode-only plans (every request has
- * at most one query row) in a 16-bit type it is one kernel launch: the new token is the
+ * at most one query row) in a 16-bit type with at most 16 query heads per kv head it is
+ * one kernel launch: the new token is the
  * newest key of its request, so the workgroup whose tiles hold that key takes its K and V
  * from k_new / v_new instead of the pool and also writes them to the pool for later steps
  * (flashlet README, design bullets: the NHD pool is written in place before attention reads
  * it; one launch less per layer). Other plans (prefill chunks, whose new keys many
- * workgroups read; fp32) make the two launches in order.
+ * workgroups read; decode rows of more than 16 query heads per kv head, which run as
+ * prefill units; fp32) make the two launches in order.
  * Device pointers as for fl_paged_kv_append and fl_paged_attn_run; all 16-byte aligned.
  * Errors: those of the two calls (FL_ERR_INVALID_ARG when the plan has no valid append
  * slots). Enqueues on `stream`; never synchronises or allocates (graph-capturable: the
@@ -287,8 +289,9 @@ fl_status fl_paged_attn_plan_info(fl_handle h, int32_t *num_work_items, int32_t 
  * The launch the current plan needs (works on host-only handles, which plan as the device
  * would): *launch_class names the kernel variant and grid of fl_paged_attn_run, and
  * *fused_class those of the one-launch fl_paged_attn_run_append (0 when the plan takes two
- * launches there: prefill rows, fp32, or no valid append slots); *grid is the number of
- * workgroups launched and *busy_groups how many of them have work (the rest exit at once).
+ * launches there: prefill rows, more than 16 query heads per kv head, fp32, or no valid
+ * append slots); *grid is the number of workgroups launched and *busy_groups how many of
+ * them have work (the rest exit at once).
  * Plans with equal classes launch identically, so a graph captured under one replays
  * correctly under the other. Outputs may be NULL. FL_ERR_NOT_PLANNED without a plan.
  */

@@ -187,7 +187,10 @@ LaunchDesc launch_desc(const fl_paged_attn *h, const Plan &p) {
     d.early = h->cfg.dtype != FL_F32 && (d.head_dim >= 128 || p.groups_per_cu == 1);
     d.grid = p.forced ? std::max<int32_t>(1, p.num_groups) : h->lim.num_cus * p.groups_per_cu;
     d.cls = (d.grid << 3) | (d.early << 2) | (d.wr << 1) | 1;
-    if (p.decode_only && h->cfg.dtype != FL_F32 && p.append_ok)
+    // the one-launch append: decode-only plans in a 16-bit type whose rows run no prefill
+    // unit (its kernel has no unit path), i.e. at most 16 query heads per kv head (above
+    // that a decode row spans two 16-row blocks, which run as a unit)
+    if (p.decode_only && h->cfg.dtype != FL_F32 && p.append_ok && h->group <= fl::kBlockRows && !p.units)
         d.fcls = (1 << 30) | (d.grid << 3) | (1 << 2) | (d.wr << 1) | 1;
     return d;
 }

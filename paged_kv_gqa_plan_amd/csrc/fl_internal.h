@@ -189,6 +189,7 @@ struct Plan {
     bool whole_rows = false;        // blocks hold every query head of a request and read whole
                                     // token rows (one virtual kv head of Hkv * D values)
     bool decode_only = false;       // every request has at most one query row
+    bool units = false;             // the plan holds prefill units (16-bit, > 16 flattened rows)
     bool forced = false;            // num_splits > 0: one workgroup per piece, grid = num_groups
     int32_t max_splits = 0;
     int64_t part_rows = 0;

@@ -276,6 +276,7 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
         T += tiles[b];
     }
     const int64_t nquads = (int64_t)quads.size();
+    out.units = nquads > 0;
     std::vector<int64_t> qsteps(nquads);
     int64_t QS = 0;
     for (int64_t q = 0; q < nquads; ++q) {

@@ -216,7 +216,7 @@ def test_run_append_modes_and_pieces(whole_rows, splits, dtype):
                       whole_rows=whole_rows)
 
 
-@pytest.mark.parametrize("case", ["ragged", "f32", "d128-p256"])
+@pytest.mark.parametrize("case", ["ragged", "f32", "d128-p256", "g32"])
 def test_run_append_other_plans(case):
     kw = dict(num_qo_heads=14, num_kv_heads=2, head_dim=64, page_size=16, dtype="bf16")
     kv, qo = [80, 17, 300, 33], None
@@ -224,11 +224,14 @@ def test_run_append_other_plans(case):
         qo = [37, 1, 1, 5]
     elif case == "f32":
         kw["dtype"] = "f32"
+    elif case == "g32":       # decode rows of 32 heads per kv head run as prefill units
+        kw.update(num_qo_heads=32, num_kv_heads=1)
     else:                     # fused at head_dim 128, 256-slot pages
         kw.update(num_qo_heads=12, head_dim=128, page_size=256, dtype="f16")
         kv = [1, 256, 257, 700]
     b = W.make_batch(kv, qo, seed=92, num_pages=40, keep_dense=True, **kw)
-    _run_append_check(b, f"run_append {case}")
+    h = _run_append_check(b, f"run_append {case}")
+    assert (h.launch()[1] != 0) == (case == "d128-p256")  # the one-launch form
 
 
 @pytest.mark.parametrize("whole_rows", [1, -1])

@@ -572,6 +572,28 @@ def test_decode_class_changes_only_where_whole_rows_switch_on():
     assert classes[256] == classes[300] == classes[512] != classes[255]
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(32, 1), (17, 1), (16, 1), (12, 2)])
+def test_decode_rows_of_more_than_16_heads_run_as_units_and_never_fused(Hq, Hkv):
+    """A decode row of more than 16 query heads per kv head spans two 16-row blocks, which
+    run as a prefill unit: such a handle's decode steps never take the one-launch append,
+    whose kernel has no unit path. At head_dim 128 decode and prefill steps share one
+    launch class."""
+    G = Hq // Hkv
+    h = host_handle(Hq=Hq, Hkv=Hkv, D=128, P=16, dtype="f16", max_rows=256)
+    idx = {n: i for i, n in enumerate(fl.WORK_ITEM_FIELDS)}
+    rng = np.random.default_rng(14)
+    qo, kp, ki, last, pool = _meta([100, 40, 300], [1, 1, 1], 16, rng)
+    h.plan(qo, kp, ki, last, pool)
+    items = h.work_items()
+    assert (items[:, idx["row_begin"]] > 0).any() == (G > 16)  # a second block per row
+    cls, fcls, grid, busy = h.launch()
+    assert (fcls == 0) == (G > 16)
+    qo, kp, ki, last, pool = _meta([100, 40, 300], [1, 9, 1], 16, rng)
+    h.plan(qo, kp, ki, last, pool)
+    c2, f2, g2, _ = h.launch()
+    assert f2 == 0 and g2 == grid and c2 == cls
+
+
 def test_forced_splits_launch_one_workgroup_per_piece():
     b = W.tiny_decode()
     h = host_handle()
