@@ -101,6 +101,7 @@ VARIANTS = [
     dict(dtype="bf16", D=64, P=16, Hq=2, Hkv=2),      # G = 1
     dict(dtype="f16", D=128, P=128, Hq=16, Hkv=1),    # G = 16: a full 16-row block
     dict(dtype="bf16", D=64, P=16, Hq=32, Hkv=1),     # G = 32: two row blocks per decode row
+    dict(dtype="f16", D=128, P=32, Hq=24, Hkv=1),     # G = 24: a full block and one of 8 rows
     dict(dtype="f32", D=64, P=64, Hq=8, Hkv=8),       # MHA
 ]
 
@@ -125,7 +126,7 @@ def _random_case(seed):
     dtype = ["bf16", "f16", "f32"][r.integers(3)]
     D = [64, 128][r.integers(2)]
     P = [16, 32, 64, 128, 256][r.integers(5)]
-    Hq, Hkv = [(14, 2), (12, 2), (8, 1), (4, 4), (32, 4), (6, 3)][r.integers(6)]
+    Hq, Hkv = [(14, 2), (12, 2), (8, 1), (4, 4), (32, 4), (6, 3), (24, 1)][r.integers(7)]
     B = int(r.integers(1, 25))
     kinds = r.integers(4, size=B)
     kv = np.where(kinds == 0, r.integers(1, 40, size=B),
