@@ -20,8 +20,9 @@ constexpr int kTileTokens = 16;
 // Flattened query rows (query row * G + head in group) per row block: the 16-column N
 // dimension of the same instructions.
 constexpr int kBlockRows = 16;
-// Tiles of K and V each wave keeps in flight. Every segment's per-wave step count is a
-// multiple of it, so segment boundaries fall on the same loop step in every wave.
+// Tiles of K and V each wave keeps in flight. Every segment's per-wave step count but a
+// share's last is a multiple of it, so segment boundaries fall on the same loop step in
+// every wave, the first of a ring group; every share has at least that many steps.
 #ifndef FL_RING_DEPTH
 #define FL_RING_DEPTH 2
 #endif

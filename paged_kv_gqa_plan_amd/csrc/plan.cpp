@@ -18,8 +18,9 @@
 //     A block cut by a share boundary becomes several pieces whose partial results are
 //     merged by log-sum-exp; only the first and last piece of a share can be partial.
 //   * Within a share's segment, tile j runs on wave j % NW as that wave's step j / NW, and
-//     each segment's per-wave step count is padded to a multiple of the ring depth, so
-//     segment boundaries fall on the same step in every wave. For each wave and step the
+//     each segment's per-wave step count but the share's last is padded to a multiple of
+//     the ring depth, so segment boundaries fall on the same step in every wave and on a
+//     ring group's first step. For each wave and step the
 //     plan records the pool row of the tile's first key, (page * P + slot) * Hkv + kv_head,
 //     so the kernel addresses K and V without reading the page table.
 //   * The plan depends on the lengths only; page ids enter only the recorded pool rows.
