@@ -303,10 +303,12 @@ def _counter_per_dispatch(dir_, name_has: str, counter: str):
 
 
 def summarize_profiles(workload: str, kt: str, pf: str, pw: str, cf: str, cw: str, calib_mib: int,
-                       commands: str):
+                       commands: str, steps: int, layers: int):
     """Write profiles/attn_kernel_<workload>.md and profiles/traffic_<workload>.txt from
     rocprofv3 CSV output: a kernel-trace run (kt) and FETCH_SIZE / WRITE_SIZE passes of the
-    benchmark (pf, pw) and of a plain copy of known size (cf, cw)."""
+    benchmark (pf, pw) and of a plain copy of known size (cf, cw). steps: the timed steps of
+    the profiled benchmark command; its last steps * layers attention dispatches are also
+    averaged on their own (the earlier ones are warmup steps and first, cold launches)."""
     import glob
     stats = None
     others = []
@@ -318,6 +320,13 @@ def summarize_profiles(workload: str, kt: str, pf: str, pw: str, cf: str, cw: st
                 others.append(r)
     if stats is None:
         raise SystemExit(f"no attention kernel in the kernel stats under {kt}")
+    durs = []
+    for path in glob.glob(os.path.join(kt, "**", "*kernel_trace.csv"), recursive=True):
+        rows = [r for r in _csv_rows(path) if "attn_kernel" in r["Kernel_Name"]]
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        durs += [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    layers = layers or LAYERS[workload]
+    timed = durs[-steps * layers:] if steps > 0 and len(durs) >= steps * layers else []
     fetch, nf = _counter_per_dispatch(pf, "attn_kernel", "FETCH_SIZE")
     write, nw = _counter_per_dispatch(pw, "attn_kernel", "WRITE_SIZE")
     cfetch, _ = _counter_per_dispatch(cf, "copyBuffer", "FETCH_SIZE")
@@ -336,6 +345,15 @@ def summarize_profiles(workload: str, kt: str, pf: str, pw: str, cf: str, cw: st
          "calibration": f"plain device copy of {calib_mib} MiB: FETCH_SIZE {cfetch:.1f} KiB, "
                         f"WRITE_SIZE {cwrite:.1f} KiB per dispatch",
          "kernel_avg_us": avg_ns / 1e3, "algorithmic_kv_bytes": algo}
+    timed_line = []
+    if timed:
+        d["kernel_timed_avg_us"] = sum(timed) / len(timed)
+        d["kernel_timed_median_us"] = sorted(timed)[len(timed) // 2]
+        d["kernel_timed_dispatches"] = len(timed)
+        timed_line = [f"The last {len(timed)} attention dispatches ({steps} timed steps x {layers} "
+                      f"layers, from the per-dispatch trace): average {d['kernel_timed_avg_us']:.3f} us, "
+                      f"median {d['kernel_timed_median_us']:.3f} us. The average in the table also holds "
+                      f"the warmup steps and the first, cold launches.", ""]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.txt"), "w") as f:
         f.write(json.dumps(d, indent=1) + "\n")
@@ -351,7 +369,7 @@ def summarize_profiles(workload: str, kt: str, pf: str, pw: str, cf: str, cw: st
           f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} |"
           for r in sorted(others, key=lambda r: -float(r["TotalDurationNs"]))[:6]] + ["",
           "The attention kernel is one launch per layer; stage_copy_kernel copies each plan's "
-          "metadata (one launch per step); the other rows are torch's input setup.", "",
+          "metadata (one launch per step); the other rows are torch's input setup.", ""] + timed_line + [
           f"Algorithmic K+V bytes per call: {algo} -> {algo / avg_ns:.1f} GB/s at the average "
           f"duration ({algo / avg_ns / 8000.0 * 100:.1f}% of 8 TB/s).", "",
           "## HBM traffic (rocprofv3 --pmc, one counter per run)", "",
@@ -681,7 +699,8 @@ def main(argv=None):
         summarize_sq(args.workload, *args.summarize_sq, args.commands)
         return 0
     if args.summarize_profiles:
-        summarize_profiles(args.workload, *args.summarize_profiles, args.calib_mib, args.commands)
+        summarize_profiles(args.workload, *args.summarize_profiles, args.calib_mib, args.commands,
+                           args.steps, args.layers)
         return 0
 
     if args.gpus != 1:
