@@ -387,9 +387,11 @@ SQ_PASS_A = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTI
              "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_INSTS_VALU")
 SQ_PASS_B = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
              "SQ_ACTIVE_INST_VMEM", "SQ_INSTS_SALU", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_VMEM")
-# flops per MFMA instruction of the 16-bit path: per tile NC = D/32 instructions of 16x16x32
-# (16384 flops) and 2 * D/16 of 16x16x16 (8192 flops), the same 1:4 mix at d 64 and 128
-FLOPS_PER_MFMA_16BIT = (16384 + 4 * 8192) / 5
+# flops per MFMA instruction of the 16-bit decode tiles: per tile NC = D/32 instructions of
+# 16x16x32 (16384 flops) and 2 * D/16 of 16x16x16 (8192 flops), the same 1:4 mix at d 64 and
+# 128; the prefill units issue only 16x16x32
+FLOPS_PER_MFMA_DECODE = (16384 + 4 * 8192) / 5
+FLOPS_PER_MFMA_16X16X32 = 16384
 
 
 def summarize_sq(workload: str, da: str, db: str, commands: str):
@@ -417,13 +419,20 @@ def summarize_sq(workload: str, da: str, db: str, commands: str):
               f"* LDS bank-conflict cycles per LDS instruction: "
               f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_INSTS_LDS'], 1):.2f}"]
     if b.dtype != "f32":
-        mf = c["SQ_INSTS_MFMA"] * FLOPS_PER_MFMA_16BIT
-        lines += [f"* MFMA instructions: {c['SQ_INSTS_MFMA']:.4g} per dispatch, {mf / 1e9:.2f} GFLOP issued"]
+        n = c["SQ_INSTS_MFMA"]
+        lo = n * FLOPS_PER_MFMA_DECODE
+        # with prefill rows the instructions mix the decode tiles' 1:4 forms and the prefill
+        # units' 16x16x32 only: the issued flops lie between the two pricings
+        hi = n * FLOPS_PER_MFMA_16X16X32 if b.rows > b.batch_size else lo
+        rng = lambda f, p=2: f"{f(lo):.{p}f}" if hi == lo else f"{f(lo):.{p}f}-{f(hi):.{p}f}"
+        lines += [f"* MFMA instructions: {n:.4g} per dispatch, {rng(lambda x: x / 1e9)} GFLOP issued"
+                  + ("" if hi == lo else " (every instruction priced as a decode tile's mix, or as "
+                                         "16x16x32 like the prefill units')")]
         if tr is not None:
-            us = tr["kernel_avg_us"]
-            lines += [f"* at the kernel-trace average of {us:.2f} us (profiles/traffic_{workload}.txt): "
-                      f"{mf / us / 1e6:.0f} TFLOP/s issued on MFMA, {mf / us / 1e6 / 2500:.1%} of the "
-                      f"2.5 PFLOP/s dense 16-bit peak"]
+            us = tr.get("kernel_timed_avg_us", tr["kernel_avg_us"])
+            lines += [f"* at the timed dispatches' average of {us:.2f} us (profiles/traffic_{workload}.txt): "
+                      f"{rng(lambda x: x / us / 1e6, 0)} TFLOP/s issued on MFMA, "
+                      f"{rng(lambda x: x / us / 1e6 / 2500 * 100, 1)}% of the 2.5 PFLOP/s dense 16-bit peak"]
     lines.append("")
     with open(os.path.join(ROOT, "profiles", f"sq_{workload}.md"), "w") as f:
         f.write("\n".join(lines))
