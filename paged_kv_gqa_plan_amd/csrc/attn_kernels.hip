@@ -68,22 +68,22 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // gfx950 lane-swap instructions: a swap of x with itself leaves, in the two results, x of
 // lane l and of lane l^16 (or l^32) in some order, so max and + of the pair are the same in
 // both lanes of it (bit-identical: both operations are commutative).
-// max of two values that are never NaN (scores are finite or -inf): one instruction, with
-// none of the quieting that fmaxf adds for operands of unknown origin. Only for operands
-// produced by ordinary VALU instructions: the compiler does not count inline asm among the
-// readers of an MFMA result that must wait for it.
-__device__ __forceinline__ float max_nonan(float a, float b) {
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
+// max of the two values a lane holds after a 16- or 32-lane swap, never NaN (scores are
+// finite or -inf): one instruction, with none of the quieting that fmaxf adds for operands
+// of unknown origin. It takes the swap's result pair, so its operands always come from that
+// ordinary VALU instruction, never straight from an MFMA accumulator (the compiler does not
+// count inline asm among the readers of an MFMA result that must wait for it).
+template <class SwapPair>
+__device__ __forceinline__ float max_of_swap(const SwapPair &r) {
+    float m;
+    asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+    return m;
 }
 __device__ __forceinline__ float max_xor16(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return max_nonan(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max_of_swap(__builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false));
 }
 __device__ __forceinline__ float max_xor32(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return max_nonan(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max_of_swap(__builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false));
 }
 __device__ __forceinline__ float sum_xor16(float x) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
