@@ -43,9 +43,9 @@ struct Block {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 fl_status fail(std::string *err, fl_status st, const char *fmt, long long a = 0,
-               long long b = 0, long long c = 0) {
+               long long b = 0, long long c = 0, long long d = 0) {
     char buf[256];
-    std::snprintf(buf, sizeof buf, fmt, a, b, c);
+    std::snprintf(buf, sizeof buf, fmt, a, b, c, d);
     if (err) *err = buf;
     return st;
 }
@@ -414,8 +414,9 @@ fl_status build_plan(const PlanLimits &lim, const PlanInput &in, Plan &out, std:
     int64_t nslots = 0;  // segment slots: one per decode piece, kQuadBlocks per quad piece
     for (const Piece &pc : pieces) nslots += pc.quad ? kQuadBlocks : 1;
     if (nslots > lim.seg_cap || G_wg > lim.group_cap)
-        return fail(err, FL_ERR_CAPACITY, "%lld work items / %lld workgroups exceed the handle's "
-                    "capacity (%lld); lower num_splits", nslots, G_wg, lim.seg_cap);
+        return fail(err, FL_ERR_CAPACITY, "%lld work items (the handle holds %lld) and %lld "
+                    "workgroups (it launches at most %lld): lower num_splits", nslots, lim.seg_cap,
+                    G_wg, lim.group_cap);
 
     // pieces per block, partial rows and merge tickets (a quad's blocks are cut alike)
     std::vector<int32_t> npieces(nblocks, 0), piece_idx(pieces.size());
