@@ -147,6 +147,44 @@ def test_random_configurations(seed):
     _check(b, num_splits=splits, what=f"random-{seed}")
 
 
+def _wide_case(seed):
+    """A seeded configuration from a wider space than _random_case: head ratios 1-32 (17,
+    20, 31 among them: a decode row's second 16-row block partly filled), up to 8 kv heads,
+    histories up to 9000 tokens, prefill chunks up to 700 rows, requests without query rows,
+    up to 50 forced slices per row block."""
+    r = np.random.default_rng(50000 + seed)
+    dtype = ["bf16", "f16", "f32"][r.integers(3)]
+    D = [64, 128][r.integers(2)]
+    P = [16, 32, 64, 128, 256][r.integers(5)]
+    Hkv = [1, 2, 4, 8][r.integers(4)]
+    G = [1, 2, 3, 4, 5, 6, 7, 8, 12, 14, 16, 17, 20, 24, 31, 32][r.integers(16)]
+    B = int(r.integers(1, 41))
+    kinds = r.integers(5, size=B)
+    kv = np.where(kinds == 0, r.integers(1, 40, size=B),
+         np.where(kinds == 1, 16 * r.integers(1, 60, size=B),
+         np.where(kinds == 2, P * r.integers(1, 8, size=B),
+         np.where(kinds == 3, r.integers(40, 3000, size=B), r.integers(3000, 9000, size=B)))))
+    qo = np.where(r.random(B) < 0.2, np.minimum(kv, r.integers(2, 700, size=B)), 1)
+    if r.random() < 0.1:
+        qo = np.where(r.random(B) < 0.3, 0, qo)
+    causal = bool(r.random() < 0.85)
+    splits = int([0, 0, 0, 0, 1, 2, 3, 7, 50][r.integers(9)])
+    b = W.make_batch(kv.tolist(), qo.tolist(), num_qo_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D,
+                     page_size=P, dtype=dtype, seed=seed, causal=causal,
+                     num_pages=int(sum(-(-k // P) for k in kv)) + 5)
+    return b, splits
+
+
+# seeds of _wide_case chosen to span its corners (each plans within the handle's capacity)
+WIDE_SEEDS = [341, 88, 590, 35, 475, 283, 105, 240, 346, 98, 294, 480, 577, 275, 249, 133]
+
+
+@pytest.mark.parametrize("seed", WIDE_SEEDS)
+def test_wide_configurations(seed):
+    b, splits = _wide_case(seed)
+    _check(b, num_splits=splits, what=f"wide-{seed}")
+
+
 def test_fp32_long_context_skew_full():
     """The long-context skew batch at full size in fp32 (8 x 32768 + 56 x 512 cached tokens,
     12/2 heads, d 128, 256-slot pages): the most pieces per row block and the deepest
