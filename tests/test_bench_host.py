@@ -32,3 +32,10 @@ def test_code_text_keeps_literals_and_sees_code_changes(tmp_path):
 def test_source_hash_is_stable():
     assert bench.source_hash() == bench.source_hash()
     assert len(bench.source_hash()) == 16
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work(capsys):
+    """The benchmark measures one GPU: --gpus N > 1 exits with status 2 and a message,
+    before torch or the library is imported."""
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU only" in capsys.readouterr().err
