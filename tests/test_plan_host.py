@@ -147,6 +147,53 @@ def test_plan_covers_every_row_and_key_once(name, splits):
         assert ms == 1 and ws == 0
 
 
+def _wide_plan_case(seed):
+    """Lengths and shapes from a wide seeded space (page-table metadata only, no pools):
+    head ratios 1-32, 1-8 kv heads, histories up to 9000 tokens, chunks up to 700 rows,
+    requests without query rows, the mask, forced slices up to 50."""
+    from types import SimpleNamespace
+    r = np.random.default_rng(70000 + seed)
+    dtype = ["bf16", "f16", "f32"][r.integers(3)]
+    D = [64, 128][r.integers(2)]
+    P = [16, 32, 64, 128, 256][r.integers(5)]
+    Hkv = [1, 2, 4, 8][r.integers(4)]
+    G = [1, 2, 3, 4, 5, 6, 7, 8, 12, 14, 16, 17, 20, 24, 31, 32][r.integers(16)]
+    B = int(r.integers(1, 65))
+    kinds = r.integers(5, size=B)
+    kv = np.where(kinds == 0, r.integers(1, 40, size=B),
+         np.where(kinds == 1, 16 * r.integers(1, 60, size=B),
+         np.where(kinds == 2, P * r.integers(1, 8, size=B),
+         np.where(kinds == 3, r.integers(40, 3000, size=B), r.integers(3000, 9000, size=B)))))
+    qo = np.where(r.random(B) < 0.2, np.minimum(kv, r.integers(2, 700, size=B)), 1)
+    if r.random() < 0.1:
+        qo = np.where(r.random(B) < 0.3, 0, qo)
+    causal = bool(r.random() < 0.85)
+    splits = int([0, 0, 0, 0, 1, 2, 3, 7, 50][r.integers(9)])
+    qo_indptr, kv_indptr, kv_indices, last, pool = _meta(kv, qo, P, r)
+    b = SimpleNamespace(num_qo_heads=G * Hkv, num_kv_heads=Hkv, group=G, head_dim=D, page_size=P,
+                        dtype=dtype, batch_size=B, kv_lens=kv.astype(np.int64), qo_lens=qo.astype(np.int64),
+                        qo_indptr=qo_indptr, kv_indptr=kv_indptr, kv_indices=kv_indices,
+                        last_page_len=last, num_pages=pool, causal=causal)
+    return b, splits
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_plan_covers_every_row_and_key_once_over_a_wide_space(seed):
+    """Coverage, cut and request facts of the work list over 60 seeded shapes: every
+    flattened row of every kv head sees exactly its causal key range, once. A plan beyond
+    the handle's capacity (forced slices) is refused with FL_ERR_CAPACITY, nothing else."""
+    b, splits = _wide_plan_case(seed)
+    h = host_handle(Hq=b.num_qo_heads, Hkv=b.num_kv_heads, D=b.head_dim, P=b.page_size, dtype=b.dtype,
+                    max_batch=64, max_rows=int(b.qo_lens.sum()) + 1, max_pages=int(b.num_pages) + 1,
+                    num_cus=256)
+    try:
+        items = plan_batch(h, b, num_splits=splits)
+    except fl.FlError as e:
+        assert e.status == fl.FL_ERR_CAPACITY and splits > 0, str(e)
+        return
+    check_coverage(items, b, causal=b.causal)
+
+
 def test_plan_non_causal_prefill_covers_whole_history():
     b = W.make_batch([60, 9, 300], [7, 3, 20], num_qo_heads=4, num_kv_heads=2, head_dim=64,
                      page_size=16, dtype="f32", causal=False)
