@@ -317,11 +317,11 @@ __device__ __forceinline__ void softmax_tile(const f32x4 &s, int t0, int grp, in
                                              bool &rescaled) {
     f32x4 x = s;  // masked in place on tiles that need it
     if (!full) {
+        // key t0 + 4grp + e, compared as 4grp against tile-relative bounds (nothing per key
+        // is computed on the tiles that need no mask)
+        const int g4 = 4 * grp, end_rel = tok_end - t0, over = g4 - (limit - t0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = t0 + 4 * grp + e;
-            x[e] = (t < tok_end) && (t <= limit) ? x[e] : kNegInf;
-        }
+        for (int e = 0; e < 4; ++e) x[e] = (g4 < end_rel - e) && (over <= -e) ? x[e] : kNegInf;
     }
     // fmaxf, not the inline-asm max: x may be the MFMA accumulator itself, and the compiler
     // inserts the wait states an MFMA result needs before a VALU read only for instructions
@@ -600,9 +600,9 @@ struct HalfTile {
         const uint32_t l23 = H::pack(p[2] - H::lo_f(h23), p[3] - H::hi_f(h23));
         // keys at or past tok_end may hold anything (NaN included): their V becomes 0
         if (t0 + kTileTokens > tok_end) {
-            const int k0 = t0 + 4 * grp;
-            const u32x2 vmask = {(k0 < tok_end ? 0xFFFFu : 0u) | (k0 + 1 < tok_end ? 0xFFFF0000u : 0u),
-                                 (k0 + 2 < tok_end ? 0xFFFFu : 0u) | (k0 + 3 < tok_end ? 0xFFFF0000u : 0u)};
+            const int g4 = 4 * grp, r = tok_end - t0;  // key t0 + 4grp + j is below tok_end
+            const u32x2 vmask = {(g4 < r ? 0xFFFFu : 0u) | (g4 < r - 1 ? 0xFFFF0000u : 0u),
+                                 (g4 < r - 2 ? 0xFFFFu : 0u) | (g4 < r - 3 ? 0xFFFF0000u : 0u)};
 #pragma unroll
             for (int j = 0; j < NJ; ++j) vt[j] &= vmask;
         }
@@ -1100,12 +1100,16 @@ __device__ __forceinline__ void unit_step(const lds_char *buf, const uint32_t *r
     for (int b = 0; b < NB; ++b) {
         if (!act[b]) continue;
         if (!full[b]) {
+            // key t = t0 + 16u + 4grp + e is visible when t < tok_end and t <= the row's
+            // limit, compared as 4grp against step-relative bounds so that nothing per key
+            // is computed on the steps that need no mask
+            const int g4 = 4 * grp, end_rel = tok_end - t0, over = g4 - (bs[b].ri.limit - t0);
 #pragma unroll
             for (int u = 0; u < kQuadStepTiles; ++u)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = t0 + kTileTokens * u + 4 * grp + e;
-                    s[b][u][e] = (t < tok_end) && (t <= bs[b].ri.limit) ? s[b][u][e] : kNegInf;
+                    const int c = kTileTokens * u + e;
+                    s[b][u][e] = (g4 < end_rel - c) && (over <= -c) ? s[b][u][e] : kNegInf;
                 }
         }
         // one running-max update for the 64 keys (lazy: moves only by more than kSlack)
@@ -1147,11 +1151,12 @@ __device__ __forceinline__ void unit_step(const lds_char *buf, const uint32_t *r
             vt[j] = u32x4{x0[0], x0[1], x1[0], x1[1]};
         }
         if (tail) {  // wave-uniform: only a piece's last step can reach past tok_end
-            const int k0 = t0 + kTileTokens * u0 + 4 * grp, k1 = t0 + kTileTokens * u1 + 4 * grp;
-            const u32x4 m = {(k0 < tok_end ? 0xFFFFu : 0u) | (k0 + 1 < tok_end ? 0xFFFF0000u : 0u),
-                             (k0 + 2 < tok_end ? 0xFFFFu : 0u) | (k0 + 3 < tok_end ? 0xFFFF0000u : 0u),
-                             (k1 < tok_end ? 0xFFFFu : 0u) | (k1 + 1 < tok_end ? 0xFFFF0000u : 0u),
-                             (k1 + 2 < tok_end ? 0xFFFFu : 0u) | (k1 + 3 < tok_end ? 0xFFFF0000u : 0u)};
+            // key t0 + 16u + 4grp + j is below tok_end when 4grp < tok_end - t0 - 16u - j
+            const int g4 = 4 * grp, r0 = tok_end - t0 - kTileTokens * u0, r1 = tok_end - t0 - kTileTokens * u1;
+            const u32x4 m = {(g4 < r0 ? 0xFFFFu : 0u) | (g4 < r0 - 1 ? 0xFFFF0000u : 0u),
+                             (g4 < r0 - 2 ? 0xFFFFu : 0u) | (g4 < r0 - 3 ? 0xFFFF0000u : 0u),
+                             (g4 < r1 ? 0xFFFFu : 0u) | (g4 < r1 - 1 ? 0xFFFF0000u : 0u),
+                             (g4 < r1 - 2 ? 0xFFFFu : 0u) | (g4 < r1 - 3 ? 0xFFFF0000u : 0u)};
 #pragma unroll
             for (int j = 0; j < NJ; ++j) vt[j] &= m;
         }
