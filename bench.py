@@ -42,6 +42,7 @@ LAYERS = {"tiny_decode": 24, "saturated_decode": 24, "ragged_mixed_step": 24,
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "csrc", "attn_kernels.hip")
 PLAN_SRC = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "csrc", "plan.cpp")
 INTERNAL_H = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "csrc", "fl_internal.h")  # planner costs, layouts
+BUILD_PY = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "_build.py")  # compiler flags per source
 
 
 def code_text(path: str) -> str:
@@ -72,10 +73,11 @@ def code_text(path: str) -> str:
 
 
 def source_hash() -> str:
-    """Hash of the attention kernel's and the planner's code and of their shared header
-    (comments excluded)."""
+    """Hash of the attention kernel's and the planner's code, their shared header and the
+    build's compiler flags (C and C++ comments excluded; the build script's own comments
+    count, a conservative choice)."""
     h = hashlib.sha256()
-    for p in (KERNEL_SRC, PLAN_SRC, INTERNAL_H):
+    for p in (KERNEL_SRC, PLAN_SRC, INTERNAL_H, BUILD_PY):
         h.update(code_text(p).encode())
     return h.hexdigest()[:16]
 
