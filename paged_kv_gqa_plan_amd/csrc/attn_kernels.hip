@@ -168,20 +168,19 @@ __device__ __forceinline__ void wait_vm_in(int n) {
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Loads straight into LDS: lane l's 16 (4) bytes at base + voff land at LDS byte
-// lds + 16l (4l); lds is wave-uniform. They are issued from inline assembly, so the
-// compiler neither counts nor waits for them: every read of their data follows an
+// lds + 16l (4l); base and lds are wave-uniform. They are issued from inline assembly, so
+// the compiler neither counts nor waits for them: every read of their data follows an
 // explicit wait_vm (loads complete in issue order), and the compiler's own waits for the
-// loads it does see only grow stricter with loads it does not. Each lane passes its full
-// 64-bit address.
+// loads it does see only grow stricter with loads it does not. The address is the
+// instruction's scalar base plus the lane's 32-bit offset, so no lane forms a 64-bit
+// address of its own.
 __device__ __forceinline__ void dma_b128(const void *base, uint32_t voff, const lds_char *lds) {
-    const char *ptr = (const char *)base + voff;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(ptr),
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
                  "s"((uint32_t)(uintptr_t)lds)
                  : "memory", "m0");
 }
 __device__ __forceinline__ void dma_b32(const void *base, uint32_t voff, const lds_char *lds) {
-    const char *ptr = (const char *)base + voff;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(ptr),
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base),
                  "s"((uint32_t)(uintptr_t)lds)
                  : "memory", "m0");
 }
