@@ -42,7 +42,6 @@ LAYERS = {"tiny_decode": 24, "saturated_decode": 24, "ragged_mixed_step": 24,
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "csrc", "attn_kernels.hip")
 PLAN_SRC = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "csrc", "plan.cpp")
 INTERNAL_H = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "csrc", "fl_internal.h")  # planner costs, layouts
-BUILD_PY = os.path.join(ROOT, "paged_kv_gqa_plan_amd", "_build.py")  # compiler flags per source
 
 
 def code_text(path: str) -> str:
@@ -73,12 +72,14 @@ def code_text(path: str) -> str:
 
 
 def source_hash() -> str:
-    """Hash of the attention kernel's and the planner's code, their shared header and the
-    build's compiler flags (C and C++ comments excluded; the build script's own comments
-    count, a conservative choice)."""
+    """Hash of the attention kernel's and the planner's code and their shared header
+    (comments excluded), and of the compiler flags the library's build gives them."""
+    from paged_kv_gqa_plan_amd import _build
     h = hashlib.sha256()
-    for p in (KERNEL_SRC, PLAN_SRC, INTERNAL_H, BUILD_PY):
+    for p in (KERNEL_SRC, PLAN_SRC, INTERNAL_H):
         h.update(code_text(p).encode())
+    h.update(repr((_build.ARCH, _build.OPT, _build.DEVICE_FLAGS,
+                   {s: _build.FILE_FLAGS.get(s, []) for s in ("attn_kernels.hip", "plan.cpp")})).encode())
     return h.hexdigest()[:16]
 
 

@@ -60,11 +60,12 @@ _lib = None
 
 
 def load_library(path: Optional[str] = None):
-    """Load the built library (raises if it is missing)."""
+    """Load the built library (raises if it is missing): `path`, else the file named by the
+    FL_PAGED_ATTN_LIB environment variable (a checking build, say), else the in-tree build."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("FL_PAGED_ATTN_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise ImportError(f"{p} is not built; run `python -c 'import __graft_entry__ as g; "
                           f"g.build()'` (hipcc, gfx950)")

@@ -24,6 +24,7 @@ ARCH = "gfx950"
 # into SGPRs at dispatch.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-kernarg-preload-count=7"]
+OPT = "-O3"
 # Per-source flags. The attention kernels never compute on a NaN: scores of keys past a
 # request's end (whose pool rows may hold anything, NaN included) are replaced by -inf
 # through index comparisons before any arithmetic reads them, and their V rows are zeroed
@@ -41,12 +42,21 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build_library(verbose: bool = False, out: str = LIB, defines=(), sources=None) -> str:
+# Host-side sanitizers for a checking build of the host code (planner, allocator, entry
+# points): every flag applies to the host compilation only, never to GPU code. Such a
+# library is loaded with the sanitizer runtime preloaded (LD_PRELOAD) for the host tests.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_library(verbose: bool = False, out: str = LIB, defines=(), sources=None,
+                  host_sanitize: bool = False) -> str:
     """Compile each source to an object (in parallel, with its own flags from FILE_FLAGS)
-    and link them into the shared library `out`."""
+    and link them into the shared library `out`; host_sanitize: the checking build."""
     srcs = list(sources or SOURCES)
-    common = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
-              "-Wno-unused-function", *DEVICE_FLAGS, *[f"-D{d}" for d in defines],
+    san = HOST_SANITIZE if host_sanitize else []
+    common = [hipcc(), f"--offload-arch={ARCH}", "-O1" if host_sanitize else OPT, "-std=c++17", "-fPIC",
+              "-Wall", "-Wno-unused-function", *DEVICE_FLAGS, *san, *[f"-D{d}" for d in defines],
               "-I", INCLUDE, "-I", CSRC]
     noise = "is not a recognized feature for this target"
 
@@ -67,7 +77,7 @@ def build_library(verbose: bool = False, out: str = LIB, defines=(), sources=Non
         with ThreadPoolExecutor(max_workers=max(1, min(len(cmds), os.cpu_count() or 1, 16))) as ex:
             list(ex.map(run, cmds))
         tmp = out + ".tmp"
-        run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+        run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *san, "-o", tmp])
         os.replace(tmp, out)
     return out
 
@@ -77,5 +87,10 @@ def build_probe(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build_library(verbose=True))
-    print(build_probe(verbose=True))
+    import sys
+    if len(sys.argv) == 3 and sys.argv[1] == "--host-sanitize":
+        # the checking build, written to the path given (the in-tree library is left alone)
+        print(build_library(verbose=True, out=os.path.abspath(sys.argv[2]), host_sanitize=True))
+    else:
+        print(build_library(verbose=True))
+        print(build_probe(verbose=True))
