@@ -470,6 +470,19 @@ def tile_rows(b):
     return np.concatenate(out).astype(np.int32)
 
 
+def whole_row_tiles(b):
+    """Pool row page * P + slot of the first key of every 16-key tile of every request: the
+    same tiles as tile_rows, each read as whole token rows (every kv head at once)."""
+    import numpy as np
+    P = b.page_size
+    out = []
+    for r in range(b.batch_size):
+        t = np.arange(0, int(b.kv_lens[r]), 16)
+        pages = b.kv_indices[b.kv_indptr[r] + t // P].astype(np.int64)
+        out.append(pages * P + t % P)
+    return np.concatenate(out).astype(np.int32)
+
+
 def graph_us(body, stream, L: int, replays: int = 20):
     """Median time per layer of `body` (L launches) captured in one HIP graph."""
     import torch
@@ -524,6 +537,24 @@ def floors(b, ks, vs, L: int, stream, grid: int = 256):
         for _ in range(L):
             assert lib.fl_probe_empty(grid, s) == 0
     read_us, empty_us = graph_us(reads, stream, L), graph_us(empties, stream, L)
+    # the same pages read as whole token rows (every kv head's slice at once): the bound of
+    # a kernel that streamed whole rows instead of one kv head's slices
+    row_bytes = b.num_kv_heads * slice_bytes
+    whole = {}
+    if b.num_kv_heads > 1 and row_bytes in (256, 512):
+        wrows = torch.from_numpy(whole_row_tiles(b)).to("cuda:0")
+        wnb = 4 if row_bytes == 256 else 2
+
+        def whole_reads():
+            s = torch.cuda.current_stream().cuda_stream
+            for l in range(L):
+                assert lib.fl_probe_read_tiles(wrows.data_ptr(), wrows.numel(), ks[l].data_ptr(), vs[l].data_ptr(),
+                                               1, row_bytes, wnb, sink.data_ptr(), grid, s) == 0
+        wus = graph_us(whole_reads, stream, L)
+        whole = {"whole_row_read_floor_us": round(wus, 3),
+                 "whole_row_read_floor_kind": f"the same pages read as whole {row_bytes}-byte token rows "
+                                              f"({wrows.numel()} tiles of 16 rows of K and V), {grid} "
+                                              f"workgroups, {wnb} tiles in flight per wave, graph of {L} launches"}
     tile_bytes = rows.numel() * 16 * slice_bytes * 2
     tiles_per_wave = -(-rows.numel() // (grid * 4))
     return {"read_floor_us": round(read_us, 3),
@@ -534,7 +565,7 @@ def floors(b, ks, vs, L: int, stream, grid: int = 256):
                                f"({'all of them' if tiles_per_wave <= nb else f'of {tiles_per_wave}'}), "
                                f"graph of {L} launches",
             "launch_floor_us": round(empty_us, 3),
-            "launch_floor_kind": f"empty kernel of {grid} workgroups, graph of {L} launches"}
+            "launch_floor_kind": f"empty kernel of {grid} workgroups, graph of {L} launches", **whole}
 
 
 def prefill_flops(b) -> int:

@@ -13,7 +13,8 @@
 //   tile_rows   device int32[num_tiles]: pool row (page * P + slot) * Hkv + kv_head of the
 //               tile's first key; its 16 keys are Hkv rows apart
 //   k, v        the pools; a row is slice_bytes (head_dim * element size) long
-//   slice_bytes 128 or 256
+//   slice_bytes 128 or 256 (or, to read whole token rows of every kv head at once, the
+//               row's full width 256 or 512 with hkv = 1 and rows page * P + slot)
 //   sink        device int32[grid * 4]
 // fl_probe_empty launches `grid` workgroups of 256 threads that do nothing.
 #include <hip/hip_runtime.h>
@@ -87,6 +88,9 @@ extern "C" int fl_probe_read_tiles(const int32_t *tile_rows, int64_t num_tiles, 
                            hkv, sink);
     else if (slice_bytes == 256 && tiles_in_flight == 2)
         hipLaunchKernelGGL((read_tiles_kernel<256, 2>), dim3(grid), dim3(256), 0, s, tile_rows, num_tiles, kp, vp,
+                           hkv, sink);
+    else if (slice_bytes == 512 && tiles_in_flight == 2)
+        hipLaunchKernelGGL((read_tiles_kernel<512, 2>), dim3(grid), dim3(256), 0, s, tile_rows, num_tiles, kp, vp,
                            hkv, sink);
     else
         return (int)hipErrorInvalidValue;
