@@ -1252,7 +1252,8 @@ __device__ __forceinline__ void quad_path(const int *rv, const AttnArgs &a, cons
     };
     // step g's tile of this wave into buffer g % kQuadBufs; at a unit's first step, its Q
     // rows go out first (into the wave's Q buffers of that unit's parity). The tile's pool
-    // row was read one step earlier (next_row), so no scalar load waits in front of it.
+    // row was read at the end of the step before (next_row), so its scalar load is never
+    // outstanding at the step's LDS waits.
     int next_row = 0;
     auto issue = [&](int g, auto buf) {  // buf: g % kQuadBufs, a compile-time constant
         constexpr int B = decltype(buf)::value;
@@ -1264,7 +1265,6 @@ __device__ __forceinline__ void quad_path(const int *rv, const AttnArgs &a, cons
             stage_q(iq & 1);
         }
         T::ring_issue(ring, B * kQuadStepTiles + wv, k_pool, v_pool, next_row);
-        if (g + 1 < nsteps) next_row = rows[kQuadStepTiles * (g + 1) + wv];
     };
     // compute cursor (taken before issue(1), which moves the issue cursor on when the
     // first piece has a single step)
@@ -1278,6 +1278,7 @@ __device__ __forceinline__ void quad_path(const int *rv, const AttnArgs &a, cons
     if (nsteps > 1) {
         next_row = rows[kQuadStepTiles + wv];
         issue(1, std::integral_constant<int, 1>{});
+        if (nsteps > 2) next_row = rows[2 * kQuadStepTiles + wv];
     }
 
     int npend = 0;
@@ -1348,6 +1349,11 @@ __device__ __forceinline__ void quad_path(const int *rv, const AttnArgs &a, cons
                 q_end += unit_steps(bs[0].w);
             }
         }
+        // the pool row of step g + 3's tile, for the next step's issue: read at the step's
+        // end, after its last LDS wait (a scalar load outstanding at an LDS wait makes that
+        // wait cover the scalar load too)
+        __builtin_amdgcn_sched_barrier(0);
+        if (g + 3 < nsteps) next_row = rows[kQuadStepTiles * (g + 3) + wv];
     };
     static_assert(kQuadBufs == 3, "the step loop is unrolled by the three buffers");
     for (int g = 0; g < nsteps; g += kQuadBufs) {
